@@ -1,0 +1,26 @@
+"""Shared test helpers: seeded workloads turned into oracle inputs."""
+import functools
+
+import numpy as np
+
+import workload
+
+
+def to_u16(t) -> np.ndarray:
+    """torch.bfloat16 CPU tensor -> uint16 bit patterns (no arithmetic)."""
+    import torch
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@functools.lru_cache(maxsize=4)
+def weights(cfg_index: int, gains: str = "ones"):
+    wl = workload.config(cfg_index)
+    return wl, workload.make_weights(wl, gains=gains)
+
+
+def oracle_model(cfg_index: int, gains: str = "ones", cache: bool = True, kv_round: bool = True,
+                 shape=None, w=None):
+    from oracle.decoder import Model
+    wl, wt = weights(cfg_index, gains) if w is None else (workload.config(cfg_index), w)
+    u16 = {k: to_u16(v) for k, v in wt.items()}
+    return Model(shape or wl.shape, u16, cache=cache, kv_round=kv_round)
