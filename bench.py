@@ -1,0 +1,178 @@
+"""Decode benchmark: per-token latency and HBM roofline fraction of the
+persistent decode megakernel on one MI355X.
+
+Workload (default): the Llama-3.2-1B-shaped decoder at batch 1, seeded random
+bf16 weights, a 39-token prompt consumed untimed, then K greedy decode steps
+inside ONE persistent launch (mk_generate), timed with HIP events on the
+launch stream. Also timed, for context: the same steps with one launch per
+operator (the baseline built from the same task bodies), and the CPU oracle on
+a bounded sample.
+
+Prints one JSON line (rank 0). `--gpus N` with N > 1 exits: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X published HBM3E bandwidth
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(shape, positions) -> int:
+    """Bytes one decode step must move: every weight once (matrices, norm
+    gains, one embedding row per sequence, the LM head), the KV cache of
+    positions 0..p for each sequence (K and V, bf16; the entry at p is the one
+    written this step)."""
+    H, D, F, V, L = shape.hidden, shape.head_dim, shape.ffn, shape.vocab, shape.n_layers
+    Hq, Hkv = shape.n_q_heads, shape.n_kv_heads
+    per_layer = (Hq * D * H + 2 * Hkv * D * H + H * Hq * D + 2 * F * H + H * F + 2 * H) * 2
+    w = L * per_layer + V * H * 2 + H * 2 + len(positions) * H * 2
+    kv_per_pos = L * Hkv * D * 2 * 2
+    return w + sum((p + 1) * kv_per_pos for p in positions)
+
+
+def cpu_baseline(wl, weights, seconds: float = 15.0):
+    """The float64 oracle as it stands, timed on the host cores: single decode
+    steps of the same shape at the prompt's last position (empty cache prefix),
+    repeated until about `seconds` have elapsed (at least one step)."""
+    import numpy as np
+    import torch
+    from oracle.decoder import Model
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    u16 = {k: v.contiguous().view(torch.int16).numpy().view(np.uint16) for k, v in weights.items()}
+    m = Model(wl.shape, u16, cache=False)
+    P = wl.prompt_len or 1
+    st = m.new_state(1, P + 8)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        m.decode_step(st, [1 + n], [P - 1 + n])
+        n += 1
+        if time.perf_counter() - t0 > seconds or n >= 8:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": dt / n * 1e6, "unit": "us/token", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} float64 oracle decode steps of the {wl.name} config at positions "
+                      f"{P - 1}..{P - 2 + n} (empty cache prefix), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1: Llama-3.2-1B shape)")
+    ap.add_argument("--oplaunch-steps", type=int, default=32, help="steps timed for the per-operator baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is described in the design record, not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workload
+    from decode_persistent_megakernel_amd import MK_MODE_OPLAUNCH
+    from decode_persistent_megakernel_amd.session import Session
+
+    wl = workload.config(args.config)
+    if wl.batch != 1 or wl.kv_prefill != "none":
+        log("note: non-default workload")
+    torch.cuda.set_device(0)
+    t = time.time()
+    w = workload.make_weights(wl)
+    log(f"weights generated in {time.time() - t:.1f}s")
+    ss = Session(wl.shape, w, wl.batch, wl.max_seq)
+    log(f"model loaded: {ss.n_tasks} tasks, {ss.num_cus} CUs, packed weights {ss.packed_bytes / 1e9:.3f} GB")
+    prompt = workload.make_prompt(wl)[0]
+    P = len(prompt)
+    K, W = args.steps, args.warmup
+    if P - 1 + max(K, W) > wl.max_seq:
+        raise SystemExit("steps exceed max_seq")
+    for p in range(P - 1):
+        ss.decode_step([int(prompt[p])], [p], logits=False)
+    torch.cuda.synchronize()
+    ss.check()
+    log("prompt prefilled")
+
+    stream = torch.cuda.current_stream()
+    out = torch.zeros((max(K, W, 1), 1), dtype=torch.int32, device="cuda")
+    if W > 0:
+        ss.generate([int(prompt[-1])], [P - 1], W, out=out[:W])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    ss.generate([int(prompt[-1])], [P - 1], K, out=out[:K])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ss.check()
+    ms = e0.elapsed_time(e1)
+    us_tok = ms * 1e3 / K
+    positions = [P - 1 + k for k in range(K)]
+    bytes_launch = sum(algorithmic_bytes(wl.shape, [p]) for p in positions)
+    achieved = bytes_launch / (ms * 1e-3) / 1e9
+    log(f"megakernel: {K} steps in {ms:.3f} ms (wall {wall * 1e3:.1f} ms): {us_tok:.2f} us/token, "
+        f"{achieved:.1f} GB/s algorithmic")
+
+    # per-operator-launch baseline (same task bodies), a shorter run
+    Kb = min(args.oplaunch_steps, K)
+    tok = int(prompt[-1])
+    toks_b = out[:Kb, 0].tolist()
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for k in range(Kb):
+        ss.tok[0] = tok if k == 0 else toks_b[k - 1]
+        ss.pos[0] = P - 1 + k
+        from decode_persistent_megakernel_amd import mk_decode_step
+        mk_decode_step(ss.model, ss.tok, ss.pos, 1, None, ss.next, MK_MODE_OPLAUNCH)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    ss.check()
+    us_b = b0.elapsed_time(b1) * 1e3 / Kb
+    log(f"per-operator launches: {us_b:.2f} us/token over {Kb} steps")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, w, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads")
+
+    rec = {
+        "metric": "decode us/token at batch 1 + achieved HBM GB/s as % of roofline",
+        "value": round(us_tok, 3), "unit": "us/token", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms / K, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 weights, fp32 arithmetic", "data": "synthetic",
+        "config": {"workload": wl.name, "global_batch": wl.batch, "seq_len": P - 1 + K,
+                   "prompt": P, "decode_steps": K, "parallelism": "none (1 GPU)"},
+        "achieved_gbs": round(achieved, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "mk_persistent", "launch_ms": round(ms, 4),
+                     "bytes_per_launch": bytes_launch},
+        "oplaunch_baseline_us_per_token": round(us_b, 3),
+        "cpu_baseline": cpu,
+    }
+    ss.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

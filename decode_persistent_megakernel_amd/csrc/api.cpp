@@ -1,0 +1,427 @@
+// C ABI of libmk: graph building, model load (weight packing), decode calls.
+// The declarations and their contracts are in include/mk.h.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "device.h"
+#include "graph.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return MK_EHIP;
+}
+
+#define HIP_TRY(expr, what)                   \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct mk_model {
+  mk::Graph g;
+  int device = 0;
+  int lds_bytes = 0;
+  uint64_t packed_bytes = 0;
+  uint32_t epoch = 0;
+  uint32_t max_threshold = 1;
+  bool need_reset = false;
+  uint64_t timeout_ticks = 200000000ull;  // 2 s at 100 MHz
+  uint64_t* profile = nullptr;
+  int32_t drop_task = -1;
+  size_t profile_bytes = 0;
+  mk::Params base{};                      // everything but the per-call fields
+  std::vector<void*> allocs;              // device buffers owned by the model
+
+  ~mk_model() {
+    for (void* p : allocs) (void)hipFree(p);
+  }
+  template <class T>
+  int alloc(T** p, size_t count, const char* what) {
+    void* q = nullptr;
+    if (count == 0) count = 1;
+    hipError_t e = hipMalloc(&q, count * sizeof(T));
+    if (e != hipSuccess) return fail(MK_ENOMEM, std::string("hipMalloc failed for ") + what);
+    allocs.push_back(q);
+    *p = static_cast<T*>(q);
+    return MK_OK;
+  }
+};
+
+extern "C" {
+
+const char* mk_last_error(void) { return g_err.c_str(); }
+
+int mk_build_task_graph(const mk_model_desc* desc, const mk_graph_opts* opts, mk_graph** out) {
+  if (!desc || !out) return fail(MK_EINVAL, "mk_build_task_graph: NULL argument");
+  mk_graph* g = new (std::nothrow) mk_graph;
+  if (!g) return fail(MK_ENOMEM, "mk_build_task_graph: out of host memory");
+  std::string err;
+  int rc = mk::build_graph(*desc, opts, &g->g, &err);
+  if (rc != MK_OK) {
+    delete g;
+    return fail(rc, "mk_build_task_graph: " + err);
+  }
+  *out = g;
+  return MK_OK;
+}
+
+int mk_graph_serialize(const mk_graph* g, uint8_t* buf, size_t cap, size_t* len) {
+  if (!g || !len) return fail(MK_EINVAL, "mk_graph_serialize: NULL argument");
+  const std::vector<uint8_t> b = mk::serialize(g->g);
+  *len = b.size();
+  if (!buf) return cap == 0 ? MK_OK : fail(MK_EINVAL, "mk_graph_serialize: NULL buffer");
+  if (cap < b.size()) return fail(MK_EINVAL, "mk_graph_serialize: buffer too small");
+  std::memcpy(buf, b.data(), b.size());
+  return MK_OK;
+}
+
+int mk_graph_info(const mk_graph* g, int32_t* n_tasks, int32_t* n_events, mk_graph_opts* resolved) {
+  if (!g) return fail(MK_EINVAL, "mk_graph_info: NULL graph");
+  if (n_tasks) *n_tasks = static_cast<int32_t>(g->g.tasks.size());
+  if (n_events) *n_events = static_cast<int32_t>(g->g.events.size());
+  if (resolved) *resolved = g->g.opts;
+  return MK_OK;
+}
+
+void mk_free_graph(mk_graph* g) { delete g; }
+
+int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_model** out) {
+  using namespace mk;
+  if (!gr || !w || !out || !w->layers || !w->embed || !w->g_final || !w->k_cache || !w->v_cache)
+    return fail(MK_EINVAL, "mk_load_weights: NULL argument");
+  const mk_model_desc& d = gr->g.desc;
+  if (!d.tied_embeddings && !w->lm_head) return fail(MK_EINVAL, "mk_load_weights: lm_head is NULL but not tied");
+  for (int l = 0; l < d.n_layers; ++l) {
+    const mk_layer_weights& L = w->layers[l];
+    if (!L.wq || !L.wk || !L.wv || !L.wo || !L.wg || !L.wu || !L.wd || !L.g_attn || !L.g_mlp)
+      return fail(MK_EINVAL, "mk_load_weights: NULL layer weight");
+  }
+  const int G = d.n_q_heads / d.n_kv_heads;
+  if (G > 8) return fail(MK_EUNSUPPORTED, "mk_load_weights: more than 8 query heads per kv head");
+  if (G * d.head_dim > 1024) return fail(MK_EUNSUPPORTED, "mk_load_weights: (Hq/Hkv)*head_dim > 1024");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  mk_model* m = new (std::nothrow) mk_model;
+  if (!m) return fail(MK_ENOMEM, "mk_load_weights: out of host memory");
+  struct Guard {
+    mk_model*& m;
+    ~Guard() { delete m; }
+  } guard{m};
+  m->g = gr->g;
+  const Graph& g = m->g;
+  HIP_TRY(hipGetDevice(&m->device), "hipGetDevice");
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, m->device), "hipGetDeviceProperties");
+
+  // --- task descriptors and packed-weight offsets ---------------------------
+  const int kb_h = static_cast<int>(cdiv(d.hidden, kUnitCols));
+  const int kb_qd = static_cast<int>(cdiv(int64_t(d.n_q_heads) * d.head_dim, kUnitCols));
+  const int kb_f = static_cast<int>(cdiv(d.ffn, kUnitCols));
+  std::vector<DevTask> dt(g.tasks.size());
+  std::vector<PackJob> jobs;
+  uint64_t off = 0;
+  int max_vrows = 4;
+  std::vector<int32_t> ordinal_in_op(g.tasks.size());
+  for (const auto& op : g.ops)
+    for (int32_t i = op.first; i < op.second; ++i) ordinal_in_op[i] = i - op.first;
+  for (size_t i = 0; i < g.tasks.size(); ++i) {
+    const Task& t = g.tasks[i];
+    DevTask& x = dt[i];
+    x = DevTask{t.type, t.layer, t.b, t.g, t.chunk, t.row0, t.row1, t.dep, t.trig, ordinal_in_op[i], 0, 0, 0};
+    int K = 0, KB = 0;
+    switch (t.type) {
+      case T_QKV: case T_GU: case T_LM: K = d.hidden; KB = kb_h; break;
+      case T_O: K = d.n_q_heads * d.head_dim; KB = kb_qd; break;
+      case T_D: K = d.ffn; KB = kb_f; break;
+      default: break;
+    }
+    if (KB == 0) continue;
+    const int nrb = static_cast<int>(cdiv(t.row1 - t.row0, kUnitRows));
+    x.n_vrb = t.type == T_GU ? 2 * nrb : nrb;
+    x.n_units = x.n_vrb * KB;
+    x.w_off = static_cast<int64_t>(off);
+    max_vrows = std::max(max_vrows, x.n_vrb * kUnitRows);
+    jobs.push_back(PackJob{x.w_off, t.type, t.layer, t.g, t.row0, t.row1, K, KB, x.n_vrb});
+    off += uint64_t(x.n_units) * kUnitBytes;
+  }
+  m->packed_bytes = off;
+
+  // --- LDS budget -------------------------------------------------------------
+  const int ncap = std::min<int>(d.max_batch, kMaxCols);
+  const int kp = std::max({kb_h, kb_qd, kb_f}) * kUnitCols;
+  const int att_floats = G * d.head_dim + 2 * d.head_dim + 3 * G + G * kAttTile;
+  const size_t lds = 128 * 4 + size_t(4) * (size_t(ncap) * kp + size_t(kWaves) * ncap * max_vrows + att_floats);
+  if (d.max_batch > kMaxCols)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: max_batch above 4 is not supported by the VALU task bodies");
+  if (lds > 160 * 1024)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: shape needs " + std::to_string(lds) + " bytes of LDS (> 160 KiB)");
+  m->lds_bytes = static_cast<int>(lds);
+  HIP_TRY(set_lds_limit(m->lds_bytes), "hipFuncSetAttribute(max dynamic LDS)");
+  int per_cu = 0;
+  HIP_TRY(persistent_occupancy(m->lds_bytes, &per_cu), "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (int64_t(per_cu) * prop.multiProcessorCount < g.opts.num_cus)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: num_cus=" + std::to_string(g.opts.num_cus) +
+                                     " workgroups cannot be co-resident (" + std::to_string(prop.multiProcessorCount) +
+                                     " CUs x " + std::to_string(per_cu) + ")");
+
+  // --- device buffers -----------------------------------------------------------
+  Params& P = m->base;
+  P = Params{};
+  const int64_t H = d.hidden, V = d.vocab, L = d.n_layers, B = d.max_batch, S = d.max_seq, D = d.head_dim;
+  const int64_t Hq = d.n_q_heads, Hkv = d.n_kv_heads, F = d.ffn;
+  int nlm = 0;
+  for (const Task& t : g.tasks) nlm += t.type == T_LM;
+  DevTask* d_tasks;
+  int32_t *d_qptr, *d_qids;
+  uint32_t *d_thr, *d_cnt;
+  int rc;
+  if ((rc = m->alloc(&d_tasks, dt.size(), "tasks")) || (rc = m->alloc(&d_qptr, g.queues.size() + 1, "queues")) ||
+      (rc = m->alloc(&d_qids, g.tasks.size(), "queue ids")) || (rc = m->alloc(&d_thr, g.events.size(), "thresholds")) ||
+      (rc = m->alloc(&d_cnt, g.events.size(), "counters")))
+    return rc;
+  std::vector<int32_t> qptr(1, 0), qids;
+  for (const auto& q : g.queues) {
+    qids.insert(qids.end(), q.begin(), q.end());
+    qptr.push_back(static_cast<int32_t>(qids.size()));
+  }
+  std::vector<uint32_t> thr(g.events.size());
+  for (size_t e = 0; e < g.events.size(); ++e) {
+    thr[e] = static_cast<uint32_t>(g.events[e].threshold);
+    m->max_threshold = std::max(m->max_threshold, thr[e]);
+  }
+  HIP_TRY(hipMemcpy(d_tasks, dt.data(), dt.size() * sizeof(DevTask), hipMemcpyHostToDevice), "copy tasks");
+  HIP_TRY(hipMemcpy(d_qptr, qptr.data(), qptr.size() * 4, hipMemcpyHostToDevice), "copy queue offsets");
+  HIP_TRY(hipMemcpy(d_qids, qids.data(), qids.size() * 4, hipMemcpyHostToDevice), "copy queues");
+  HIP_TRY(hipMemcpy(d_thr, thr.data(), thr.size() * 4, hipMemcpyHostToDevice), "copy thresholds");
+  HIP_TRY(hipMemset(d_cnt, 0, thr.size() * 4), "clear counters");
+
+  uint8_t* d_wpack;
+  uint16_t *d_embed, *d_gains;
+  float2* d_rope;
+  if ((rc = m->alloc(&d_wpack, m->packed_bytes, "packed weights")) || (rc = m->alloc(&d_embed, V * H, "embedding")) ||
+      (rc = m->alloc(&d_gains, (2 * L + 1) * H, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")))
+    return rc;
+  HIP_TRY(hipMemcpyAsync(d_embed, w->embed, V * H * 2, hipMemcpyDeviceToDevice, s), "copy embedding");
+  for (int l = 0; l < L; ++l) {
+    HIP_TRY(hipMemcpyAsync(d_gains + (2 * l) * H, w->layers[l].g_attn, H * 2, hipMemcpyDeviceToDevice, s), "copy gain");
+    HIP_TRY(hipMemcpyAsync(d_gains + (2 * l + 1) * H, w->layers[l].g_mlp, H * 2, hipMemcpyDeviceToDevice, s), "copy gain");
+  }
+  HIP_TRY(hipMemcpyAsync(d_gains + 2 * L * H, w->g_final, H * 2, hipMemcpyDeviceToDevice, s), "copy gain");
+  {  // RoPE: angle p * theta^(-2j/D) in double, cos/sin rounded to float
+    std::vector<float2> cs(size_t(S) * (D / 2));
+    for (int64_t p = 0; p < S; ++p)
+      for (int64_t j = 0; j < D / 2; ++j) {
+        const double a = double(p) * std::pow(double(d.rope_theta), -2.0 * double(j) / double(D));
+        cs[p * (D / 2) + j] = float2{float(std::cos(a)), float(std::sin(a))};
+      }
+    HIP_TRY(hipMemcpy(d_rope, cs.data(), cs.size() * sizeof(float2), hipMemcpyHostToDevice), "copy rope table");
+  }
+  {  // pack weights
+    std::vector<PackSrc> srcs(L + 1);
+    for (int l = 0; l < L; ++l) {
+      const mk_layer_weights& Lw = w->layers[l];
+      srcs[l] = PackSrc{{static_cast<const uint16_t*>(Lw.wq), static_cast<const uint16_t*>(Lw.wk),
+                         static_cast<const uint16_t*>(Lw.wv), static_cast<const uint16_t*>(Lw.wo),
+                         static_cast<const uint16_t*>(Lw.wg), static_cast<const uint16_t*>(Lw.wu),
+                         static_cast<const uint16_t*>(Lw.wd)}};
+    }
+    srcs[L] = PackSrc{{static_cast<const uint16_t*>(d.tied_embeddings ? w->embed : w->lm_head)}};
+    PackJob* d_jobs;
+    PackSrc* d_srcs;
+    void *pj = nullptr, *ps = nullptr;
+    HIP_TRY(hipMalloc(&pj, jobs.size() * sizeof(PackJob)), "hipMalloc pack jobs");
+    d_jobs = static_cast<PackJob*>(pj);
+    hipError_t e = hipMalloc(&ps, srcs.size() * sizeof(PackSrc));
+    if (e != hipSuccess) { (void)hipFree(pj); return hip_fail(e, "hipMalloc pack sources"); }
+    d_srcs = static_cast<PackSrc*>(ps);
+    e = hipMemcpy(d_jobs, jobs.data(), jobs.size() * sizeof(PackJob), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(d_srcs, srcs.data(), srcs.size() * sizeof(PackSrc), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = launch_pack(d_jobs, static_cast<int>(jobs.size()), d_srcs, d_wpack, G, d.head_dim, d.n_layers, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    (void)hipFree(pj);
+    (void)hipFree(ps);
+    if (e != hipSuccess) return hip_fail(e, "weight packing");
+  }
+
+  float *d_x, *d_qkv, *d_pml, *d_pacc, *d_attn, *d_mlp, *d_lmv;
+  int32_t *d_lmi, *d_tok, *d_status, *d_abort;
+  const int64_t Nc = g.opts.attn_chunks;
+  if ((rc = m->alloc(&d_x, B * H, "x")) || (rc = m->alloc(&d_qkv, B * Hkv * (G + 2) * D, "qkv")) ||
+      (rc = m->alloc(&d_pml, B * Hq * Nc * 2, "attention partials")) ||
+      (rc = m->alloc(&d_pacc, B * Hq * Nc * D, "attention partials")) || (rc = m->alloc(&d_attn, B * Hq * D, "attn")) ||
+      (rc = m->alloc(&d_mlp, B * F, "mlp")) || (rc = m->alloc(&d_lmv, B * nlm, "lm partials")) ||
+      (rc = m->alloc(&d_lmi, B * nlm, "lm partials")) || (rc = m->alloc(&d_tok, B, "tokens")) ||
+      (rc = m->alloc(&d_status, 1, "status")) || (rc = m->alloc(&d_abort, 1, "abort flag")))
+    return rc;
+  HIP_TRY(hipMemset(d_status, 0, 4), "clear status");
+  HIP_TRY(hipMemset(d_abort, 0, 4), "clear abort flag");
+  HIP_TRY(hipMemset(d_tok, 0, B * 4), "clear tokens");
+  HIP_TRY(hipStreamSynchronize(s), "load synchronisation");
+
+  P.tasks = d_tasks;
+  P.queue_ptr = d_qptr;
+  P.queue_ids = d_qids;
+  P.thresholds = d_thr;
+  P.counters = d_cnt;
+  P.n_tasks = static_cast<int32_t>(g.tasks.size());
+  P.L = d.n_layers; P.H = d.hidden; P.Hq = d.n_q_heads; P.Hkv = d.n_kv_heads; P.D = d.head_dim; P.F = d.ffn;
+  P.V = d.vocab; P.G = G; P.B = d.max_batch; P.S = d.max_seq; P.Nc = g.opts.attn_chunks; P.n_lm = nlm;
+  P.kb_h = kb_h; P.kb_qd = kb_qd; P.kb_f = kb_f;
+  P.eps = d.rms_eps;
+  P.attn_scale = static_cast<float>(1.0 / std::sqrt(double(d.head_dim)));
+  P.kp = kp;
+  P.vrow_stride = max_vrows;
+  P.ncap = ncap;
+  P.wpack = d_wpack;
+  P.embed = d_embed;
+  P.gains = d_gains;
+  P.kcache = static_cast<uint16_t*>(w->k_cache);
+  P.vcache = static_cast<uint16_t*>(w->v_cache);
+  P.rope_cs = d_rope;
+  P.x = d_x; P.qkv = d_qkv; P.part_ml = d_pml; P.part_acc = d_pacc; P.attn = d_attn; P.mlp = d_mlp;
+  P.lm_val = d_lmv; P.lm_idx = d_lmi; P.tok_cur = d_tok; P.status = d_status; P.abort_flag = d_abort;
+  *out = m;
+  m = nullptr;  // ownership passes to the caller
+  return MK_OK;
+}
+
+static int check_call(mk_model* m, const int32_t* tok, const int32_t* pos, int32_t batch, const void* outp) {
+  if (!m) return fail(MK_EINVAL, "NULL model");
+  if (!tok || !pos || !outp) return fail(MK_EINVAL, "NULL token, position or output pointer");
+  if (batch < 1 || batch > m->g.desc.max_batch)
+    return fail(MK_EINVAL, "batch must be in 1..max_batch (" + std::to_string(m->g.desc.max_batch) + ")");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != m->device)
+    return fail(MK_EINVAL, "the current HIP device is not the model's device");
+  return MK_OK;
+}
+
+static int prepare_epoch(mk_model* m, int32_t n_steps, hipStream_t s) {
+  const uint64_t top = (uint64_t(m->epoch) + uint64_t(n_steps) + 1) * m->max_threshold;
+  if (m->need_reset || top >= (1ull << 31)) {
+    HIP_TRY(hipMemsetAsync(const_cast<uint32_t*>(m->base.counters), 0, m->g.events.size() * 4, s), "reset counters");
+    HIP_TRY(hipMemsetAsync(m->base.abort_flag, 0, 4, s), "reset abort flag");
+    m->epoch = 0;
+    m->need_reset = false;
+  }
+  return MK_OK;
+}
+
+static int run_megakernel(mk_model* m, const int32_t* tok, const int32_t* pos, int32_t batch, int32_t n_steps,
+                          int32_t* out_tokens, float* logits, hipStream_t s) {
+  int rc = prepare_epoch(m, n_steps, s);
+  if (rc) return rc;
+  mk::Params P = m->base;
+  P.tokens_in = tok;
+  P.pos_in = pos;
+  P.out_tokens = out_tokens;
+  P.logits_out = logits;
+  P.batch = batch;
+  P.n_steps = n_steps;
+  P.epoch0 = m->epoch;
+  P.timeout_ticks = m->timeout_ticks;
+  P.drop_task = m->drop_task;
+  P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * 32) ? m->profile : nullptr;
+  HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
+  m->epoch += static_cast<uint32_t>(n_steps);
+  return MK_OK;
+}
+
+int mk_decode_step(mk_model* m, const int32_t* d_tokens, const int32_t* d_pos, int32_t batch, float* d_logits,
+                   int32_t* d_next, int32_t mode, void* stream) {
+  int rc = check_call(m, d_tokens, d_pos, batch, d_next);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == MK_MODE_MEGAKERNEL) return run_megakernel(m, d_tokens, d_pos, batch, 1, d_next, d_logits, s);
+  if (mode != MK_MODE_OPLAUNCH) return fail(MK_EINVAL, "mk_decode_step: unknown mode");
+  mk::Params P = m->base;
+  P.tokens_in = d_tokens;
+  P.pos_in = d_pos;
+  P.out_tokens = d_next;
+  P.logits_out = d_logits;
+  P.batch = batch;
+  P.n_steps = 1;
+  P.epoch0 = 0;
+  P.timeout_ticks = m->timeout_ticks;
+  P.drop_task = -1;
+  for (const auto& op : m->g.ops)
+    HIP_TRY(mk::launch_op(P, op.first, op.second - op.first, m->lds_bytes, s), "hipLaunchKernel(mk_oplaunch)");
+  return MK_OK;
+}
+
+int mk_generate(mk_model* m, const int32_t* d_tokens0, const int32_t* d_pos0, int32_t batch, int32_t n_steps,
+                int32_t* d_out_tokens, float* d_last_logits, void* stream) {
+  int rc = check_call(m, d_tokens0, d_pos0, batch, d_out_tokens);
+  if (rc) return rc;
+  if (n_steps < 1) return fail(MK_EINVAL, "mk_generate: n_steps must be >= 1");
+  return run_megakernel(m, d_tokens0, d_pos0, batch, n_steps, d_out_tokens, d_last_logits,
+                        static_cast<hipStream_t>(stream));
+}
+
+int mk_check(mk_model* m, void* stream) {
+  if (!m) return fail(MK_EINVAL, "mk_check: NULL model");
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+  int32_t st = 0;
+  HIP_TRY(hipMemcpy(&st, m->base.status, 4, hipMemcpyDeviceToHost), "read status");
+  if (st == 0) return MK_OK;
+  HIP_TRY(hipMemset(m->base.status, 0, 4), "clear status");
+  if (st & mk::kStatusTimeout) {
+    m->need_reset = true;
+    return fail(MK_ETIMEOUT, "device watchdog expired; counters are reset on the next call");
+  }
+  return fail(MK_EDEVICE, std::string("device argument error:") + ((st & mk::kStatusBadToken) ? " token>=vocab" : "") +
+                              ((st & mk::kStatusBadPos) ? " position>=max_seq" : ""));
+}
+
+int mk_set_watchdog_ms(mk_model* m, int32_t ms) {
+  if (!m || ms < 0) return fail(MK_EINVAL, "mk_set_watchdog_ms: bad argument");
+  m->timeout_ticks = uint64_t(ms ? ms : 2000) * 100000ull;
+  return MK_OK;
+}
+
+int mk_debug_drop_signal(mk_model* m, int32_t task_id) {
+  if (!m || task_id < -1 || task_id >= static_cast<int32_t>(m->g.tasks.size()))
+    return fail(MK_EINVAL, "mk_debug_drop_signal: bad argument");
+  m->drop_task = task_id;
+  return MK_OK;
+}
+
+int mk_set_profile_buffer(mk_model* m, void* d_buf, size_t bytes) {
+  if (!m) return fail(MK_EINVAL, "mk_set_profile_buffer: NULL model");
+  if (d_buf && bytes < m->g.tasks.size() * 32) return fail(MK_EINVAL, "mk_set_profile_buffer: buffer too small");
+  m->profile = static_cast<uint64_t*>(d_buf);
+  m->profile_bytes = d_buf ? bytes : 0;
+  return MK_OK;
+}
+
+int mk_model_info(const mk_model* m, uint64_t* packed_weight_bytes, int32_t* num_cus, int32_t* n_tasks) {
+  if (!m) return fail(MK_EINVAL, "mk_model_info: NULL model");
+  if (packed_weight_bytes) *packed_weight_bytes = m->packed_bytes;
+  if (num_cus) *num_cus = m->g.opts.num_cus;
+  if (n_tasks) *n_tasks = static_cast<int32_t>(m->g.tasks.size());
+  return MK_OK;
+}
+
+void mk_free_model(mk_model* m) { delete m; }
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+// Host compiler: operator list of one decode step -> tasks, events with
+// thresholds, round-robin per-compute-unit queues, canonical bytes.
+//
+// The operator order is the pages' wiring of one step (MPK walk-through
+// section 3.3.1, build_mirage_graph; Hazy megakernel summary, fused
+// instruction list). The partition, event and byte-format rules are this
+// project's specification (design record, section 1); oracle/graph.py
+// implements the same specification separately and the tests compare bytes.
+#include "graph.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace mk {
+namespace {
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Builder {
+  Graph* g;
+  int32_t new_event(int32_t threshold) {
+    g->events.push_back(Event{threshold, -1, 0});
+    return static_cast<int32_t>(g->events.size()) - 1;
+  }
+  // Appends one operator's tasks, placing its i-th task on unit i mod N.
+  void add_op(std::vector<Task>&& op) {
+    const int32_t n = g->opts.num_cus;
+    const int32_t begin = static_cast<int32_t>(g->tasks.size());
+    for (size_t i = 0; i < op.size(); ++i) {
+      op[i].cu = static_cast<int32_t>(i % n);
+      g->tasks.push_back(op[i]);
+    }
+    g->ops.emplace_back(begin, static_cast<int32_t>(g->tasks.size()));
+  }
+};
+
+Task blank(int32_t type) { return Task{type, -1, -1, -1, -1, -1, -1, -1, -1, -1}; }
+
+// rows -> T ranges made of whole blocks of rb rows (balanced over blocks).
+std::vector<std::pair<int32_t, int32_t>> row_split(int32_t rows, int32_t T, int32_t rb) {
+  std::vector<std::pair<int32_t, int32_t>> r;
+  const int64_t nb = cdiv(rows, rb);
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t b0 = t * nb / T, b1 = (t + 1) * nb / T;
+    r.emplace_back(static_cast<int32_t>(b0 * rb), static_cast<int32_t>(std::min<int64_t>(rows, b1 * rb)));
+  }
+  return r;
+}
+
+}  // namespace
+
+int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std::string* err) {
+  auto fail = [&](const char* m) { *err = m; return MK_EINVAL; };
+  if (d.n_layers < 1 || d.hidden < 1 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.head_dim < 2 ||
+      d.ffn < 1 || d.vocab < 1 || d.max_batch < 1 || d.max_seq < 1)
+    return fail("mk_model_desc: every size must be positive");
+  if (d.n_q_heads % d.n_kv_heads) return fail("n_q_heads must be a multiple of n_kv_heads");
+  if (d.head_dim % 8) return fail("head_dim must be a multiple of 8");
+  if (d.hidden % 8 || d.ffn % 8) return fail("hidden and ffn must be multiples of 8");
+  if (!(d.rms_eps >= 0.f) || !(d.rope_theta > 0.f)) return fail("rms_eps >= 0 and rope_theta > 0 required");
+  mk_graph_opts o{};
+  if (in) o = *in;
+  if (o.num_cus < 0 || o.qkv_tasks_per_group < 0 || o.o_tasks < 0 || o.gu_tasks < 0 || o.d_tasks < 0 ||
+      o.lm_tasks < 0 || o.attn_chunks < 0 || o.row_block < 0)
+    return fail("mk_graph_opts: negative option");
+
+  const int32_t N = o.num_cus ? o.num_cus : 256;
+  const int32_t rb = o.row_block ? o.row_block : (d.max_batch == 1 ? 4 : 16);
+  const int32_t Hkv = d.n_kv_heads, G = d.n_q_heads / d.n_kv_heads, B = d.max_batch;
+  const int32_t grp_rows = (G + 2) * d.head_dim;
+  auto cap = [&](int32_t req, int32_t rows) {
+    return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(req, cdiv(rows, rb))));
+  };
+  mk_graph_opts r{};
+  r.num_cus = N;
+  r.row_block = rb;
+  r.qkv_tasks_per_group = cap(o.qkv_tasks_per_group ? o.qkv_tasks_per_group : cdiv(N, Hkv), grp_rows);
+  r.o_tasks = cap(o.o_tasks ? o.o_tasks : N, d.hidden);
+  r.gu_tasks = cap(o.gu_tasks ? o.gu_tasks : N, d.ffn);
+  r.d_tasks = cap(o.d_tasks ? o.d_tasks : N, d.hidden);
+  r.lm_tasks = cap(o.lm_tasks ? o.lm_tasks : N, d.vocab);
+  r.attn_chunks = o.attn_chunks
+                      ? o.attn_chunks
+                      : std::max(1, std::min(N / (B * Hkv), std::max(1, d.max_seq / 16)));
+  const int32_t Nc = r.attn_chunks;
+
+  Graph& g = *out;
+  g = Graph{};
+  g.desc = d;
+  g.opts = r;
+  Builder bld{&g};
+
+  // events in creation order
+  const int32_t e_tok = bld.new_event(B);
+  const int32_t e_emb = bld.new_event(B);
+  const int32_t L = d.n_layers;
+  std::vector<int32_t> e_qkv(size_t(L) * Hkv), e_att(size_t(L) * Hkv * B), e_comb(L), e_o(L), e_gu(L), e_d(L);
+  for (int32_t l = 0; l < L; ++l) {
+    for (int32_t gi = 0; gi < Hkv; ++gi) e_qkv[size_t(l) * Hkv + gi] = bld.new_event(r.qkv_tasks_per_group);
+    for (int32_t gi = 0; gi < Hkv; ++gi)
+      for (int32_t b = 0; b < B; ++b) e_att[(size_t(l) * Hkv + gi) * B + b] = bld.new_event(Nc);
+    e_comb[l] = bld.new_event(Hkv * B);
+    e_o[l] = bld.new_event(r.o_tasks);
+    e_gu[l] = bld.new_event(r.gu_tasks);
+    e_d[l] = bld.new_event(r.d_tasks);
+  }
+  const int32_t e_lm = bld.new_event(r.lm_tasks);
+
+  {  // embedding
+    std::vector<Task> op;
+    for (int32_t b = 0; b < B; ++b) {
+      Task t = blank(T_EMB);
+      t.b = b; t.dep = e_tok; t.trig = e_emb;
+      op.push_back(t);
+    }
+    bld.add_op(std::move(op));
+  }
+  for (int32_t l = 0; l < L; ++l) {
+    const int32_t dep_in = l == 0 ? e_emb : e_d[l - 1];
+    {
+      std::vector<Task> op;
+      const auto split = row_split(grp_rows, r.qkv_tasks_per_group, rb);
+      for (int32_t gi = 0; gi < Hkv; ++gi)
+        for (const auto& rr : split) {
+          Task t = blank(T_QKV);
+          t.layer = l; t.g = gi; t.row0 = rr.first; t.row1 = rr.second;
+          t.dep = dep_in; t.trig = e_qkv[size_t(l) * Hkv + gi];
+          op.push_back(t);
+        }
+      bld.add_op(std::move(op));
+    }
+    {
+      std::vector<Task> op;
+      for (int32_t gi = 0; gi < Hkv; ++gi)
+        for (int32_t b = 0; b < B; ++b)
+          for (int32_t c = 0; c < Nc; ++c) {
+            Task t = blank(T_ATT);
+            t.layer = l; t.g = gi; t.b = b; t.chunk = c;
+            t.dep = e_qkv[size_t(l) * Hkv + gi]; t.trig = e_att[(size_t(l) * Hkv + gi) * B + b];
+            op.push_back(t);
+          }
+      bld.add_op(std::move(op));
+    }
+    {
+      std::vector<Task> op;
+      for (int32_t gi = 0; gi < Hkv; ++gi)
+        for (int32_t b = 0; b < B; ++b) {
+          Task t = blank(T_COMB);
+          t.layer = l; t.g = gi; t.b = b;
+          t.dep = e_att[(size_t(l) * Hkv + gi) * B + b]; t.trig = e_comb[l];
+          op.push_back(t);
+        }
+      bld.add_op(std::move(op));
+    }
+    struct RowOp { int32_t type, rows, tasks, dep, trig; };
+    const RowOp row_ops[3] = {{T_O, d.hidden, r.o_tasks, e_comb[l], e_o[l]},
+                              {T_GU, d.ffn, r.gu_tasks, e_o[l], e_gu[l]},
+                              {T_D, d.hidden, r.d_tasks, e_gu[l], e_d[l]}};
+    for (const RowOp& ro : row_ops) {
+      std::vector<Task> op;
+      for (const auto& rr : row_split(ro.rows, ro.tasks, rb)) {
+        Task t = blank(ro.type);
+        t.layer = l; t.row0 = rr.first; t.row1 = rr.second; t.dep = ro.dep; t.trig = ro.trig;
+        op.push_back(t);
+      }
+      bld.add_op(std::move(op));
+    }
+  }
+  {
+    std::vector<Task> op;
+    for (const auto& rr : row_split(d.vocab, r.lm_tasks, rb)) {
+      Task t = blank(T_LM);
+      t.row0 = rr.first; t.row1 = rr.second; t.dep = e_d[L - 1]; t.trig = e_lm;
+      op.push_back(t);
+    }
+    bld.add_op(std::move(op));
+  }
+  {
+    std::vector<Task> op;
+    for (int32_t b = 0; b < B; ++b) {
+      Task t = blank(T_ARGMAX);
+      t.b = b; t.dep = e_lm; t.trig = e_tok;
+      op.push_back(t);
+    }
+    bld.add_op(std::move(op));
+  }
+
+  for (size_t i = 0; i < g.tasks.size(); ++i) {
+    Event& ev = g.events[g.tasks[i].dep];
+    if (ev.n_dependents == 0) ev.first_dependent = static_cast<int32_t>(i);
+    ++ev.n_dependents;
+  }
+  g.queues.assign(N, {});
+  for (size_t i = 0; i < g.tasks.size(); ++i) g.queues[g.tasks[i].cu].push_back(static_cast<int32_t>(i));
+  return MK_OK;
+}
+
+namespace {
+struct Writer {
+  std::vector<uint8_t> b;
+  void u32(uint32_t v) { for (int i = 0; i < 4; ++i) b.push_back(uint8_t(v >> (8 * i))); }
+  void i32(int32_t v) { u32(static_cast<uint32_t>(v)); }
+  void f32(float v) { uint32_t u; std::memcpy(&u, &v, 4); u32(u); }
+};
+}  // namespace
+
+std::vector<uint8_t> serialize(const Graph& g) {
+  Writer w;
+  const char magic[8] = {'M', 'K', 'G', 'R', 'A', 'P', 'H', '1'};
+  w.b.insert(w.b.end(), magic, magic + 8);
+  w.u32(1);
+  const mk_model_desc& d = g.desc;
+  for (int32_t v : {d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab,
+                    d.tied_embeddings, d.max_batch, d.max_seq})
+    w.i32(v);
+  w.f32(d.rms_eps);
+  w.f32(d.rope_theta);
+  const mk_graph_opts& o = g.opts;
+  for (int32_t v : {o.num_cus, o.qkv_tasks_per_group, o.o_tasks, o.gu_tasks, o.d_tasks, o.lm_tasks,
+                    o.attn_chunks, o.row_block})
+    w.i32(v);
+  w.i32(static_cast<int32_t>(g.tasks.size()));
+  w.i32(static_cast<int32_t>(g.events.size()));
+  for (const Task& t : g.tasks)
+    for (int32_t v : {t.type, t.layer, t.b, t.g, t.chunk, t.row0, t.row1, t.dep, t.trig, t.cu}) w.i32(v);
+  for (const Event& e : g.events)
+    for (int32_t v : {e.threshold, e.first_dependent, e.n_dependents}) w.i32(v);
+  for (const auto& q : g.queues) {
+    w.i32(static_cast<int32_t>(q.size()));
+    for (int32_t id : q) w.i32(id);
+  }
+  return w.b;
+}
+
+}  // namespace mk

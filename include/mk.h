@@ -1,0 +1,177 @@
+/*
+ * mk.h -- C ABI of the MI355X persistent decode megakernel (libmk.so).
+ *
+ * One autoregressive decode step of a Llama-style decoder runs as a static,
+ * fine-grained task graph inside one long-lived HIP kernel (MPK blog
+ * translation, "MPK runtime" section and Figure 3; MPK walk-through sections
+ * 0.2 and 3.2; Hazy megakernel summary: one kernel per forward pass).
+ *
+ * Conventions for every call:
+ *  - Return value: MK_OK (0) or a negative MK_E* code. No exception crosses the
+ *    ABI. mk_last_error() returns a thread-local message for the last failure.
+ *  - "device pointer" = memory on the current HIP device (e.g. torch tensor
+ *    data_ptr()); "host pointer" = ordinary CPU memory.
+ *  - Streams are hipStream_t passed as void* (NULL = the null stream).
+ *  - Nothing here allocates or frees caller memory; the library owns only what
+ *    its own mk_* objects hold and releases it in mk_free_*.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MK_OK            0
+#define MK_EINVAL       (-1)   /* bad argument (shape, NULL, range) */
+#define MK_ENOMEM       (-2)   /* device or host allocation failed */
+#define MK_EHIP         (-3)   /* a HIP runtime call failed */
+#define MK_ETIMEOUT     (-4)   /* device watchdog expired inside the kernel */
+#define MK_EUNSUPPORTED (-5)   /* shape/option/device this build cannot run */
+#define MK_EDEVICE      (-6)   /* device-side argument error (token or position out of range) */
+
+/* decode modes for mk_decode_step */
+#define MK_MODE_MEGAKERNEL 0   /* one persistent launch runs the whole step */
+#define MK_MODE_OPLAUNCH   1   /* one launch per operator, same task bodies (baseline) */
+
+/* Model shape (MPK walk-through 3.3.1: hidden size, heads, kv heads, head dim,
+ * vocab; max_seq_length in the PersistentKernel constructor). tied_embeddings
+ * = 1 uses the embedding as LM head. rms_eps is added inside the square root of
+ * RMSNorm; rope_theta is the RoPE base (half-split pairs, no scaling). */
+typedef struct mk_model_desc {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+    int32_t tied_embeddings, max_batch, max_seq;
+    float rms_eps, rope_theta;
+} mk_model_desc;
+
+/* Task-graph knobs (MPK walk-through 3.3.1: per-layer grid sizes and worker
+ * counts). 0 = default; the defaults and the partition rules are a pure
+ * function of (desc, num_cus) and are spelled out with the canonical byte
+ * format in the design record. */
+typedef struct mk_graph_opts {
+    int32_t num_cus;             /* compute units = workgroups of the persistent kernel */
+    int32_t qkv_tasks_per_group; /* QKV tasks per kv head group */
+    int32_t o_tasks, gu_tasks, d_tasks, lm_tasks;
+    int32_t attn_chunks;         /* attention position chunks per (kv group, sequence) */
+    int32_t row_block;           /* rows per matvec block (task row ranges are whole blocks) */
+} mk_graph_opts;
+
+typedef struct mk_graph mk_graph;   /* host-only task graph */
+typedef struct mk_model mk_model;   /* graph + packed weights + device state */
+
+/* Per-layer weights: device pointers to bf16, HF layout [out, in] row-major.
+ * wq [Hq*D, H], wk/wv [Hkv*D, H], wo [H, Hq*D], wg/wu [F, H], wd [H, F],
+ * g_attn/g_mlp [H] (RMSNorm gains). */
+typedef struct mk_layer_weights {
+    const void *wq, *wk, *wv, *wo, *wg, *wu, *wd, *g_attn, *g_mlp;
+} mk_layer_weights;
+
+/* All model tensors (MPK walk-through 3.3.1: attach_input of every weight and
+ * of the per-layer k_cache / v_cache). embed [V, H] bf16; lm_head [V, H] bf16 or
+ * NULL when tied; g_final [H] bf16; layers = HOST array of n_layers entries.
+ * k_cache / v_cache: bf16 [L][max_batch][Hkv][max_seq][D], caller-owned decode
+ * state that must stay alive and unmoved while the model is used; keys are
+ * stored after RoPE. */
+typedef struct mk_weights {
+    const void *embed, *lm_head, *g_final;
+    const mk_layer_weights *layers;
+    void *k_cache, *v_cache;
+} mk_weights;
+
+/* Split each operator of one decode step into per-compute-unit tasks joined by
+ * events with trigger thresholds, and place them round-robin on per-unit queues
+ * (MPK blog translation, "MPK compiler" section and Figure 2; MPK walk-through
+ * 3.2 task-graph generation: dependency analysis, event generation, TaskDesc /
+ * EventDesc). Host only; touches no device. *out receives a new graph the
+ * caller frees with mk_free_graph. opts may be NULL (all defaults).
+ * Errors: MK_EINVAL for an inconsistent shape (Hq not a multiple of Hkv, odd
+ * head_dim, K dims not multiples of 8, ...), MK_ENOMEM. */
+int mk_build_task_graph(const mk_model_desc *desc, const mk_graph_opts *opts, mk_graph **out);
+
+/* Canonical little-endian bytes of the graph (header, tasks, events, queues).
+ * Writes at most cap bytes into buf (buf may be NULL with cap 0 to query) and
+ * always stores the full length in *len. MK_EINVAL if buf is too small. */
+int mk_graph_serialize(const mk_graph *g, uint8_t *buf, size_t cap, size_t *len);
+
+/* Counts and the resolved (default-filled) options of a graph. Any output
+ * pointer may be NULL. */
+int mk_graph_info(const mk_graph *g, int32_t *n_tasks, int32_t *n_events, mk_graph_opts *resolved);
+
+void mk_free_graph(mk_graph *g);
+
+/* Bind a graph to the current HIP device: pack the weights into the library's
+ * tile-major copy (QKV rows grouped per kv head and gate/up rows interleaved per
+ * block, as fuse_tensors does in MPK walk-through 3.3.1), upload task
+ * descriptors, per-unit queues, event thresholds and counters, build the RoPE
+ * cos/sin tables, and allocate the activation workspace (MPK walk-through 3.2,
+ * runtime initialisation). Weight pointers may be freed after this returns; the
+ * KV cache may not. Work is enqueued on `stream` and completed before return.
+ * *out receives a model the caller frees with mk_free_model (after its work
+ * has finished). The graph may be freed afterwards.
+ * Errors: MK_EINVAL (NULL pointer), MK_EUNSUPPORTED (fewer resident compute
+ * units than num_cus, shape outside this build), MK_ENOMEM, MK_EHIP. */
+int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_model **out);
+
+/* One decode step for `batch` (1..max_batch) sequences: feed d_tokens[b] at
+ * position d_pos[b], write K/V there, attend over 0..d_pos[b], and write the
+ * greedy next token to d_next[b] and (if d_logits != NULL) the fp32 logits to
+ * d_logits [batch, V] row-major. All four arrays are device pointers (int32 /
+ * fp32). mode MK_MODE_MEGAKERNEL = one persistent launch; MK_MODE_OPLAUNCH = one
+ * launch per operator with the same task bodies. Asynchronous on `stream`;
+ * argument errors return synchronously. Device-side errors (token >= V,
+ * position >= max_seq, watchdog) are recorded in the model's status word and
+ * returned by mk_check or by the next call. */
+int mk_decode_step(mk_model *m, const int32_t *d_tokens, const int32_t *d_pos, int32_t batch,
+                   float *d_logits, int32_t *d_next, int32_t mode, void *stream);
+
+/* n_steps greedy decode steps inside ONE persistent launch (MPK walk-through
+ * 0.2: the CPU launches once; the step counter and token buffer live on the
+ * device). Step k feeds, for every sequence b, d_tokens0[b] (k = 0) or the
+ * token chosen at step k-1, at position d_pos0[b] + k. Chosen tokens go to
+ * d_out_tokens [n_steps, batch] (int32, device); if d_last_logits != NULL the
+ * fp32 logits of the final step go there [batch, V]. Asynchronous on `stream`;
+ * errors as for mk_decode_step. */
+int mk_generate(mk_model *m, const int32_t *d_tokens0, const int32_t *d_pos0, int32_t batch,
+                int32_t n_steps, int32_t *d_out_tokens, float *d_last_logits, void *stream);
+
+/* Synchronise `stream`, then read and clear the model's device status word.
+ * Returns MK_OK, MK_EDEVICE (token or position out of range was seen; the
+ * offending task was skipped), or MK_ETIMEOUT (a wait exceeded the watchdog;
+ * every wave left the kernel). After MK_ETIMEOUT the event counters are reset
+ * on the next call. */
+int mk_check(mk_model *m, void *stream);
+
+/* Watchdog bound for every wait inside the persistent kernel, in
+ * milliseconds (default 2000). 0 restores the default. */
+int mk_set_watchdog_ms(mk_model *m, int32_t ms);
+
+/* Fault injection for testing the watchdog: the task with global id
+ * `task_id` (in every step of later megakernel calls) finishes without adding
+ * to its triggering event, so its dependents wait until the watchdog expires
+ * and every wave leaves the kernel. -1 disables. MK_EINVAL if out of range. */
+int mk_debug_drop_signal(mk_model *m, int32_t task_id);
+
+/* Optional per-task timeline (MPK walk-through 3.3.1: profiler_tensor).
+ * d_buf: device buffer of `bytes` bytes receiving, for each executed task of
+ * the last megakernel call, 4 x uint64 {task_id | cu << 32, t_ready, t_start,
+ * t_end} in 100 MHz constant-clock ticks, slot = step * n_tasks + task id.
+ * NULL disables. MK_EINVAL if bytes is too small for one step. */
+int mk_set_profile_buffer(mk_model *m, void *d_buf, size_t bytes);
+
+/* Device bytes the model reads per step for its weights (packed copy, padding
+ * included) -- the numerator of the roofline. */
+int mk_model_info(const mk_model *m, uint64_t *packed_weight_bytes, int32_t *num_cus,
+                  int32_t *n_tasks);
+
+void mk_free_model(mk_model *m);
+
+const char *mk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */
