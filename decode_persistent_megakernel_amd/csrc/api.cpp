@@ -117,8 +117,6 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
       return fail(MK_EINVAL, "mk_load_weights: NULL layer weight");
   }
   const int G = d.n_q_heads / d.n_kv_heads;
-  if (G > 8) return fail(MK_EUNSUPPORTED, "mk_load_weights: more than 8 query heads per kv head");
-  if (G * d.head_dim > 1024) return fail(MK_EUNSUPPORTED, "mk_load_weights: (Hq/Hkv)*head_dim > 1024");
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   mk_model* m = new (std::nothrow) mk_model;
@@ -147,7 +145,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   for (size_t i = 0; i < g.tasks.size(); ++i) {
     const Task& t = g.tasks[i];
     DevTask& x = dt[i];
-    x = DevTask{t.type, t.layer, t.b, t.g, t.chunk, t.row0, t.row1, t.dep, t.trig, ordinal_in_op[i], 0, 0, 0};
+    x = DevTask{t.type, t.layer, t.b, t.g, t.chunk, t.row0, t.row1, t.dep, t.trig, ordinal_in_op[i], 0, 0, 0, 0, 0};
     int K = 0, KB = 0;
     switch (t.type) {
       case T_QKV: case T_GU: case T_LM: K = d.hidden; KB = kb_h; break;
@@ -157,24 +155,59 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
     }
     if (KB == 0) continue;
     const int nrb = static_cast<int>(cdiv(t.row1 - t.row0, kUnitRows));
-    x.n_vrb = t.type == T_GU ? 2 * nrb : nrb;
-    x.n_units = x.n_vrb * KB;
+    const int n_vrb = t.type == T_GU ? 2 * nrb : nrb;
+    x.n_units = n_vrb * KB;
+    x.kb = KB;
+    x.kdim = K;
     x.w_off = static_cast<int64_t>(off);
-    max_vrows = std::max(max_vrows, x.n_vrb * kUnitRows);
-    jobs.push_back(PackJob{x.w_off, t.type, t.layer, t.g, t.row0, t.row1, K, KB, x.n_vrb});
+    max_vrows = std::max(max_vrows, n_vrb * kUnitRows);
+    jobs.push_back(PackJob{x.w_off, t.type, t.layer, t.g, t.row0, t.row1, K, KB, n_vrb});
     off += uint64_t(x.n_units) * kUnitBytes;
   }
   m->packed_bytes = off;
 
   // --- LDS budget -------------------------------------------------------------
-  const int ncap = std::min<int>(d.max_batch, kMaxCols);
-  const int kp = std::max({kb_h, kb_qd, kb_f}) * kUnitCols;
-  const int att_floats = G * d.head_dim + 2 * d.head_dim + 3 * G + G * kAttTile;
-  const size_t lds = 128 * 4 + size_t(4) * (size_t(ncap) * kp + size_t(kWaves) * ncap * max_vrows + att_floats);
+  const int D = d.head_dim;
   if (d.max_batch > kMaxCols)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: max_batch above 4 is not supported by the VALU task bodies");
-  if (lds > 160 * 1024)
-    return fail(MK_EUNSUPPORTED, "mk_load_weights: shape needs " + std::to_string(lds) + " bytes of LDS (> 160 KiB)");
+  if (G > kMaxG) return fail(MK_EUNSUPPORTED, "mk_load_weights: more than 4 query heads per kv head");
+  if (64 % (D / 8) != 0) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim/8 must divide 64");
+  if (d.hidden > 4096) return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden above 4096");
+  if (std::max({kb_h, kb_qd, kb_f}) > 255) return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32640");
+  // LDS: control words, two small staging slots, one big slot (down-projection
+  // inputs and attention merges), three partial-sum areas, then the rings.
+  // Staged copies move whole 1 KiB pieces, so every region is rounded up to
+  // 256 floats where a copy lands.
+  auto r256 = [](int64_t n) { return (n + 255) / 256 * 256; };
+  const int ncap = std::min<int>(d.max_batch, kMaxCols);
+  const int kp = static_cast<int>(r256(std::max(d.hidden, d.n_q_heads * D)));
+  const int kp_big = static_cast<int>(r256(d.ffn));
+  int nlm_tasks = 0;
+  for (const Task& t : g.tasks) nlm_tasks += t.type == T_LM;
+  const int64_t Ncx = g.opts.attn_chunks;
+  const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * max_vrows;
+  const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D;
+  const int64_t need_arg = r256(nlm_tasks) * 2;
+  const int64_t need_emb = r256(d.hidden / 2 + 1);
+  const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * max_vrows;
+  const int64_t need_comb = r256(int64_t(G) * Ncx * 2) + r256(int64_t(G) * Ncx * D);
+  const int64_t small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
+  const int64_t big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
+  const int64_t part_floats =
+      (std::max<int64_t>(int64_t(kPairs) * ncap * max_vrows, int64_t(kPairs) * G * (D + 2)) + 3) & ~int64_t(3);
+  const size_t fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats);
+  const size_t lds_max = 160 * 1024;
+  // ring entries are 2 KiB items (two units); a loader keeps up to 24 in flight
+  const int64_t item_bytes = 2 * kUnitBytes;
+  const int64_t ring = std::min<int64_t>(kMaxRing, (int64_t(lds_max) - int64_t(fixed)) / (kPairs * item_bytes));
+  static const int kInflight[] = {24, 20, 16, 12, 8};
+  int inflight = 0;
+  for (int v : kInflight)
+    if (v <= ring - 2) { inflight = v; break; }
+  if (inflight == 0)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: staging needs " + std::to_string(fixed) +
+                                     " bytes of LDS, leaving no room for the weight rings");
+  const size_t lds = fixed + size_t(kPairs) * size_t(ring) * size_t(item_bytes);
   m->lds_bytes = static_cast<int>(lds);
   HIP_TRY(set_lds_limit(m->lds_bytes), "hipFuncSetAttribute(max dynamic LDS)");
   int per_cu = 0;
@@ -187,7 +220,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   // --- device buffers -----------------------------------------------------------
   Params& P = m->base;
   P = Params{};
-  const int64_t H = d.hidden, V = d.vocab, L = d.n_layers, B = d.max_batch, S = d.max_seq, D = d.head_dim;
+  const int64_t H = d.hidden, V = d.vocab, L = d.n_layers, B = d.max_batch, S = d.max_seq;
   const int64_t Hq = d.n_q_heads, Hkv = d.n_kv_heads, F = d.ffn;
   int nlm = 0;
   for (const Task& t : g.tasks) nlm += t.type == T_LM;
@@ -197,7 +230,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   int rc;
   if ((rc = m->alloc(&d_tasks, dt.size(), "tasks")) || (rc = m->alloc(&d_qptr, g.queues.size() + 1, "queues")) ||
       (rc = m->alloc(&d_qids, g.tasks.size(), "queue ids")) || (rc = m->alloc(&d_thr, g.events.size(), "thresholds")) ||
-      (rc = m->alloc(&d_cnt, g.events.size(), "counters")))
+      (rc = m->alloc(&d_cnt, g.events.size() * kEventWords, "counters")))
     return rc;
   std::vector<int32_t> qptr(1, 0), qids;
   for (const auto& q : g.queues) {
@@ -213,12 +246,12 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   HIP_TRY(hipMemcpy(d_qptr, qptr.data(), qptr.size() * 4, hipMemcpyHostToDevice), "copy queue offsets");
   HIP_TRY(hipMemcpy(d_qids, qids.data(), qids.size() * 4, hipMemcpyHostToDevice), "copy queues");
   HIP_TRY(hipMemcpy(d_thr, thr.data(), thr.size() * 4, hipMemcpyHostToDevice), "copy thresholds");
-  HIP_TRY(hipMemset(d_cnt, 0, thr.size() * 4), "clear counters");
+  HIP_TRY(hipMemset(d_cnt, 0, thr.size() * 4 * kEventWords), "clear counters");
 
   uint8_t* d_wpack;
   uint16_t *d_embed, *d_gains;
   float2* d_rope;
-  if ((rc = m->alloc(&d_wpack, m->packed_bytes, "packed weights")) || (rc = m->alloc(&d_embed, V * H, "embedding")) ||
+  if ((rc = m->alloc(&d_wpack, m->packed_bytes, "packed weights")) || (rc = m->alloc(&d_embed, V * H + 512, "embedding")) ||
       (rc = m->alloc(&d_gains, (2 * L + 1) * H, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")))
     return rc;
   HIP_TRY(hipMemcpyAsync(d_embed, w->embed, V * H * 2, hipMemcpyDeviceToDevice, s), "copy embedding");
@@ -266,11 +299,13 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   float *d_x, *d_qkv, *d_pml, *d_pacc, *d_attn, *d_mlp, *d_lmv;
   int32_t *d_lmi, *d_tok, *d_status, *d_abort;
   const int64_t Nc = g.opts.attn_chunks;
-  if ((rc = m->alloc(&d_x, B * H, "x")) || (rc = m->alloc(&d_qkv, B * Hkv * (G + 2) * D, "qkv")) ||
-      (rc = m->alloc(&d_pml, B * Hq * Nc * 2, "attention partials")) ||
-      (rc = m->alloc(&d_pacc, B * Hq * Nc * D, "attention partials")) || (rc = m->alloc(&d_attn, B * Hq * D, "attn")) ||
-      (rc = m->alloc(&d_mlp, B * F, "mlp")) || (rc = m->alloc(&d_lmv, B * nlm, "lm partials")) ||
-      (rc = m->alloc(&d_lmi, B * nlm, "lm partials")) || (rc = m->alloc(&d_tok, B, "tokens")) ||
+  const int64_t slack = 4096;  // floats read past the end by 1 KiB-granular copies
+  if ((rc = m->alloc(&d_x, B * H + slack, "x")) || (rc = m->alloc(&d_qkv, B * Hkv * (G + 2) * D + slack, "qkv")) ||
+      (rc = m->alloc(&d_pml, B * Hq * Nc * 2 + slack, "attention partials")) ||
+      (rc = m->alloc(&d_pacc, B * Hq * Nc * D + slack, "attention partials")) ||
+      (rc = m->alloc(&d_attn, B * Hq * D + slack, "attn")) || (rc = m->alloc(&d_mlp, B * F + slack, "mlp")) ||
+      (rc = m->alloc(&d_lmv, B * nlm + slack, "lm partials")) || (rc = m->alloc(&d_lmi, B * nlm + slack, "lm partials")) ||
+      (rc = m->alloc(&d_tok, B + 64, "tokens")) ||
       (rc = m->alloc(&d_status, 1, "status")) || (rc = m->alloc(&d_abort, 1, "abort flag")))
     return rc;
   HIP_TRY(hipMemset(d_status, 0, 4), "clear status");
@@ -286,8 +321,13 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   P.n_tasks = static_cast<int32_t>(g.tasks.size());
   P.L = d.n_layers; P.H = d.hidden; P.Hq = d.n_q_heads; P.Hkv = d.n_kv_heads; P.D = d.head_dim; P.F = d.ffn;
   P.V = d.vocab; P.G = G; P.B = d.max_batch; P.S = d.max_seq; P.Nc = g.opts.attn_chunks; P.n_lm = nlm;
-  P.kb_h = kb_h; P.kb_qd = kb_qd; P.kb_f = kb_f;
   P.eps = d.rms_eps;
+  P.small_floats = static_cast<int32_t>(small_floats);
+  P.big_floats = static_cast<int32_t>(big_floats);
+  P.ring_slots = static_cast<int32_t>(ring);
+  P.ring_inflight = inflight;
+  P.kp_big = kp_big;
+  P.part_floats = static_cast<int32_t>(part_floats);
   P.attn_scale = static_cast<float>(1.0 / std::sqrt(double(d.head_dim)));
   P.kp = kp;
   P.vrow_stride = max_vrows;
@@ -319,7 +359,7 @@ static int check_call(mk_model* m, const int32_t* tok, const int32_t* pos, int32
 static int prepare_epoch(mk_model* m, int32_t n_steps, hipStream_t s) {
   const uint64_t top = (uint64_t(m->epoch) + uint64_t(n_steps) + 1) * m->max_threshold;
   if (m->need_reset || top >= (1ull << 31)) {
-    HIP_TRY(hipMemsetAsync(const_cast<uint32_t*>(m->base.counters), 0, m->g.events.size() * 4, s), "reset counters");
+    HIP_TRY(hipMemsetAsync(m->base.counters, 0, m->g.events.size() * 4 * mk::kEventWords, s), "reset counters");
     HIP_TRY(hipMemsetAsync(m->base.abort_flag, 0, 4, s), "reset abort flag");
     m->epoch = 0;
     m->need_reset = false;
@@ -339,6 +379,7 @@ static int run_megakernel(mk_model* m, const int32_t* tok, const int32_t* pos, i
   P.batch = batch;
   P.n_steps = n_steps;
   P.epoch0 = m->epoch;
+  P.use_events = 1;
   P.timeout_ticks = m->timeout_ticks;
   P.drop_task = m->drop_task;
   P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * 32) ? m->profile : nullptr;
@@ -362,6 +403,7 @@ int mk_decode_step(mk_model* m, const int32_t* d_tokens, const int32_t* d_pos, i
   P.batch = batch;
   P.n_steps = 1;
   P.epoch0 = 0;
+  P.use_events = 0;
   P.timeout_ticks = m->timeout_ticks;
   P.drop_task = -1;
   for (const auto& op : m->g.ops)

@@ -16,10 +16,19 @@ constexpr int kUnitBytes = 1024;
 constexpr int kUnitCols = 128;
 constexpr int kUnitRows = 4;
 
-constexpr int kThreads = 256;  // workgroup size: 4 wave64
-constexpr int kWaves = kThreads / 64;
-constexpr int kMaxCols = 4;    // sequences a matvec task handles (VALU path)
-constexpr int kAttTile = 256;  // positions per attention tile
+// Workgroup layout: wave 0 stages task inputs (and polls events), wave 1
+// retires tasks (epilogue, stores, signals); then kPairs loader waves and
+// kPairs compute waves. Loader p streams the units of pair p into an LDS ring
+// that compute wave p consumes.
+constexpr int kCtlWaves = 2;
+constexpr int kPairs = 3;
+constexpr int kThreads = 64 * (kCtlWaves + 2 * kPairs);
+constexpr int kMaxRing = 64;   // ring slots per pair (upper bound)
+constexpr int kMaxCols = 4;    // sequences a matvec task handles
+constexpr int kMaxG = 4;       // query heads per kv head
+constexpr int kStripes = 8;    // event counter stripes (one per XCD)
+constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte line
+constexpr int kCtlBytes = 1024;             // control words + ring metadata (see kernels)
 
 // status word bits (device)
 constexpr int32_t kStatusBadToken = 1;
@@ -31,7 +40,9 @@ struct DevTask {
   int32_t dep, trig;
   int32_t ordinal;   // index of the task within its operator
   int32_t n_units;   // weight units of a matvec task (0 otherwise)
-  int32_t n_vrb;     // row blocks streamed (gate/up count both)
+  int32_t kb;        // column blocks of a matvec task
+  int32_t kdim;      // K of a matvec task
+  int32_t pad;
   int64_t w_off;     // byte offset of the task's units in the packed weights
 };
 
@@ -41,16 +52,21 @@ struct Params {
   const int32_t* queue_ptr;   // [num_cus + 1]
   const int32_t* queue_ids;
   const uint32_t* thresholds;
-  uint32_t* counters;
+  uint32_t* counters;         // [n_events][kEventWords]
   int32_t n_tasks;
   // shape
   int32_t L, H, Hq, Hkv, D, F, V, G, B, S, Nc, n_lm;
-  int32_t kb_h, kb_qd, kb_f;  // column blocks of 128 for K = H, Hq*D, F
   float eps;
   float attn_scale;
-  int32_t kp;           // staged floats per column (max padded K)
-  int32_t vrow_stride;  // partial-sum rows per wave and column
+  int32_t kp;           // staged floats per column in the small slots (K rounded up to 256)
+  int32_t kp_big;       // staged floats per column in the big slot (FFN rounded up to 256)
+  int32_t vrow_stride;  // partial-sum rows per (wave, column)
   int32_t ncap;         // staged columns = min(max_batch, kMaxCols)
+  int32_t small_floats; // LDS staging slot size (two small slots)
+  int32_t big_floats;   // LDS staging slot size for down-projection and merge tasks
+  int32_t part_floats;  // LDS partial-sum area per slot
+  int32_t ring_slots;   // ring slots per loader/compute pair
+  int32_t ring_inflight;// loads a loader keeps in flight (8, 12, 16, 20, 24, 32, 40 or 48)
   // model data
   const uint8_t* wpack;
   const uint16_t* embed;      // [V][H] bf16 (library copy)
@@ -58,7 +74,7 @@ struct Params {
   uint16_t* kcache;           // [L][B][Hkv][S][D] bf16 (caller-owned)
   uint16_t* vcache;
   const float2* rope_cs;      // [S][D/2] (cos, sin)
-  // workspace (fp32 activations)
+  // workspace (fp32 activations; every buffer has 16 KiB of slack at the end)
   float* x;                   // [B][H]
   float* qkv;                 // [B][Hkv][(G+2)D]
   float* part_ml;             // [B][Hq][Nc][2]
@@ -78,6 +94,7 @@ struct Params {
   int32_t batch;
   int32_t n_steps;
   uint32_t epoch0;
+  int32_t use_events;         // 0: single-task workgroups ordered by the stream
   uint64_t timeout_ticks;     // 100 MHz constant clock
   uint64_t* profile;          // null or [n_steps][n_tasks][4]
   int32_t drop_task;          // fault injection: this task never signals (-1: off)

@@ -1,16 +1,34 @@
 // gfx950 device code of the persistent decode megakernel (internal to libmk).
 //
-//  * task bodies: EMB, RMSNorm+QKV, split attention (RoPE + KV append), merge,
-//    O-proj+residual, RMSNorm+gate/up+SiLU*up, down+residual, final
-//    RMSNorm+LM head+partial argmax, argmax (Hazy megakernel summary: the fused
-//    instruction list; MPK walk-through 3.3.1: the layer calls of one step);
-//  * mk_persistent: one workgroup per compute unit walks its static task queue
-//    for every step; a task waits until its dependent event's counter reaches
-//    the threshold and then adds one to its triggering event (MPK blog
-//    translation, "MPK runtime" section and Figure 3);
-//  * mk_oplaunch: the same bodies, one launch per operator (the conventional
-//    many-kernel engine the pages compare against);
-//  * mk_pack: weight repacking into the streamed unit layout.
+// One workgroup per compute unit runs that unit's static task queue for every
+// decode step (MPK blog translation, "MPK runtime" section and Figure 3: a
+// worker per SM with its own queue; a task waits for its dependent event and
+// counts its triggering event on completion). The workgroup is split by wave:
+//
+//  * wave 0, the stager: for each task in queue order it waits until the task's
+//    dependent event reaches its threshold, then stages the task's inputs into
+//    an LDS slot (RMSNorm statistics and gains applied on the way in, RoPE
+//    applied to attention inputs);
+//  * wave 1, the retirer: once a task's compute is done it runs the epilogue
+//    (partial-sum reduction, residual add, SiLU*up, attention merge, argmax),
+//    stores the results and adds one to the task's triggering event;
+//  * kPairs loader waves: each streams its share of every task's weight (or KV
+//    cache) units straight into an LDS ring, running ahead across task
+//    boundaries so weights keep arriving while the workgroup waits on an event
+//    (Hazy megakernel summary: paged shared memory lets the next instruction's
+//    weights load early; MPK blog translation: loads of the next layer overlap
+//    the current one);
+//  * kPairs compute waves: each consumes its loader's ring.
+//
+// Cross-compute-unit data moves with device-coherent (sc1) loads and stores;
+// a producer waits for its stores to complete before it counts the event, and
+// a consumer reads the inputs only after it has seen the count, so no cache
+// writeback or invalidate is needed. Event counters are split into 8 stripes
+// (one per XCD) to spread the atomic traffic.
+//
+// mk_oplaunch runs the same roles on a one-task queue per workgroup with no
+// event waits: one launch per operator (the conventional many-kernel engine
+// the pages compare against). mk_pack repacks the weights into units.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -22,19 +40,39 @@
 namespace mk {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kAuxCoherent = 16;   // sc1
+constexpr int kAuxStream = 2;      // nt
+constexpr int kHdr = 32;           // floats of header at the start of a slot
+constexpr uint32_t kMetaMatvec = 1, kMetaK = 2, kMetaV = 3, kMetaFirst = 4, kMetaLast = 8;
+
+// LDS control words (ints); ring metadata follows at kMetaBase
+enum {
+  C_STAGED = 0, C_RETIRED = 1, C_DONE = 2 /* 3 slots */, C_STEPOK = 5, C_ABORT = 6,
+  C_PUB = 8 /* per pair */, C_CONS = 16 /* per pair */, kMetaBase = 64
+};
+static_assert(kMetaBase * 4 + kPairs * kMaxRing * 4 <= kCtlBytes, "control area");
+// slot header fields (as int)
+enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11 };
 
 // ---------------------------------------------------------------------------
-// small helpers
+// helpers
 // ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void cbar() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt left at their maximum)
+__device__ __forceinline__ void wait_lgkm() { cbar(); __builtin_amdgcn_s_waitcnt(0xC07F); cbar(); }
+__device__ __forceinline__ void wait_all() { cbar(); __builtin_amdgcn_s_waitcnt(0); cbar(); }
 
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
 // float -> bfloat16, round to nearest even (NaN -> quiet NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
+__device__ __forceinline__ uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
   u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return u >> 16;
 }
 
 __device__ __forceinline__ void unpack8(const u32x4 w, float f[8]) {
@@ -48,206 +86,345 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+
+template <class T>
+__device__ __forceinline__ T ld_coh(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ void st_coh(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// 1 KiB per wave: lane l copies 16 bytes from its own address src into
+// lds_dst + 16*l (lds_dst is wave-uniform).
+template <int AUX>
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)lds_dst, 16, 0, AUX);
+}
+
+__device__ __forceinline__ int lds_ld(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// lane 0 only; earlier LDS accesses of this wave complete first
+__device__ __forceinline__ void lds_st(int* p, int v) {
+  wait_lgkm();
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  wait_lgkm();
+}
+__device__ __forceinline__ void lds_add(int* p, int v) {
+  wait_lgkm();
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  wait_lgkm();
+}
+
+// LDS word access for the loader waves. Their LDS DMA is tracked by vmcnt and
+// the compiler would otherwise drain it before every LDS access; these blocks
+// complete their own access (lgkmcnt) before they end.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ int lds_ld_raw(const int* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
   return v;
 }
-
-__device__ __forceinline__ void set_status(const Params& P, int32_t bits) {
-  __hip_atomic_fetch_or(P.status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void lds_st_raw(int* p, int v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(lds_addr(p)), "v"(v) : "memory");
 }
 
-// Shared-memory layout of one workgroup (dynamic LDS, sized by the host).
-struct Smem {
-  float* in;     // [kMaxCols][Kp] staged input vector(s)
-  float* part;   // [kWaves][kMaxCols][vrow_stride] matvec partial sums
-  float* scal;   // 64 floats of scratch (norm scales, reductions)
-  int* iscal;    // 64 ints of scratch
-  float* att;    // attention scratch
-  int kp;        // floats per staged column
-  int vrow_stride;
-  int ncap;      // staged columns (min(max_batch, kMaxCols))
+struct Ctx {
+  int* ctl;
+  float* slots;    // small0 | small1 | big
+  float* parts;    // three partial-sum areas
+  int small_floats, part_floats;
+  uint8_t* ring;   // [kPairs][ring_slots][1 KiB]
+  int cu;          // stripe / profile id
+  int single;      // >= 0: the one task this workgroup runs (per-operator mode)
+  int q0, q1;      // queue range
+  int lane;
 };
 
+__device__ __forceinline__ int task_at(const Params& P, const Ctx& cx, int qi) {
+  return cx.single >= 0 ? cx.single : P.queue_ids[qi];
+}
+
+__device__ __forceinline__ bool is_big(int type) { return type == T_D || type == T_COMB; }
+// Staging slot of the next task: 2 for down-projection and merge tasks, else
+// the two small slots alternate. Every role walks the queue and calls this
+// for every task, so all agree.
+__device__ __forceinline__ int next_slot(int& nsmall, int type) {
+  if (is_big(type)) return 2;
+  return (nsmall++) & 1;
+}
+__device__ __forceinline__ int slot_kp(const Params& P, int slot) { return slot == 2 ? P.kp_big : P.kp; }
+__device__ __forceinline__ float* slot_ptr(const Ctx& cx, int slot) { return cx.slots + slot * cx.small_floats; }
+__device__ __forceinline__ float* part_ptr(const Ctx& cx, int slot) { return cx.parts + slot * cx.part_floats; }
+
+__device__ __forceinline__ void raise_abort(const Params& P, const Ctx& cx, int32_t status_bits) {
+  if (cx.lane == 0) {
+    if (status_bits) __hip_atomic_fetch_or(P.status, status_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(P.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&cx.ctl[C_ABORT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Spin until ctl[w] >= v. Bounded by the watchdog; false = leave the kernel.
+__device__ __forceinline__ bool spin_ctl(const Params& P, const Ctx& cx, int w, int v) {
+  if (lds_ld(&cx.ctl[w]) >= v) { cbar(); return true; }
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    __builtin_amdgcn_s_sleep(1);
+    if (lds_ld(&cx.ctl[w]) >= v) break;
+    if (lds_ld(&cx.ctl[C_ABORT])) return false;
+    if (wall_clock64() - t0 > P.timeout_ticks) { raise_abort(P, cx, kStatusTimeout); return false; }
+  }
+  cbar();
+  return true;
+}
+
+__device__ __forceinline__ bool has_stream(int type) {
+  return type == T_QKV || type == T_O || type == T_GU || type == T_D || type == T_LM || type == T_ATT;
+}
+
 // ---------------------------------------------------------------------------
-// matvec engine: a wave streams its contiguous share of the task's units
+// stager (wave 0)
 // ---------------------------------------------------------------------------
 
-// Each of the 4 waves takes units [U*w/4, U*(w+1)/4). Inside a unit, lane
-// 16j+i multiplies its 8 weights of row j by the 8 staged inputs at the same
-// columns; a row block's 16-lane partial sums are combined when the wave leaves
-// the block and stored to part[wave][col][4*block + j].
-__device__ void matvec_share(const Params& P, const DevTask& T, int KB, int ncols, const Smem& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane >> 4, i = lane & 15;
-  const int U = T.n_units;
-  const int u0 = (U * wave) / kWaves, u1 = (U * (wave + 1)) / kWaves;
-  if (u0 >= u1) return;
-  const uint8_t* wb = P.wpack + T.w_off + lane * 16;
-  float acc[kMaxCols];
-#pragma unroll
-  for (int c = 0; c < kMaxCols; ++c) acc[c] = 0.f;
-  int vrb = u0 / KB, kb = u0 - vrb * KB;
-  float* part = sm.part + (size_t)wave * sm.ncap * sm.vrow_stride;
-
-  auto flush = [&](int blk) {
-#pragma unroll
-    for (int c = 0; c < kMaxCols; ++c) {
-      if (c < ncols) {
-        float v = acc[c];
-        v += __shfl_xor(v, 8, 64);
-        v += __shfl_xor(v, 4, 64);
-        v += __shfl_xor(v, 2, 64);
-        v += __shfl_xor(v, 1, 64);
-        if (i == 0) part[c * sm.vrow_stride + blk * 4 + j] = v;
-      }
-      acc[c] = 0.f;
+// Wait until the striped counter of `ev` reaches `need` (coherent polling).
+__device__ __forceinline__ bool wait_event(const Params& P, const Ctx& cx, int ev, uint32_t need) {
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    uint32_t v = 0;
+    if (cx.lane < kStripes) v = ld_coh(&P.counters[(size_t)ev * kEventWords + cx.lane * 32]);
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v = __shfl(v, 0, 64);
+    if ((int32_t)(v - need) >= 0) break;
+    if (ld_coh(P.abort_flag) || lds_ld(&cx.ctl[C_ABORT])) {
+      if (cx.lane == 0) __hip_atomic_store(&cx.ctl[C_ABORT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return false;
     }
-  };
+    if (wall_clock64() - t0 > P.timeout_ticks) { raise_abort(P, cx, kStatusTimeout); return false; }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  cbar();
+  return true;
+}
 
-  constexpr int NB = 16;
-  for (int u = u0; u < u1; u += NB) {
-    u32x4 w[NB];
+// DMA `n` floats (coherent) from global src into LDS dst (both 16-byte
+// aligned), in whole 1 KiB pieces: up to 255 floats past n are read (every
+// activation buffer has slack) and written (every LDS region is sized for it).
+__device__ __forceinline__ void stage_copy(const Ctx& cx, const float* src, float* dst, int n) {
+  const int nl = (n + 255) / 256;
+  for (int t = 0; t < nl; ++t) dma16<kAuxCoherent>(src + t * 256 + cx.lane * 4, dst + t * 256);
+  wait_all();
+}
+
+__device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, const DevTask& T, int slot) {
+  float* hdr = slot_ptr(cx, slot);
+  const int kp = slot_kp(P, slot);
+  float* in = hdr + kHdr;
+  float* res = in + (size_t)P.ncap * kp;
+  const int lane = cx.lane;
+  {  // clear this slot's partial sums
+    float4* pz = reinterpret_cast<float4*>(part_ptr(cx, slot));
+    for (int k = lane; k < P.part_floats / 4; k += 64) pz[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int ncols = P.batch;
+  const int K = T.kdim;
+  if (T.type == T_QKV || T.type == T_GU || T.type == T_LM) {
+    const uint16_t* gain = P.gains + (T.type == T_LM ? (size_t)P.L * 2 * P.H
+                                                     : ((size_t)T.layer * 2 + (T.type == T_GU)) * P.H);
+    for (int c = 0; c < ncols; ++c) {
+      const rsrc_t r = make_rsrc(P.x + (size_t)c * P.H, (uint32_t)P.H * 4);
+      const int nl = (K + 255) / 256;  // <= 16 (H <= 4096)
+      u32x4 buf[16];
 #pragma unroll
-    for (int k = 0; k < NB; ++k)
-      if (u + k < u1) w[k] = __builtin_nontemporal_load((const u32x4*)(wb + (size_t)(u + k) * kUnitBytes));
+      for (int t = 0; t < 16; ++t)
+        if (t < nl) buf[t] = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64 * t) * 16, 0, kAuxCoherent);
+      float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      if (u + k < u1) {
-        float f[8];
-        unpack8(w[k], f);
-#pragma unroll
-        for (int c = 0; c < kMaxCols; ++c) {
-          if (c < ncols) {
-            const float4* hp = reinterpret_cast<const float4*>(sm.in + c * sm.kp + kb * kUnitCols + i * 8);
-            const float4 h0 = hp[0], h1 = hp[1];
-            float a = acc[c];
-            a = fmaf(f[0], h0.x, a); a = fmaf(f[1], h0.y, a);
-            a = fmaf(f[2], h0.z, a); a = fmaf(f[3], h0.w, a);
-            a = fmaf(f[4], h1.x, a); a = fmaf(f[5], h1.y, a);
-            a = fmaf(f[6], h1.z, a); a = fmaf(f[7], h1.w, a);
-            acc[c] = a;
+      for (int t = 0; t < 16; ++t) {
+        if (t < nl) {
+          const int k0 = (lane + 64 * t) * 4;
+          float4 v;
+          v.x = __uint_as_float(buf[t].x); v.y = __uint_as_float(buf[t].y);
+          v.z = __uint_as_float(buf[t].z); v.w = __uint_as_float(buf[t].w);
+          if (k0 < K) {
+            ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss); ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+            const uint2 gg = *reinterpret_cast<const uint2*>(gain + k0);
+            v.x *= bf2f(gg.x & 0xffffu); v.y *= bf2f(gg.x >> 16); v.z *= bf2f(gg.y & 0xffffu); v.w *= bf2f(gg.y >> 16);
+          } else {
+            v = make_float4(0.f, 0.f, 0.f, 0.f);
           }
-        }
-        if (++kb == KB) {
-          flush(vrb);
-          kb = 0;
-          ++vrb;
+          *reinterpret_cast<float4*>(in + (size_t)c * kp + k0) = v;
         }
       }
-    }
-  }
-  if (kb != 0) flush(vrb);
-}
-
-// Stage `ncols` input vectors of length K (row stride `stride`) into sm.in,
-// optionally multiplied by a bf16 gain; zero-pad to Kp. When `norm`, also
-// compute 1/sqrt(mean(x^2) + eps) per column into sm.scal[c].
-__device__ void stage_input(const Params& P, const float* src, int stride, int K, int ncols,
-                            const uint16_t* gain, bool norm, const Smem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int c = 0; c < ncols; ++c) {
-    float ss = 0.f;
-    for (int k = tid; k < sm.kp; k += kThreads) {
-      float v = 0.f;
-      if (k < K) {
-        v = src[(size_t)c * stride + k];
-        ss = fmaf(v, v, ss);
-        if (gain) v *= bf2f(gain[k]);
-      }
-      sm.in[c * sm.kp + k] = v;
-    }
-    if (norm) {
+      for (int k = nl * 256 + lane * 4; k < kp; k += 256)
+        *reinterpret_cast<float4*>(in + (size_t)c * kp + k) = make_float4(0.f, 0.f, 0.f, 0.f);
       ss = wave_sum(ss);
-      if (lane == 0) sm.scal[8 + c * kWaves + wave] = ss;
+      if (lane == 0) hdr[c] = 1.0f / sqrtf(ss / (float)K + P.eps);
+    }
+  } else {  // O (attention output) or D (SiLU*up), plus the residual rows
+    const float* src = T.type == T_O ? P.attn : P.mlp;
+    for (int c = 0; c < ncols; ++c) {
+      stage_copy(cx, src + (size_t)c * K, in + (size_t)c * kp, K);
+      for (int k = K + lane; k < kp; k += 64) in[(size_t)c * kp + k] = 0.f;
+      const int R = T.row1 - T.row0;
+      for (int r = lane; r < R; r += 64) res[(size_t)c * P.vrow_stride + r] = ld_coh(P.x + (size_t)c * P.H + T.row0 + r);
     }
   }
-  __syncthreads();
-  if (norm && tid < ncols) {
-    float ss = 0.f;
-    for (int w = 0; w < kWaves; ++w) ss += sm.scal[8 + tid * kWaves + w];
-    sm.scal[tid] = 1.0f / sqrtf(ss / (float)K + P.eps);
+}
+
+// Attention slot layout after the header: raw q|k|v of the kv group (rounded
+// up to 256 floats), rotated queries [G][D], new key [D] and value [D] as
+// bf16-rounded floats, then their bf16 bits [2D].
+__device__ __forceinline__ int att_raw_floats(const Params& P) { return ((P.G + 2) * P.D + 255) & ~255; }
+
+__device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
+  float* hdr = slot_ptr(cx, slot);
+  int* ih = reinterpret_cast<int*>(hdr);
+  float* raw = hdr + kHdr;
+  const int G = P.G, D = P.D, Dh = D / 2, GR = (G + 2) * D;
+  float* q = raw + att_raw_floats(P);
+  float* kf = q + G * D;
+  float* vf = kf + D;
+  uint16_t* kvb = reinterpret_cast<uint16_t*>(vf + D);
+  const int lane = cx.lane;
+  const bool active = T.b < P.batch;
+  int p = active ? P.pos_in[T.b] + step : 0;
+  const bool valid = active && p >= 0 && p < P.S;
+  if (active && !valid && lane == 0) __hip_atomic_fetch_or(P.status, kStatusBadPos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!valid) p = 0;
+  const int64_t len = (int64_t)p + 1;
+  const int lo = (int)((int64_t)T.chunk * len / P.Nc), hi = (int)((int64_t)(T.chunk + 1) * len / P.Nc);
+  const bool owner = valid && T.chunk == P.Nc - 1;
+  if (lane == 0) {
+    ih[H_P] = p;
+    ih[H_LO] = lo;
+    ih[H_END] = valid ? min(hi, p) : lo;
+    ih[H_FLAGS] = (valid ? 1 : 0) | (owner ? 2 : 0) | (active ? 4 : 0);
+  }
+  if (!valid) return;
+  stage_copy(cx, P.qkv + ((size_t)T.b * P.Hkv + T.g) * GR, raw, GR);
+  for (int idx = lane; idx < (G + 1) * Dh; idx += 64) {
+    const int h = idx / Dh, jj = idx - h * Dh;
+    const float a = raw[h * D + jj], b = raw[h * D + jj + Dh];
+    const float2 cs = P.rope_cs[(size_t)p * Dh + jj];
+    const float r0 = a * cs.x - b * cs.y, r1 = b * cs.x + a * cs.y;
+    if (h < G) {
+      q[h * D + jj] = r0;
+      q[h * D + jj + Dh] = r1;
+    } else {
+      const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
+      kf[jj] = bf2f(b0);
+      kf[jj + Dh] = bf2f(b1);
+      kvb[jj] = (uint16_t)b0;
+      kvb[jj + Dh] = (uint16_t)b1;
+    }
+  }
+  for (int d = lane; d < D; d += 64) {
+    const uint32_t vb = f2bf(raw[(G + 1) * D + d]);
+    vf[d] = bf2f(vb);
+    kvb[D + d] = (uint16_t)vb;
   }
 }
 
-__device__ void zero_part(const Smem& sm) {
-  const int n = kWaves * sm.ncap * sm.vrow_stride;
-  for (int k = threadIdx.x; k < n; k += kThreads) sm.part[k] = 0.f;
+// offset of the second staged array of merge / argmax tasks
+__device__ __forceinline__ int second_off(int n) { return (n + 255) & ~255; }
+
+__device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
+  float* hdr = slot_ptr(cx, slot);
+  float* data = hdr + kHdr;
+  const int lane = cx.lane;
+  switch (T.type) {
+    case T_EMB: {
+      if (T.b >= P.batch) break;
+      int tok = step == 0 ? P.tokens_in[T.b] : ld_coh(P.tok_cur + T.b);
+      if (tok < 0 || tok >= P.V) {
+        if (lane == 0) __hip_atomic_fetch_or(P.status, kStatusBadToken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tok = 0;
+      }
+      const uint16_t* row = P.embed + (size_t)tok * P.H;
+      const int nl = (P.H * 2 + 1023) / 1024;
+      for (int t = 0; t < nl; ++t) dma16<0>(row + t * 512 + lane * 8, data + t * 256);
+      wait_all();
+      break;
+    }
+    case T_ATT: stage_att(P, cx, T, slot, step); break;
+    case T_COMB: {
+      if (T.b >= P.batch) break;
+      const size_t head0 = (size_t)T.b * P.Hq + (size_t)T.g * P.G;
+      stage_copy(cx, P.part_ml + head0 * P.Nc * 2, data, P.G * P.Nc * 2);
+      stage_copy(cx, P.part_acc + head0 * P.Nc * P.D, data + second_off(P.G * P.Nc * 2), P.G * P.Nc * P.D);
+      break;
+    }
+    case T_ARGMAX: {
+      if (T.b >= P.batch) break;
+      stage_copy(cx, P.lm_val + (size_t)T.b * P.n_lm, data, P.n_lm);
+      stage_copy(cx, reinterpret_cast<const float*>(P.lm_idx + (size_t)T.b * P.n_lm), data + second_off(P.n_lm),
+                 P.n_lm);
+      break;
+    }
+    default: stage_matvec(P, cx, T, slot); break;
+  }
 }
 
-__device__ __forceinline__ float part_sum(const Smem& sm, int c, int vrow) {
+__device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
+  int i = 0, nsmall = 0;
+  int last0 = -1, last1 = -1, last2 = -1;  // last task staged into each slot
+  for (int step = 0; step < P.n_steps; ++step) {
+    const uint32_t epoch = P.epoch0 + (uint32_t)step;
+    for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
+      const int id = task_at(P, cx, qi);
+      const DevTask T = P.tasks[id];
+      const int slot = next_slot(nsmall, T.type);
+      const int prev = slot == 0 ? last0 : slot == 1 ? last1 : last2;
+      if (prev >= 0 && !spin_ctl(P, cx, C_RETIRED, prev + 1)) return;
+      if (slot == 0) last0 = i; else if (slot == 1) last1 = i; else last2 = i;
+      if (P.use_events) {
+        const uint32_t mult = T.type == T_EMB ? epoch : epoch + 1;
+        if (!wait_event(P, cx, T.dep, P.thresholds[T.dep] * mult)) return;
+      }
+      if (qi == cx.q0) lds_st(&cx.ctl[C_STEPOK], step + 1);
+      stage_task(P, cx, T, slot, step);
+      lds_st(&cx.ctl[C_STAGED], i + 1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// retirer (wave 1)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float part_sum(const Params& P, const float* part, int c, int vrow) {
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += sm.part[((size_t)w * sm.ncap + c) * sm.vrow_stride + vrow];
+  for (int w = 0; w < kPairs; ++w) s += part[((size_t)w * P.ncap + c) * P.vrow_stride + vrow];
   return s;
 }
 
-// ---------------------------------------------------------------------------
-// task bodies (whole workgroup; every thread reaches every barrier)
-// ---------------------------------------------------------------------------
-
-__device__ void body_emb(const Params& P, const DevTask& T, int step) {
-  const int b = T.b;
-  if (b >= P.batch) return;
-  int tok = step == 0 ? P.tokens_in[b] : P.tok_cur[b];
-  if (tok < 0 || tok >= P.V) {
-    if (threadIdx.x == 0) set_status(P, kStatusBadToken);
-    tok = 0;
-  }
-  const uint16_t* row = P.embed + (size_t)tok * P.H;
-  for (int k = threadIdx.x; k < P.H; k += kThreads) P.x[(size_t)b * P.H + k] = bf2f(row[k]);
-}
-
-// RMSNorm-fused matvecs (QKV, GU, LM) and plain ones with residual (O, D).
-__device__ void body_matvec(const Params& P, const DevTask& T, int step, const Smem& sm) {
-  const int ncols = P.batch;
-  const int R = T.row1 - T.row0;
-  int K, KB, stride;
-  const float* src;
-  const uint16_t* gain = nullptr;
-  bool norm = false;
-  switch (T.type) {
-    case T_QKV: src = P.x; stride = P.H; K = P.H; KB = P.kb_h; gain = P.gains + (size_t)T.layer * 2 * P.H; norm = true; break;
-    case T_GU: src = P.x; stride = P.H; K = P.H; KB = P.kb_h; gain = P.gains + ((size_t)T.layer * 2 + 1) * P.H; norm = true; break;
-    case T_LM: src = P.x; stride = P.H; K = P.H; KB = P.kb_h; gain = P.gains + (size_t)P.L * 2 * P.H; norm = true; break;
-    case T_O: src = P.attn; stride = P.Hq * P.D; K = P.Hq * P.D; KB = P.kb_qd; break;
-    default: src = P.mlp; stride = P.F; K = P.F; KB = P.kb_f; break;  // T_D
-  }
-  zero_part(sm);
-  stage_input(P, src, stride, K, ncols, gain, norm, sm);
-  __syncthreads();
-  matvec_share(P, T, KB, ncols, sm);
-  __syncthreads();
-
-  const int tid = threadIdx.x;
-  if (T.type == T_QKV) {
-    const int GR = (P.G + 2) * P.D;
-    for (int idx = tid; idx < ncols * R; idx += kThreads) {
-      const int c = idx / R, r = idx - c * R;
-      P.qkv[((size_t)c * P.Hkv + T.g) * GR + T.row0 + r] = part_sum(sm, c, r) * sm.scal[c];
-    }
-  } else if (T.type == T_O || T.type == T_D) {
-    for (int idx = tid; idx < ncols * R; idx += kThreads) {
-      const int c = idx / R, r = idx - c * R;
-      float* xp = P.x + (size_t)c * P.H + T.row0 + r;
-      *xp = *xp + part_sum(sm, c, r);
-    }
-  } else if (T.type == T_GU) {
-    for (int idx = tid; idx < ncols * R; idx += kThreads) {
-      const int c = idx / R, r = idx - c * R;
-      const int vr = 8 * (r >> 2) + (r & 3);
-      const float gt = part_sum(sm, c, vr) * sm.scal[c];
-      const float up = part_sum(sm, c, vr + 4) * sm.scal[c];
-      P.mlp[(size_t)c * P.F + T.row0 + r] = gt / (1.0f + expf(-gt)) * up;
-    }
-  } else {  // T_LM: logits and this task's (max, lowest index) per column
+__device__ __forceinline__ void retire_matvec(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
+  const float* hdr = slot_ptr(cx, slot);
+  const float* res = hdr + kHdr + (size_t)P.ncap * slot_kp(P, slot);
+  const float* part = part_ptr(cx, slot);
+  const int lane = cx.lane, ncols = P.batch, R = T.row1 - T.row0;
+  if (T.type == T_LM) {
     const bool last = step == P.n_steps - 1;
-    const int lane = tid & 63, wave = tid >> 6;
     for (int c = 0; c < ncols; ++c) {
       float best = -INFINITY;
       int bi = 0x7fffffff;
-      for (int r = tid; r < R; r += kThreads) {
-        const float v = part_sum(sm, c, r) * sm.scal[c];
+      for (int r = lane; r < R; r += 64) {
+        const float v = part_sum(P, part, c, r) * hdr[c];
         if (last && P.logits_out) P.logits_out[(size_t)c * P.V + T.row0 + r] = v;
         if (v > best || (v == best && T.row0 + r < bi)) { best = v; bi = T.row0 + r; }
       }
@@ -256,306 +433,246 @@ __device__ void body_matvec(const Params& P, const DevTask& T, int step, const S
         const int oi = __shfl_xor(bi, o, 64);
         if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
       }
-      if (lane == 0) { sm.scal[40 + wave] = best; sm.iscal[40 + wave] = bi; }
-      __syncthreads();
-      if (tid == 0) {
-        for (int w = 1; w < kWaves; ++w) {
-          const float ov = sm.scal[40 + w];
-          const int oi = sm.iscal[40 + w];
-          if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-        }
-        P.lm_val[(size_t)c * P.n_lm + T.ordinal] = best;
-        P.lm_idx[(size_t)c * P.n_lm + T.ordinal] = bi;
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// One attention chunk of one (kv group, sequence): rotate the group's query
-// heads and the new key by the position, append K/V at the position (final
-// chunk only), then softmax statistics and the value sum over the chunk's
-// positions, tile by tile with a running maximum.
-__device__ void body_att(const Params& P, const DevTask& T, int step, const Smem& sm) {
-  const int b = T.b, g = T.g, G = P.G, D = P.D, Dh = P.D / 2;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool active = b < P.batch;
-  int p = active ? P.pos_in[b] + step : 0;
-  const bool valid = active && p >= 0 && p < P.S;
-  if (active && !valid && tid == 0) set_status(P, kStatusBadPos);
-  if (!valid) p = 0;
-  const int64_t len = (int64_t)p + 1;
-  int lo = (int)((int64_t)T.chunk * len / P.Nc), hi = (int)((int64_t)(T.chunk + 1) * len / P.Nc);
-  if (!valid) hi = lo;
-  const bool owner = valid && T.chunk == P.Nc - 1;
-
-  float* s_q = sm.att;                 // [G][D]
-  float* s_k = s_q + G * D;            // [D]
-  float* s_v = s_k + D;                // [D]
-  float* s_m = s_v + D;                // [G]
-  float* s_l = s_m + G;                // [G]
-  float* s_sc = s_l + G;               // [G] scale of this tile
-  float* s_p = s_sc + G;               // [G][kAttTile]
-
-  const size_t kvrow = (((size_t)T.layer * P.B + b) * P.Hkv + g) * (size_t)P.S;
-  const float* qsrc = P.qkv + ((size_t)b * P.Hkv + g) * (G + 2) * D;
-  if (valid) {
-    for (int idx = tid; idx < (G + 1) * Dh; idx += kThreads) {
-      const int h = idx / Dh, jj = idx - h * Dh;
-      const float* src = qsrc + h * D;  // h == G is the key
-      const float a = src[jj], bb = src[jj + Dh];
-      const float2 cs = P.rope_cs[(size_t)p * Dh + jj];
-      const float r0 = a * cs.x - bb * cs.y, r1 = bb * cs.x + a * cs.y;
-      if (h < G) {
-        s_q[h * D + jj] = r0;
-        s_q[h * D + jj + Dh] = r1;
-      } else {
-        const uint16_t k0 = f2bf(r0), k1 = f2bf(r1);
-        s_k[jj] = bf2f(k0);
-        s_k[jj + Dh] = bf2f(k1);
-        if (owner) {
-          P.kcache[(kvrow + p) * D + jj] = k0;
-          P.kcache[(kvrow + p) * D + jj + Dh] = k1;
-        }
-      }
-    }
-    for (int d = tid; d < D; d += kThreads) {
-      const uint16_t vb = f2bf(qsrc[(G + 1) * D + d]);
-      s_v[d] = bf2f(vb);
-      if (owner) P.vcache[(kvrow + p) * D + d] = vb;
-    }
-  }
-  if (tid < G) { s_m[tid] = -INFINITY; s_l[tid] = 0.f; }
-  __syncthreads();
-
-  constexpr int kMaxPairs = 4;  // (head, dim) pairs per thread: G*D <= 1024
-  float acc[kMaxPairs];
-#pragma unroll
-  for (int k = 0; k < kMaxPairs; ++k) acc[k] = 0.f;
-
-  for (int t0 = lo; t0 < hi; t0 += kAttTile) {
-    const int n = min(kAttTile, hi - t0);
-    for (int t = tid; t < n; t += kThreads) {
-      const int pos = t0 + t;
-      float dot[8];
-      for (int h = 0; h < G; ++h) dot[h] = 0.f;
-      const uint16_t* krow = P.kcache + (kvrow + pos) * D;
-      for (int d0 = 0; d0 < D; d0 += 8) {
-        float kf[8];
-        if (pos == p) {
-          for (int e = 0; e < 8; ++e) kf[e] = s_k[d0 + e];
-        } else {
-          unpack8(*reinterpret_cast<const u32x4*>(krow + d0), kf);
-        }
-        for (int h = 0; h < G; ++h) {
-          const float* q = s_q + h * D + d0;
-          float a = dot[h];
-          for (int e = 0; e < 8; ++e) a = fmaf(q[e], kf[e], a);
-          dot[h] = a;
-        }
-      }
-      for (int h = 0; h < G; ++h) s_p[h * kAttTile + t] = dot[h] * P.attn_scale;
-    }
-    __syncthreads();
-    for (int h = wave; h < G; h += kWaves) {
-      float mx = -INFINITY;
-      for (int t = lane; t < n; t += 64) mx = fmaxf(mx, s_p[h * kAttTile + t]);
-      mx = wave_max(mx);
-      const float m_new = fmaxf(s_m[h], mx);
-      float sum = 0.f;
-      for (int t = lane; t < n; t += 64) {
-        const float e = expf(s_p[h * kAttTile + t] - m_new);
-        s_p[h * kAttTile + t] = e;
-        sum += e;
-      }
-      sum = wave_sum(sum);
       if (lane == 0) {
-        const float sc = expf(s_m[h] - m_new);
-        s_l[h] = s_l[h] * sc + sum;
-        s_m[h] = m_new;
-        s_sc[h] = sc;
+        st_coh(P.lm_val + (size_t)c * P.n_lm + T.ordinal, best);
+        st_coh(P.lm_idx + (size_t)c * P.n_lm + T.ordinal, bi);
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kMaxPairs; ++k) {
-      const int idx = tid + k * kThreads;
-      if (idx < G * D) {
-        const int h = idx / D, d = idx - h * D;
-        float a = acc[k] * s_sc[h];
-        const float* pp = s_p + h * kAttTile;
-        for (int t = 0; t < n; ++t) {
-          const int pos = t0 + t;
-          const float v = pos == p ? s_v[d] : bf2f(P.vcache[(kvrow + pos) * D + d]);
-          a = fmaf(pp[t], v, a);
-        }
-        acc[k] = a;
-      }
-    }
-    __syncthreads();
+    return;
   }
-  if (active) {
-    for (int k = 0; k < kMaxPairs; ++k) {
-      const int idx = tid + k * kThreads;
-      if (idx < G * D) {
-        const int h = idx / D, d = idx - h * D;
-        const size_t slot = ((size_t)b * P.Hq + g * G + h) * P.Nc + T.chunk;
-        P.part_acc[slot * D + d] = acc[k];
-        if (d == 0) {
-          P.part_ml[slot * 2] = s_m[h];
-          P.part_ml[slot * 2 + 1] = s_l[h];
-        }
+  for (int idx = lane; idx < ncols * R; idx += 64) {
+    const int c = idx / R, r = idx - c * R;
+    switch (T.type) {
+      case T_QKV:
+        st_coh(P.qkv + ((size_t)c * P.Hkv + T.g) * (P.G + 2) * P.D + T.row0 + r, part_sum(P, part, c, r) * hdr[c]);
+        break;
+      case T_GU: {
+        const int vr = 8 * (r >> 2) + (r & 3);
+        const float gt = part_sum(P, part, c, vr) * hdr[c];
+        const float up = part_sum(P, part, c, vr + 4) * hdr[c];
+        st_coh(P.mlp + (size_t)c * P.F + T.row0 + r, gt / (1.0f + expf(-gt)) * up);
+        break;
       }
+      default:  // O, D: residual add
+        st_coh(P.x + (size_t)c * P.H + T.row0 + r, res[(size_t)c * P.vrow_stride + r] + part_sum(P, part, c, r));
+        break;
     }
   }
 }
 
-// Merge the chunk partials of one (kv group, sequence): rescale each chunk by
-// exp(m_c - max m) and divide the summed values by the summed weights.
-__device__ void body_comb(const Params& P, const DevTask& T) {
-  const int b = T.b;
-  if (b >= P.batch) return;
+// Merge the compute waves' softmax statistics and value sums for this chunk,
+// add the newest position when this chunk owns it (and append it to the KV
+// cache), and store the chunk partial.
+__device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const DevTask& T, int slot) {
+  const float* hdr = slot_ptr(cx, slot);
+  const int* ih = reinterpret_cast<const int*>(hdr);
+  const int flags = ih[H_FLAGS];
+  if (!(flags & 4)) return;  // sequence not in this call's batch
+  const bool owner = flags & 2;
   const int G = P.G, D = P.D;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  const float* q = hdr + kHdr + att_raw_floats(P);
+  const float* kf = q + G * D;
+  const float* vf = kf + D;
+  const uint32_t* kvw = reinterpret_cast<const uint32_t*>(vf + D);
+  const float* part = part_ptr(cx, slot);
+  const int lane = cx.lane, p = ih[H_P];
+  float sp[kMaxG];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    sp[h] = -INFINITY;
+    if (h < G && owner) {
+      float a = 0.f;
+      for (int d = lane; d < D; d += 64) a = fmaf(q[h * D + d], kf[d], a);
+      sp[h] = wave_sum(a) * P.attn_scale;
+    }
+  }
+  const int stride = G * (D + 2);
+  for (int idx = lane; idx < G * D; idx += 64) {
     const int h = idx / D, d = idx - h * D;
-    const int hq = T.g * G + h;
-    const size_t base = ((size_t)b * P.Hq + hq) * P.Nc;
-    float M = -INFINITY;
-    for (int c = 0; c < P.Nc; ++c) M = fmaxf(M, P.part_ml[(base + c) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < P.Nc; ++c) {
-      const float mc = P.part_ml[(base + c) * 2];
-      if (mc == -INFINITY) continue;
-      const float w = expf(mc - M);
-      num = fmaf(w, P.part_acc[(base + c) * D + d], num);
-      den = fmaf(w, P.part_ml[(base + c) * 2 + 1], den);
+    float s_new = sp[0];
+#pragma unroll
+    for (int hh = 1; hh < kMaxG; ++hh)
+      if (h == hh) s_new = sp[hh];
+    float M = s_new;
+    for (int w = 0; w < kPairs; ++w) M = fmaxf(M, part[w * stride + h * (D + 2) + D]);
+    float l = 0.f, a = 0.f;
+    for (int w = 0; w < kPairs; ++w) {
+      const float mw = part[w * stride + h * (D + 2) + D];
+      if (mw == -INFINITY) continue;
+      const float e = expf(mw - M);
+      l = fmaf(part[w * stride + h * (D + 2) + D + 1], e, l);
+      a = fmaf(part[w * stride + h * (D + 2) + d], e, a);
     }
-    P.attn[(size_t)b * P.Hq * D + (size_t)hq * D + d] = den > 0.f ? num / den : 0.f;
+    if (owner) {
+      const float e = expf(s_new - M);
+      l += e;
+      a = fmaf(e, vf[d], a);
+    }
+    const size_t slot_idx = ((size_t)T.b * P.Hq + (size_t)T.g * G + h) * P.Nc + T.chunk;
+    st_coh(P.part_acc + slot_idx * D + d, a);
+    if (d == 0) {
+      st_coh(P.part_ml + slot_idx * 2, M);
+      st_coh(P.part_ml + slot_idx * 2 + 1, l);
+    }
+  }
+  if (owner) {
+    const size_t row = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.S + p) * D;
+    uint32_t* kc = reinterpret_cast<uint32_t*>(P.kcache + row);
+    uint32_t* vc = reinterpret_cast<uint32_t*>(P.vcache + row);
+    for (int w = lane; w < D / 2; w += 64) {
+      st_coh(kc + w, kvw[w]);
+      st_coh(vc + w, kvw[D / 2 + w]);
+    }
   }
 }
 
-__device__ void body_argmax(const Params& P, const DevTask& T, int step, const Smem& sm) {
-  const int b = T.b;
-  if (b >= P.batch) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float best = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int t = tid; t < P.n_lm; t += kThreads) {
-    const float v = P.lm_val[(size_t)b * P.n_lm + t];
-    const int ix = P.lm_idx[(size_t)b * P.n_lm + t];
-    if (v > best || (v == best && ix < bi)) { best = v; bi = ix; }
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-  }
-  if (lane == 0) { sm.scal[48 + wave] = best; sm.iscal[48 + wave] = bi; }
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kWaves; ++w) {
-      const float ov = sm.scal[48 + w];
-      const int oi = sm.iscal[48 + w];
-      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-    }
-    if (bi < 0 || bi >= P.V) bi = 0;  // every logit was NaN
-    P.out_tokens[(size_t)step * P.batch + b] = bi;
-    P.tok_cur[b] = bi;
-  }
-}
-
-__device__ void exec_task(const Params& P, const DevTask& T, int step, const Smem& sm) {
+__device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
+  const float* hdr = slot_ptr(cx, slot);
+  const float* data = hdr + kHdr;
+  const int lane = cx.lane;
   switch (T.type) {
-    case T_EMB: body_emb(P, T, step); break;
-    case T_ATT: body_att(P, T, step, sm); break;
-    case T_COMB: body_comb(P, T); break;
-    case T_ARGMAX: body_argmax(P, T, step, sm); break;
-    default: body_matvec(P, T, step, sm); break;
-  }
-}
-
-// LDS carve-up: 64 float + 64 int scratch, staged inputs, matvec partials,
-// attention scratch (sizes from Params; the host checks the total).
-__device__ Smem carve(const Params& P, char* base) {
-  Smem s;
-  s.kp = P.kp;
-  s.vrow_stride = P.vrow_stride;
-  s.ncap = P.ncap;
-  s.scal = reinterpret_cast<float*>(base);
-  s.iscal = reinterpret_cast<int*>(base + 64 * 4);
-  s.in = reinterpret_cast<float*>(base + 128 * 4);
-  s.part = s.in + (size_t)P.ncap * P.kp;
-  s.att = s.part + (size_t)kWaves * P.ncap * P.vrow_stride;
-  return s;
-}
-
-// ---------------------------------------------------------------------------
-// runtime: events
-// ---------------------------------------------------------------------------
-
-// Spin until counter[ev] >= need (acquire), bounded by the watchdog. Returns
-// false when the kernel must stop (timeout here or elsewhere).
-__device__ bool wait_event(const Params& P, int ev, uint32_t need) {
-  const uint64_t t0 = wall_clock64();
-  for (;;) {
-    const uint32_t v = __hip_atomic_load(&P.counters[ev], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int32_t)(v - need) >= 0) break;
-    if (__hip_atomic_load(P.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
-    if (wall_clock64() - t0 > P.timeout_ticks) {
-      set_status(P, kStatusTimeout);
-      __hip_atomic_store(P.abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return true;
-}
-
-extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent(Params P) {
-  extern __shared__ __align__(16) char smem_raw[];
-  const Smem sm = carve(P, smem_raw);
-  __shared__ int s_go;
-  const int cu = blockIdx.x;
-  const int q0 = P.queue_ptr[cu], q1 = P.queue_ptr[cu + 1];
-  for (int step = 0; step < P.n_steps; ++step) {
-    const uint32_t epoch = P.epoch0 + (uint32_t)step;
-    for (int qi = q0; qi < q1; ++qi) {
-      const int id = P.queue_ids[qi];
-      const DevTask T = P.tasks[id];
-      uint64_t t_ready = 0, t_start = 0;
-      if (threadIdx.x == 0) {
-        const uint32_t mult = T.type == T_EMB ? epoch : epoch + 1;
-        s_go = wait_event(P, T.dep, P.thresholds[T.dep] * mult) ? 1 : 0;
-        t_ready = wall_clock64();
+    case T_EMB: {
+      if (T.b >= P.batch) break;
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(data);  // bf16 pairs
+      const rsrc_t r = make_rsrc(P.x + (size_t)T.b * P.H, (uint32_t)P.H * 4);
+      for (int k4 = lane * 4; k4 < P.H; k4 += 256) {
+        const uint32_t a = row[k4 / 2], b = row[k4 / 2 + 1];
+        u32x4 v;
+        v.x = a << 16; v.y = a & 0xffff0000u; v.z = b << 16; v.w = b & 0xffff0000u;
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, k4 * 4, 0, kAuxCoherent);
       }
-      __syncthreads();
-      if (!s_go) return;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      if (threadIdx.x == 0) t_start = wall_clock64();
-      exec_task(P, T, step, sm);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        if (id != P.drop_task)
-          __hip_atomic_fetch_add(&P.counters[T.trig], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    case T_ATT: retire_att(P, cx, T, slot); break;
+    case T_COMB: {
+      if (T.b >= P.batch) break;
+      const int G = P.G, D = P.D, Nc = P.Nc;
+      float* ml = const_cast<float*>(data);  // (m, l) per (head, chunk); m becomes the weight
+      const float* acc = data + second_off(G * Nc * 2);
+      // per head: the largest chunk maximum, then weight_c = exp(m_c - M) / sum_c exp(m_c - M) l_c
+      for (int h = 0; h < G; ++h) {
+        float M = -INFINITY;
+        for (int c = lane; c < Nc; c += 64) M = fmaxf(M, ml[(h * Nc + c) * 2]);
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        float den = 0.f;
+        for (int c = lane; c < Nc; c += 64) {
+          const float mc = ml[(h * Nc + c) * 2];
+          den += mc == -INFINITY ? 0.f : expf(mc - M) * ml[(h * Nc + c) * 2 + 1];
+        }
+        den = wave_sum(den);
+        const float inv = den > 0.f ? 1.0f / den : 0.f;
+        wait_lgkm();
+        for (int c = lane; c < Nc; c += 64) {
+          const float mc = ml[(h * Nc + c) * 2];
+          ml[(h * Nc + c) * 2] = mc == -INFINITY ? 0.f : expf(mc - M) * inv;
+        }
+        wait_lgkm();
+      }
+      for (int idx = lane; idx < G * D; idx += 64) {
+        const int h = idx / D, d = idx - h * D;
+        float num = 0.f;
+        for (int c = 0; c < Nc; ++c) num = fmaf(ml[(h * Nc + c) * 2], acc[(size_t)(h * Nc + c) * D + d], num);
+        st_coh(P.attn + (size_t)T.b * P.Hq * D + ((size_t)T.g * G + h) * D + d, num);
+      }
+      break;
+    }
+    case T_ARGMAX: {
+      if (T.b >= P.batch) break;
+      const float* val = data;
+      const int* ix = reinterpret_cast<const int*>(data + second_off(P.n_lm));
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int t = lane; t < P.n_lm; t += 64) {
+        const float v = val[t];
+        const int i2 = ix[t];
+        if (v > best || (v == best && i2 < bi)) { best = v; bi = i2; }
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+      }
+      if (lane == 0) {
+        if (bi < 0 || bi >= P.V) bi = 0;  // every logit was NaN
+        P.out_tokens[(size_t)step * P.batch + T.b] = bi;
+        st_coh(P.tok_cur + T.b, bi);
+      }
+      break;
+    }
+    default: retire_matvec(P, cx, T, slot, step); break;
+  }
+}
+
+__device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
+  int i = 0, nsmall = 0;
+  for (int step = 0; step < P.n_steps; ++step) {
+    for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
+      const int id = task_at(P, cx, qi);
+      const DevTask T = P.tasks[id];
+      const int slot = next_slot(nsmall, T.type);
+      if (!spin_ctl(P, cx, C_STAGED, i + 1)) return;
+      const uint64_t t_staged = wall_clock64();
+      if (has_stream(T.type) && !spin_ctl(P, cx, C_DONE + slot, kPairs)) return;
+      const uint64_t t_computed = wall_clock64();
+      retire_task(P, cx, T, slot, step);
+      wait_all();  // every store of the epilogue has completed
+      if (cx.lane == 0) {
+        if (P.use_events && id != P.drop_task)
+          __hip_atomic_fetch_add(&P.counters[(size_t)T.trig * kEventWords + (cx.cu & (kStripes - 1)) * 32], 1u,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (P.profile) {
           uint64_t* rec = P.profile + ((size_t)step * P.n_tasks + id) * 4;
-          rec[0] = (uint64_t)(uint32_t)id | ((uint64_t)cu << 32);
-          rec[1] = t_ready;
-          rec[2] = t_start;
+          rec[0] = (uint64_t)(uint32_t)id | ((uint64_t)(uint32_t)cx.cu << 32);
+          rec[1] = t_staged;
+          rec[2] = t_computed;
           rec[3] = wall_clock64();
         }
+        __hip_atomic_store(&cx.ctl[C_DONE + slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
+      lds_st(&cx.ctl[C_RETIRED], i + 1);
     }
   }
 }
 
+#include "pipeline.h"
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void run(const Params& P, int cu, int single) {
+  extern __shared__ __align__(16) char smem[];
+  Ctx cx;
+  cx.ctl = reinterpret_cast<int*>(smem);
+  float* base = reinterpret_cast<float*>(smem + kCtlBytes);
+  cx.slots = base;
+  cx.small_floats = P.small_floats;
+  cx.parts = base + 2 * P.small_floats + P.big_floats;
+  cx.part_floats = P.part_floats;
+  cx.ring = reinterpret_cast<uint8_t*>(cx.parts + 3 * P.part_floats);
+  cx.cu = cu;
+  cx.single = single;
+  if (single >= 0) {
+    cx.q0 = 0;
+    cx.q1 = 1;
+  } else {
+    cx.q0 = P.queue_ptr[cu];
+    cx.q1 = P.queue_ptr[cu + 1];
+  }
+  cx.lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) cx.ctl[threadIdx.x] = 0;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  if (wave == 0) run_stager(P, cx);
+  else if (wave == 1) run_retirer(P, cx);
+  else if (wave < kCtlWaves + kPairs) run_loader(P, cx, wave - kCtlWaves);
+  else run_compute(P, cx, wave - kCtlWaves - kPairs);
+}
+
+extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent(Params P) { run(P, blockIdx.x, -1); }
+
 extern "C" __global__ void __launch_bounds__(kThreads) mk_oplaunch(Params P, int first) {
-  extern __shared__ __align__(16) char smem_raw[];
-  const Smem sm = carve(P, smem_raw);
-  const DevTask T = P.tasks[first + blockIdx.x];
-  exec_task(P, T, 0, sm);
+  run(P, blockIdx.x, first + blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -600,12 +717,9 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack(const PackJob* jobs, c
   }
 }
 
-}  // namespace mk
-
 // ---------------------------------------------------------------------------
 // host-side launchers (called from api.cpp)
 // ---------------------------------------------------------------------------
-namespace mk {
 
 hipError_t set_lds_limit(int bytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
