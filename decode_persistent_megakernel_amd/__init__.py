@@ -17,7 +17,7 @@ __all__ = [
     "MKError", "ModelDesc", "GraphOpts", "lib", "lib_path",
     "mk_build_task_graph", "mk_graph_serialize", "mk_graph_info", "mk_free_graph",
     "mk_load_weights", "mk_decode_step", "mk_generate", "mk_check", "mk_set_watchdog_ms",
-    "mk_set_profile_buffer", "mk_debug_drop_signal", "mk_model_info", "mk_free_model", "mk_last_error",
+    "mk_set_profile_buffer", "mk_set_wait_counters", "mk_debug_drop_signal", "mk_model_info", "mk_free_model", "mk_last_error",
     "MK_MODE_MEGAKERNEL", "MK_MODE_OPLAUNCH", "STATUS_NAMES",
 ]
 
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "mk_set_watchdog_ms": [vp, i32],
         "mk_debug_drop_signal": [vp, i32],
         "mk_set_profile_buffer": [vp, vp, ctypes.c_size_t],
+        "mk_set_wait_counters": [vp, vp, ctypes.c_size_t],
         "mk_model_info": [vp, u64p, ctypes.POINTER(i32), ctypes.POINTER(i32)],
     }
     for name, args in sig.items():
@@ -198,6 +199,10 @@ def mk_debug_drop_signal(model: int, task_id: int) -> None:
 
 def mk_set_profile_buffer(model: int, buf, nbytes: int) -> None:
     _ok(lib().mk_set_profile_buffer(model, _ptr(buf), nbytes))
+
+
+def mk_set_wait_counters(model: int, buf, nbytes: int) -> None:
+    _ok(lib().mk_set_wait_counters(model, _ptr(buf), nbytes))
 
 
 def mk_model_info(model: int):

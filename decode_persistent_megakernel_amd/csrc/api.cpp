@@ -49,6 +49,7 @@ struct mk_model {
   uint64_t* profile = nullptr;
   int32_t drop_task = -1;
   size_t profile_bytes = 0;
+  uint64_t* waits = nullptr;
   mk::Params base{};                      // everything but the per-call fields
   std::vector<void*> allocs;              // device buffers owned by the model
 
@@ -174,6 +175,8 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   if (64 % (D / 8) != 0) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim/8 must divide 64");
   if (d.hidden > 4096) return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden above 4096");
   if (std::max({kb_h, kb_qd, kb_f}) > 255) return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32640");
+  if (d.hidden % 4 || (d.n_q_heads * d.head_dim) % 4 || d.ffn % 4)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden, q width and ffn must be multiples of 4");
   // LDS: control words, two small staging slots, one big slot (down-projection
   // inputs and attention merges), three partial-sum areas, then the rings.
   // Staged copies move whole 1 KiB pieces, so every region is rounded up to
@@ -194,20 +197,19 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   const int64_t small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
   const int64_t big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
   const int64_t part_floats =
-      (std::max<int64_t>(int64_t(kPairs) * ncap * max_vrows, int64_t(kPairs) * G * (D + 2)) + 3) & ~int64_t(3);
+      (std::max<int64_t>(int64_t(kStreams) * ncap * max_vrows, int64_t(kStreams) * G * (D + 2)) + 3) & ~int64_t(3);
   const size_t fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats);
   const size_t lds_max = 160 * 1024;
-  // ring entries are 2 KiB items (two units); a loader keeps up to 24 in flight
+  // The rest holds the stream waves' rings of 2 KiB items; each slot is one
+  // item in flight, and a few suffice to keep HBM busy (8 KiB in flight per
+  // wave already streams near the HBM peak).
   const int64_t item_bytes = 2 * kUnitBytes;
-  const int64_t ring = std::min<int64_t>(kMaxRing, (int64_t(lds_max) - int64_t(fixed)) / (kPairs * item_bytes));
-  static const int kInflight[] = {24, 20, 16, 12, 8};
-  int inflight = 0;
-  for (int v : kInflight)
-    if (v <= ring - 2) { inflight = v; break; }
-  if (inflight == 0)
+  int64_t ring = std::min<int64_t>(kMaxDepth, (int64_t(lds_max) - int64_t(fixed)) / (kStreams * item_bytes));
+  ring = ring >= 8 ? 8 : ring >= 6 ? 6 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
+  if (ring < kMinDepth)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: staging needs " + std::to_string(fixed) +
                                      " bytes of LDS, leaving no room for the weight rings");
-  const size_t lds = fixed + size_t(kPairs) * size_t(ring) * size_t(item_bytes);
+  const size_t lds = fixed + size_t(kStreams) * size_t(ring) * size_t(item_bytes);
   m->lds_bytes = static_cast<int>(lds);
   HIP_TRY(set_lds_limit(m->lds_bytes), "hipFuncSetAttribute(max dynamic LDS)");
   int per_cu = 0;
@@ -325,7 +327,6 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   P.small_floats = static_cast<int32_t>(small_floats);
   P.big_floats = static_cast<int32_t>(big_floats);
   P.ring_slots = static_cast<int32_t>(ring);
-  P.ring_inflight = inflight;
   P.kp_big = kp_big;
   P.part_floats = static_cast<int32_t>(part_floats);
   P.attn_scale = static_cast<float>(1.0 / std::sqrt(double(d.head_dim)));
@@ -383,6 +384,7 @@ static int run_megakernel(mk_model* m, const int32_t* tok, const int32_t* pos, i
   P.timeout_ticks = m->timeout_ticks;
   P.drop_task = m->drop_task;
   P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * 32) ? m->profile : nullptr;
+  P.waits = m->waits;
   HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
   m->epoch += static_cast<uint32_t>(n_steps);
   return MK_OK;
@@ -453,6 +455,14 @@ int mk_set_profile_buffer(mk_model* m, void* d_buf, size_t bytes) {
   if (d_buf && bytes < m->g.tasks.size() * 32) return fail(MK_EINVAL, "mk_set_profile_buffer: buffer too small");
   m->profile = static_cast<uint64_t*>(d_buf);
   m->profile_bytes = d_buf ? bytes : 0;
+  return MK_OK;
+}
+
+int mk_set_wait_counters(mk_model* m, void* d_buf, size_t bytes) {
+  if (!m) return fail(MK_EINVAL, "mk_set_wait_counters: NULL model");
+  if (d_buf && bytes < size_t(m->g.opts.num_cus) * mk::kWaves * mk::kWaitWords * 8)
+    return fail(MK_EINVAL, "mk_set_wait_counters: buffer too small");
+  m->waits = static_cast<uint64_t*>(d_buf);
   return MK_OK;
 }
 

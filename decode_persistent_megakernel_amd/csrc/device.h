@@ -8,7 +8,9 @@ namespace mk {
 
 // Weights are streamed in 1 KiB "units": 64 lanes x 16 bytes. A unit covers a
 // block of 4 consecutive rows and 128 consecutive columns: lane 16*j + i holds
-// columns [8i, 8i+8) of row j of the block (8 bf16 values). A matvec task's
+// columns [4i, 4i+4) and [64+4i, 64+4i+4) of row j of the block (8 bf16
+// values), so that the 16 lanes of a row read their activations as two
+// contiguous 256-byte runs of LDS (no bank conflicts). A matvec task's
 // weights are its units in (row block, column block) order, stored
 // contiguously in the packed buffer; gate/up tasks alternate a gate row block
 // and the up row block of the same rows.
@@ -17,18 +19,21 @@ constexpr int kUnitCols = 128;
 constexpr int kUnitRows = 4;
 
 // Workgroup layout: wave 0 stages task inputs (and polls events), wave 1
-// retires tasks (epilogue, stores, signals); then kPairs loader waves and
-// kPairs compute waves. Loader p streams the units of pair p into an LDS ring
-// that compute wave p consumes.
+// retires tasks (epilogue, stores, signals); then kStreams stream waves, each
+// copying its piece of every streamed task into its own LDS ring and
+// computing on it.
 constexpr int kCtlWaves = 2;
-constexpr int kPairs = 3;
-constexpr int kThreads = 64 * (kCtlWaves + 2 * kPairs);
-constexpr int kMaxRing = 64;   // ring slots per pair (upper bound)
+constexpr int kStreams = 4;
+constexpr int kThreads = 64 * (kCtlWaves + kStreams);
+constexpr int kMaxDepth = 8;   // ring slots (2 KiB items) per stream wave: 4, 6 or 8
+constexpr int kMinDepth = 4;   // fewer cannot hide the copy latency
 constexpr int kMaxCols = 4;    // sequences a matvec task handles
 constexpr int kMaxG = 4;       // query heads per kv head
 constexpr int kStripes = 8;    // event counter stripes (one per XCD)
 constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte line
 constexpr int kCtlBytes = 1024;             // control words + ring metadata (see kernels)
+constexpr int kWaves = kThreads / 64;
+constexpr int kWaitWords = 8;               // per-wave wait counters (mk_set_wait_counters)
 
 // status word bits (device)
 constexpr int32_t kStatusBadToken = 1;
@@ -65,8 +70,7 @@ struct Params {
   int32_t small_floats; // LDS staging slot size (two small slots)
   int32_t big_floats;   // LDS staging slot size for down-projection and merge tasks
   int32_t part_floats;  // LDS partial-sum area per slot
-  int32_t ring_slots;   // ring slots per loader/compute pair
-  int32_t ring_inflight;// loads a loader keeps in flight (8, 12, 16, 20, 24, 32, 40 or 48)
+  int32_t ring_slots;   // ring slots per stream wave = items it keeps in flight
   // model data
   const uint8_t* wpack;
   const uint16_t* embed;      // [V][H] bf16 (library copy)
@@ -98,6 +102,7 @@ struct Params {
   uint64_t timeout_ticks;     // 100 MHz constant clock
   uint64_t* profile;          // null or [n_steps][n_tasks][4]
   int32_t drop_task;          // fault injection: this task never signals (-1: off)
+  uint64_t* waits;            // null or [grid][kWaves][kWaitWords] wait-time counters
 };
 
 // One matvec task to repack: rows [row0, row1) of its logical matrix (the

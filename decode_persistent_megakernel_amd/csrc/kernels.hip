@@ -12,13 +12,12 @@
 //  * wave 1, the retirer: once a task's compute is done it runs the epilogue
 //    (partial-sum reduction, residual add, SiLU*up, attention merge, argmax),
 //    stores the results and adds one to the task's triggering event;
-//  * kPairs loader waves: each streams its share of every task's weight (or KV
-//    cache) units straight into an LDS ring, running ahead across task
-//    boundaries so weights keep arriving while the workgroup waits on an event
-//    (Hazy megakernel summary: paged shared memory lets the next instruction's
-//    weights load early; MPK blog translation: loads of the next layer overlap
-//    the current one);
-//  * kPairs compute waves: each consumes its loader's ring.
+//  * kStreams stream waves: each copies its share of every task's weight (or
+//    KV cache) units straight into its own LDS ring and computes on them,
+//    copying ahead across task boundaries so weights keep arriving while the
+//    workgroup waits on an event (Hazy megakernel summary: paged shared memory
+//    lets the next instruction's weights load early; MPK blog translation:
+//    loads of the next layer overlap the current one).
 //
 // Cross-compute-unit data moves with device-coherent (sc1) loads and stores;
 // a producer waits for its stores to complete before it counts the event, and
@@ -45,14 +44,10 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kAuxCoherent = 16;   // sc1
 constexpr int kAuxStream = 2;      // nt
 constexpr int kHdr = 32;           // floats of header at the start of a slot
-constexpr uint32_t kMetaMatvec = 1, kMetaK = 2, kMetaV = 3, kMetaFirst = 4, kMetaLast = 8;
 
-// LDS control words (ints); ring metadata follows at kMetaBase
-enum {
-  C_STAGED = 0, C_RETIRED = 1, C_DONE = 2 /* 3 slots */, C_STEPOK = 5, C_ABORT = 6,
-  C_PUB = 8 /* per pair */, C_CONS = 16 /* per pair */, kMetaBase = 64
-};
-static_assert(kMetaBase * 4 + kPairs * kMaxRing * 4 <= kCtlBytes, "control area");
+// LDS control words (ints)
+enum { C_STAGED = 0, C_RETIRED = 1, C_DONE = 2 /* 3 slots */, C_STEPOK = 5, C_ABORT = 6, kCtlWords = 64 };
+static_assert(kCtlWords * 4 <= kCtlBytes, "control area");
 // slot header fields (as int)
 enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11 };
 
@@ -110,8 +105,10 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)lds_dst, 16, 0, AUX);
 }
 
+// Control words are read as wave-uniform values (readfirstlane), so that
+// every loop and branch on them is scalar control flow.
 __device__ __forceinline__ int lds_ld(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 // lane 0 only; earlier LDS accesses of this wave complete first
 __device__ __forceinline__ void lds_st(int* p, int v) {
@@ -134,7 +131,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ int lds_ld_raw(const int* p) {
   int v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
-  return v;
+  return __builtin_amdgcn_readfirstlane(v);
 }
 __device__ __forceinline__ void lds_st_raw(int* p, int v) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(lds_addr(p)), "v"(v) : "memory");
@@ -145,15 +142,36 @@ struct Ctx {
   float* slots;    // small0 | small1 | big
   float* parts;    // three partial-sum areas
   int small_floats, part_floats;
-  uint8_t* ring;   // [kPairs][ring_slots][1 KiB]
+  uint8_t* ring;   // [kStreams][ring_slots][2 KiB]
   int cu;          // stripe / profile id
   int single;      // >= 0: the one task this workgroup runs (per-operator mode)
   int q0, q1;      // queue range
   int lane;
 };
 
+// Graph tables and call inputs are read-only while a kernel runs. Reading them
+// through the constant address space with a wave-uniform index makes them
+// scalar loads (lgkmcnt): a vector load would share vmcnt with the loader's
+// in-flight weight copies, and waiting for it would drain those copies.
+typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const i32x4 ci32x4;
+static_assert(sizeof(DevTask) == 64, "task descriptors are four 16-byte words");
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int idx) {
+  return ((cint32*)p)[__builtin_amdgcn_readfirstlane(idx)];
+}
+__device__ __forceinline__ DevTask ld_task(const Params& P, int id) {
+  ci32x4* src = (ci32x4*)P.tasks + 4 * __builtin_amdgcn_readfirstlane(id);
+  i32x4 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = src[i];
+  DevTask T;
+  __builtin_memcpy(&T, w, sizeof(T));
+  return T;
+}
+
 __device__ __forceinline__ int task_at(const Params& P, const Ctx& cx, int qi) {
-  return cx.single >= 0 ? cx.single : P.queue_ids[qi];
+  return cx.single >= 0 ? cx.single : ld_uniform(P.queue_ids, qi);
 }
 
 __device__ __forceinline__ bool is_big(int type) { return type == T_D || type == T_COMB; }
@@ -190,6 +208,31 @@ __device__ __forceinline__ bool spin_ctl(const Params& P, const Ctx& cx, int w, 
   return true;
 }
 
+// Optional per-wave wait accounting: four counters (100 MHz ticks or counts)
+// and the wave's lifetime, added into P.waits when the wave finishes.
+struct Waits {
+  uint64_t c[6];  // words 0-3, then 5-6 (word 4: lifetime)
+  uint64_t t0;
+  bool on;
+};
+__device__ __forceinline__ void waits_init(const Params& P, Waits& w) {
+  w.on = P.waits != nullptr;
+  w.c[0] = w.c[1] = w.c[2] = w.c[3] = w.c[4] = w.c[5] = 0;
+  w.t0 = w.on ? wall_clock64() : 0;
+}
+__device__ __forceinline__ uint64_t waits_now(const Waits& w) { return w.on ? wall_clock64() : 0; }
+__device__ __forceinline__ void waits_add(Waits& w, int j, uint64_t since) {
+  if (w.on) w.c[j] += wall_clock64() - since;
+}
+__device__ __forceinline__ void waits_put(const Params& P, const Ctx& cx, const Waits& w) {
+  if (!w.on || cx.lane != 0) return;
+  uint64_t* o = P.waits + ((size_t)cx.cu * kWaves + (threadIdx.x >> 6)) * kWaitWords;
+#pragma unroll
+  for (int j = 0; j < 6; ++j)
+    __hip_atomic_fetch_add(&o[j < 4 ? j : j + 1], w.c[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_add(&o[4], wall_clock64() - w.t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ bool has_stream(int type) {
   return type == T_QKV || type == T_O || type == T_GU || type == T_D || type == T_LM || type == T_ATT;
 }
@@ -207,9 +250,9 @@ __device__ __forceinline__ bool wait_event(const Params& P, const Ctx& cx, int e
     v += __shfl_xor(v, 1, 64);
     v += __shfl_xor(v, 2, 64);
     v += __shfl_xor(v, 4, 64);
-    v = __shfl(v, 0, 64);
+    v = __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
     if ((int32_t)(v - need) >= 0) break;
-    if (ld_coh(P.abort_flag) || lds_ld(&cx.ctl[C_ABORT])) {
+    if (__builtin_amdgcn_readfirstlane(ld_coh(P.abort_flag)) || lds_ld(&cx.ctl[C_ABORT])) {
       if (cx.lane == 0) __hip_atomic_store(&cx.ctl[C_ABORT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       return false;
     }
@@ -301,7 +344,7 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
   uint16_t* kvb = reinterpret_cast<uint16_t*>(vf + D);
   const int lane = cx.lane;
   const bool active = T.b < P.batch;
-  int p = active ? P.pos_in[T.b] + step : 0;
+  int p = active ? ld_uniform(P.pos_in, T.b) + step : 0;
   const bool valid = active && p >= 0 && p < P.S;
   if (active && !valid && lane == 0) __hip_atomic_fetch_or(P.status, kStatusBadPos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!valid) p = 0;
@@ -382,24 +425,34 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
 __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
   int last0 = -1, last1 = -1, last2 = -1;  // last task staged into each slot
+  Waits wt;  // slot free, dependency event, staging, tasks
+  waits_init(P, wt);
   for (int step = 0; step < P.n_steps; ++step) {
     const uint32_t epoch = P.epoch0 + (uint32_t)step;
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
       const int id = task_at(P, cx, qi);
-      const DevTask T = P.tasks[id];
+      const DevTask T = ld_task(P, id);
       const int slot = next_slot(nsmall, T.type);
       const int prev = slot == 0 ? last0 : slot == 1 ? last1 : last2;
+      uint64_t s0 = waits_now(wt);
       if (prev >= 0 && !spin_ctl(P, cx, C_RETIRED, prev + 1)) return;
+      waits_add(wt, 0, s0);
       if (slot == 0) last0 = i; else if (slot == 1) last1 = i; else last2 = i;
+      s0 = waits_now(wt);
       if (P.use_events) {
         const uint32_t mult = T.type == T_EMB ? epoch : epoch + 1;
         if (!wait_event(P, cx, T.dep, P.thresholds[T.dep] * mult)) return;
       }
+      waits_add(wt, 1, s0);
       if (qi == cx.q0) lds_st(&cx.ctl[C_STEPOK], step + 1);
+      s0 = waits_now(wt);
       stage_task(P, cx, T, slot, step);
+      waits_add(wt, 2, s0);
+      ++wt.c[3];
       lds_st(&cx.ctl[C_STAGED], i + 1);
     }
   }
+  waits_put(P, cx, wt);
 }
 
 // ---------------------------------------------------------------------------
@@ -409,7 +462,7 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
 __device__ __forceinline__ float part_sum(const Params& P, const float* part, int c, int vrow) {
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < kPairs; ++w) s += part[((size_t)w * P.ncap + c) * P.vrow_stride + vrow];
+  for (int w = 0; w < kStreams; ++w) s += part[((size_t)w * P.ncap + c) * P.vrow_stride + vrow];
   return s;
 }
 
@@ -494,9 +547,9 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
     for (int hh = 1; hh < kMaxG; ++hh)
       if (h == hh) s_new = sp[hh];
     float M = s_new;
-    for (int w = 0; w < kPairs; ++w) M = fmaxf(M, part[w * stride + h * (D + 2) + D]);
+    for (int w = 0; w < kStreams; ++w) M = fmaxf(M, part[w * stride + h * (D + 2) + D]);
     float l = 0.f, a = 0.f;
-    for (int w = 0; w < kPairs; ++w) {
+    for (int w = 0; w < kStreams; ++w) {
       const float mw = part[w * stride + h * (D + 2) + D];
       if (mw == -INFINITY) continue;
       const float e = expf(mw - M);
@@ -605,17 +658,24 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
 
 __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
+  Waits wt;  // staged, computed, epilogue, tasks
+  waits_init(P, wt);
   for (int step = 0; step < P.n_steps; ++step) {
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
       const int id = task_at(P, cx, qi);
-      const DevTask T = P.tasks[id];
+      const DevTask T = ld_task(P, id);
       const int slot = next_slot(nsmall, T.type);
+      const uint64_t s0 = waits_now(wt);
       if (!spin_ctl(P, cx, C_STAGED, i + 1)) return;
+      waits_add(wt, 0, s0);
       const uint64_t t_staged = wall_clock64();
-      if (has_stream(T.type) && !spin_ctl(P, cx, C_DONE + slot, kPairs)) return;
+      if (has_stream(T.type) && !spin_ctl(P, cx, C_DONE + slot, kStreams)) return;
       const uint64_t t_computed = wall_clock64();
+      if (wt.on) wt.c[1] += t_computed - t_staged;
       retire_task(P, cx, T, slot, step);
       wait_all();  // every store of the epilogue has completed
+      waits_add(wt, 2, t_computed);
+      ++wt.c[3];
       if (cx.lane == 0) {
         if (P.use_events && id != P.drop_task)
           __hip_atomic_fetch_add(&P.counters[(size_t)T.trig * kEventWords + (cx.cu & (kStripes - 1)) * 32], 1u,
@@ -632,6 +692,7 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
       lds_st(&cx.ctl[C_RETIRED], i + 1);
     }
   }
+  waits_put(P, cx, wt);
 }
 
 #include "pipeline.h"
@@ -656,17 +717,19 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
     cx.q0 = 0;
     cx.q1 = 1;
   } else {
-    cx.q0 = P.queue_ptr[cu];
-    cx.q1 = P.queue_ptr[cu + 1];
+    cx.q0 = ld_uniform(P.queue_ptr, cu);
+    cx.q1 = ld_uniform(P.queue_ptr, cu + 1);
   }
   cx.lane = threadIdx.x & 63;
   if (threadIdx.x < 64) cx.ctl[threadIdx.x] = 0;
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
+  // wave index as a wave-uniform value: every role's control flow is scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) run_stager(P, cx);
   else if (wave == 1) run_retirer(P, cx);
-  else if (wave < kCtlWaves + kPairs) run_loader(P, cx, wave - kCtlWaves);
-  else run_compute(P, cx, wave - kCtlWaves - kPairs);
+  else if (P.ring_slots >= 8) run_stream<8>(P, cx, wave - kCtlWaves);
+  else if (P.ring_slots >= 6) run_stream<6>(P, cx, wave - kCtlWaves);
+  else run_stream<4>(P, cx, wave - kCtlWaves);
 }
 
 extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent(Params P) { run(P, blockIdx.x, -1); }
@@ -689,7 +752,7 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack(const PackJob* jobs, c
     const int lane = (int)(idx & 63);
     const int vrb = (int)(u / J.KB), kb = (int)(u - (int64_t)vrb * J.KB);
     const int j = lane >> 4, i = lane & 15;
-    const int col = kb * kUnitCols + i * 8;
+    const int col = kb * kUnitCols + i * 4;  // and col + 64
     int r;  // task-relative row
     const uint16_t* m = nullptr;
     int64_t row = 0;
@@ -712,7 +775,16 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack(const PackJob* jobs, c
       }
     }
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < R && col < J.K) v = *reinterpret_cast<const u32x4*>(m + row * J.K + col);
+    if (r < R && col < J.K) {
+      const uint2 a = *reinterpret_cast<const uint2*>(m + row * J.K + col);
+      v.x = a.x;
+      v.y = a.y;
+    }
+    if (r < R && col + 64 < J.K) {
+      const uint2 b = *reinterpret_cast<const uint2*>(m + row * J.K + col + 64);
+      v.z = b.x;
+      v.w = b.y;
+    }
     *reinterpret_cast<u32x4*>(dst + J.dst_off + u * kUnitBytes + lane * 16) = v;
   }
 }

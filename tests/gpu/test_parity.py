@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import workload
+from oracle import bf16
 from tests.helpers import oracle_model, weights
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +41,21 @@ def check_logits(gpu: np.ndarray, ref: np.ndarray, what: str):
     return err.max(), rel
 
 
+def kv_close(got_u16, ref_u16, max_frac=1e-2):
+    """bf16 caches equal up to one bf16 step (relative) plus 1e-3 of the
+    tensor's rms (absolute), with differences in at most max_frac of entries."""
+    g = bf16.decode(np.asarray(got_u16, dtype=np.uint16))
+    r = bf16.decode(np.asarray(ref_u16, dtype=np.uint16))
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    tol = np.maximum(np.abs(g), np.abs(r)) * 2.0 ** -8 + 1e-3 * rms
+    d = np.abs(g - r)
+    ok = bool(np.all(d <= tol)) and float((d > 0).mean() if d.size else 0.0) < max_frac
+    if not ok:
+        i = np.unravel_index(int(np.argmax(d - tol)), d.shape)
+        print(f"kv mismatch at {i}: got {g[i]!r} ref {r[i]!r} tol {tol[i]!r}; differing {(d > 0).mean():.2e}")
+    return ok
+
+
 def prefill_and_compare(ss, om, prompt, mode=0, cmp_every=True):
     """Teacher-forced: feed each prompt token on GPU and oracle; compare logits."""
     st = om.new_state(1, ss.max_seq)
@@ -63,13 +79,15 @@ def test_tiny_teacher_forced_logits(gains):
     prompt = workload.make_prompt(wl)[0]
     st, worst = prefill_and_compare(ss, om, prompt)
     assert worst < 1e-4          # fp32 accumulation; far inside the bar
-    # KV cache written by the kernel == the oracle's bf16 cache (rare 1-ulp
-    # differences allowed where fp32 and fp64 straddle a rounding boundary)
+    # KV cache written by the kernel == the oracle's bf16 cache, up to the
+    # rounding of an fp32 computation: one bf16 step where fp32 and fp64
+    # straddle a rounding boundary, plus the fp32 absolute error where the
+    # entry is a small result of cancellation (RoPE's rotation); rare.
     P = len(prompt)
-    kg = ss.k[:, 0, :, :P].contiguous().view(torch.int16).cpu().numpy().view(np.uint16).astype(np.int64)
-    ko = st.kcache[:, 0, :, :P].astype(np.int64)
-    diff = np.abs(kg - ko)
-    assert diff.max() <= 1 and (diff > 0).mean() < 1e-3
+    for dev_cache, ref_cache in ((ss.k, st.kcache), (ss.v, st.vcache)):
+        kg = dev_cache[:, 0, :, :P].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        ko = ref_cache[:, 0, :, :P]
+        assert kv_close(kg, ko)
     ss.check()
     ss.close()
 
