@@ -175,6 +175,8 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   if (64 % (D / 8) != 0) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim/8 must divide 64");
   if (d.hidden > 4096) return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden above 4096");
   if (std::max({kb_h, kb_qd, kb_f}) > 255) return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32640");
+  if (int64_t(g.opts.attn_chunks) * (int64_t(d.max_seq) + 1) >= (int64_t(1) << 32))
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: attn_chunks * (max_seq + 1) must stay below 2^32");
   if (d.hidden % 4 || (d.n_q_heads * d.head_dim) % 4 || d.ffn % 4)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden, q width and ffn must be multiples of 4");
   // LDS: control words, two small staging slots, one big slot (down-projection

@@ -77,9 +77,87 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float f[8]) {
   f[6] = __uint_as_float(w.w << 16); f[7] = __uint_as_float(w.w & 0xffff0000u);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// ---- cross-lane exchange without the LDS crossbar ---------------------------
+// DPP lane moves inside rows of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppSwap1 = 0xB1;        // quad_perm [1,0,3,2]: lane i <- i^1
+constexpr int kDppSwap2 = 0x4E;        // quad_perm [2,3,0,1]: lane i <- i^2
+constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- i^8 within each 16
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within each 16
+
+// For lanes paired by xor o, the two values ordered (lane with bit o clear,
+// lane with bit o set): the same ordered pair in both lanes, so any function
+// of it gives both lanes the same result. o = 16 and 32 use the permlane
+// swaps (each returns exactly that pair); o = 4 goes through the crossbar.
+template <int O>
+__device__ __forceinline__ void xpair(float v, float& lo, float& hi) {
+  if constexpr (O == 16 || O == 32) {
+    const auto r = O == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                           : __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    float p;
+    if constexpr (O == 1) p = dpp<kDppSwap1>(v);
+    else if constexpr (O == 2) p = dpp<kDppSwap2>(v);
+    else if constexpr (O == 8) p = dpp<kDppRor8>(v);
+    else p = __shfl_xor(v, O, 64);
+    const bool upper = (threadIdx.x & O) != 0;
+    lo = upper ? p : v;
+    hi = upper ? v : p;
+  }
+}
+
+// Sum over the 16 lanes of each row (every lane of the row gets it).
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<kDppSwap1>(v);
+  v += dpp<kDppSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
   return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<kDppSwap1>(v));
+  v = fmaxf(v, dpp<kDppSwap2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+// Sum over aligned groups of n lanes (n a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int n) {
+  if (n >= 2) v += dpp<kDppSwap1>(v);
+  if (n >= 4) v += dpp<kDppSwap2>(v);
+  if (n >= 8) v += dpp<kDppHalfMirror>(v);
+  if (n >= 16) v += dpp<kDppMirror>(v);
+  float lo, hi;
+  if (n >= 32) { xpair<16>(v, lo, hi); v = lo + hi; }
+  if (n >= 64) { xpair<32>(v, lo, hi); v = lo + hi; }
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
+// Largest value and, among equal values, the smallest index, over the wave
+// (every lane gets it).
+template <int O>
+__device__ __forceinline__ void argmax_step(float& best, int& bi) {
+  float v1, v2, i1, i2;
+  xpair<O>(best, v1, v2);
+  xpair<O>(__int_as_float(bi), i1, i2);
+  const int j1 = __float_as_int(i1), j2 = __float_as_int(i2);
+  const bool take2 = v2 > v1 || (v2 == v1 && j2 < j1);
+  best = take2 ? v2 : v1;
+  bi = take2 ? j2 : j1;
+}
+__device__ __forceinline__ void wave_argmax(float& best, int& bi) {
+  argmax_step<1>(best, bi);
+  argmax_step<2>(best, bi);
+  argmax_step<4>(best, bi);
+  argmax_step<8>(best, bi);
+  argmax_step<16>(best, bi);
+  argmax_step<32>(best, bi);
 }
 
 template <class T>
@@ -174,6 +252,12 @@ __device__ __forceinline__ int task_at(const Params& P, const Ctx& cx, int qi) {
   return cx.single >= 0 ? cx.single : ld_uniform(P.queue_ids, qi);
 }
 
+// floor(c * len / Nc), the first position of attention chunk c of a sequence
+// of len positions (c <= Nc <= 256 and len <= 2^22 keep the product in 32 bits).
+__device__ __forceinline__ int chunk_bound(int c, int64_t len, int Nc) {
+  return (int)((uint32_t)c * (uint32_t)len / (uint32_t)Nc);
+}
+
 __device__ __forceinline__ bool is_big(int type) { return type == T_D || type == T_COMB; }
 // Staging slot of the next task: 2 for down-projection and merge tasks, else
 // the two small slots alternate. Every role walks the queue and calls this
@@ -247,10 +331,11 @@ __device__ __forceinline__ bool wait_event(const Params& P, const Ctx& cx, int e
   for (;;) {
     uint32_t v = 0;
     if (cx.lane < kStripes) v = ld_coh(&P.counters[(size_t)ev * kEventWords + cx.lane * 32]);
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v = __builtin_amdgcn_readfirstlane(__shfl(v, 0, 64));
+    // sum of the 8 stripes in lanes 0..7 (integer adds, any order)
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppSwap1, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppSwap2, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, false);
+    v = __builtin_amdgcn_readfirstlane(v);
     if ((int32_t)(v - need) >= 0) break;
     if (__builtin_amdgcn_readfirstlane(ld_coh(P.abort_flag)) || lds_ld(&cx.ctl[C_ABORT])) {
       if (cx.lane == 0) __hip_atomic_store(&cx.ctl[C_ABORT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -349,7 +434,7 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
   if (active && !valid && lane == 0) __hip_atomic_fetch_or(P.status, kStatusBadPos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!valid) p = 0;
   const int64_t len = (int64_t)p + 1;
-  const int lo = (int)((int64_t)T.chunk * len / P.Nc), hi = (int)((int64_t)(T.chunk + 1) * len / P.Nc);
+  const int lo = chunk_bound(T.chunk, len, P.Nc), hi = chunk_bound(T.chunk + 1, len, P.Nc);
   const bool owner = valid && T.chunk == P.Nc - 1;
   if (lane == 0) {
     ih[H_P] = p;
@@ -481,11 +566,7 @@ __device__ __forceinline__ void retire_matvec(const Params& P, const Ctx& cx, co
         if (last && P.logits_out) P.logits_out[(size_t)c * P.V + T.row0 + r] = v;
         if (v > best || (v == best && T.row0 + r < bi)) { best = v; bi = T.row0 + r; }
       }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-      }
+      wave_argmax(best, bi);
       if (lane == 0) {
         st_coh(P.lm_val + (size_t)c * P.n_lm + T.ordinal, best);
         st_coh(P.lm_idx + (size_t)c * P.n_lm + T.ordinal, bi);
@@ -602,29 +683,42 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
       const int G = P.G, D = P.D, Nc = P.Nc;
       float* ml = const_cast<float*>(data);  // (m, l) per (head, chunk); m becomes the weight
       const float* acc = data + second_off(G * Nc * 2);
-      // per head: the largest chunk maximum, then weight_c = exp(m_c - M) / sum_c exp(m_c - M) l_c
-      for (int h = 0; h < G; ++h) {
+      // per head: the largest chunk maximum M, then weight_c = exp(m_c - M) /
+      // sum_c exp(m_c - M) l_c; the 16 lanes of row h handle head h (G <= 4)
+      {
+        const int h = lane >> 4, c0 = lane & 15;
         float M = -INFINITY;
-        for (int c = lane; c < Nc; c += 64) M = fmaxf(M, ml[(h * Nc + c) * 2]);
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        if (h < G)
+          for (int c = c0; c < Nc; c += 16) M = fmaxf(M, ml[(h * Nc + c) * 2]);
+        M = max16(M);
         float den = 0.f;
-        for (int c = lane; c < Nc; c += 64) {
-          const float mc = ml[(h * Nc + c) * 2];
-          den += mc == -INFINITY ? 0.f : expf(mc - M) * ml[(h * Nc + c) * 2 + 1];
-        }
-        den = wave_sum(den);
+        if (h < G)
+          for (int c = c0; c < Nc; c += 16) {
+            const float mc = ml[(h * Nc + c) * 2];
+            den += mc == -INFINITY ? 0.f : expf(mc - M) * ml[(h * Nc + c) * 2 + 1];
+          }
+        den = sum16(den);
         const float inv = den > 0.f ? 1.0f / den : 0.f;
-        wait_lgkm();
-        for (int c = lane; c < Nc; c += 64) {
-          const float mc = ml[(h * Nc + c) * 2];
-          ml[(h * Nc + c) * 2] = mc == -INFINITY ? 0.f : expf(mc - M) * inv;
-        }
+        if (h < G)
+          for (int c = c0; c < Nc; c += 16) {
+            const float mc = ml[(h * Nc + c) * 2];
+            ml[(h * Nc + c) * 2] = mc == -INFINITY ? 0.f : expf(mc - M) * inv;
+          }
         wait_lgkm();
       }
+      // weighted sum over chunks, eight independent chains so the LDS reads overlap
       for (int idx = lane; idx < G * D; idx += 64) {
         const int h = idx / D, d = idx - h * D;
-        float num = 0.f;
-        for (int c = 0; c < Nc; ++c) num = fmaf(ml[(h * Nc + c) * 2], acc[(size_t)(h * Nc + c) * D + d], num);
+        const float* wc = ml + h * Nc * 2;
+        const float* ac = acc + (size_t)h * Nc * D + d;
+        float n[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int c = 0;
+        for (; c + 8 <= Nc; c += 8) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) n[j] = fmaf(wc[(c + j) * 2], ac[(size_t)(c + j) * D], n[j]);
+        }
+        for (; c < Nc; ++c) n[0] = fmaf(wc[c * 2], ac[(size_t)c * D], n[0]);
+        const float num = ((n[0] + n[1]) + (n[2] + n[3])) + ((n[4] + n[5]) + (n[6] + n[7]));
         st_coh(P.attn + (size_t)T.b * P.Hq * D + ((size_t)T.g * G + h) * D + d, num);
       }
       break;
@@ -640,11 +734,7 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
         const int i2 = ix[t];
         if (v > best || (v == best && i2 < bi)) { best = v; bi = i2; }
       }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-      }
+      wave_argmax(best, bi);
       if (lane == 0) {
         if (bi < 0 || bi >= P.V) bi = 0;  // every logit was NaN
         P.out_tokens[(size_t)step * P.batch + T.b] = bi;

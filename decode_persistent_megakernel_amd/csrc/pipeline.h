@@ -263,8 +263,8 @@ __device__ __forceinline__ void walker_init(Walker& w, const Ctx& cx) {
 
 // [a0, a1): piece s of n things cut into kStreams nearly equal contiguous pieces
 __device__ __forceinline__ void piece(int n, int s, int& a0, int& a1) {
-  a0 = (int)((int64_t)n * s / kStreams);
-  a1 = (int)((int64_t)n * (s + 1) / kStreams);
+  a0 = (int)((uint32_t)n * (uint32_t)s / kStreams);
+  a1 = (int)((uint32_t)n * (uint32_t)(s + 1) / kStreams);
 }
 
 __device__ __forceinline__ void walker_next(const Params& P, Walker& w, const Ctx& cx, int s) {
@@ -295,8 +295,8 @@ __device__ __forceinline__ void walker_next(const Params& P, Walker& w, const Ct
         const int pos = ld_uniform(P.pos_in, w.b) + w.step;
         if (pos >= 0 && pos < P.S) {
           const int64_t len = (int64_t)pos + 1;
-          w.lo = (int)((int64_t)T.chunk * len / P.Nc);
-          w.end = min((int)((int64_t)(T.chunk + 1) * len / P.Nc), pos);
+          w.lo = chunk_bound(T.chunk, len, P.Nc);
+          w.end = min(chunk_bound(T.chunk + 1, len, P.Nc), pos);
           const int ppu = 512 / P.D;  // positions per unit
           const int npu = w.end > w.lo ? (w.end - w.lo + ppu - 1) / ppu : 0;
           int j1;
@@ -441,35 +441,6 @@ __device__ __forceinline__ void feed_done(const Params& P, const Ctx& cx, int s,
 // arithmetic
 // ---------------------------------------------------------------------------
 
-// DPP lane moves inside rows of 16 lanes
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppSwap1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppSwap2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
-constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within each 16
-
-// Sum over aligned groups of n lanes (n a power of two <= 64); every lane of a
-// group ends with the same value.
-__device__ __forceinline__ float group_sum(float v, int n) {
-  if (n >= 2) v += dpp<kDppSwap1>(v);
-  if (n >= 4) v += dpp<kDppSwap2>(v);
-  if (n >= 8) v += dpp<kDppHalfMirror>(v);
-  if (n >= 16) v += dpp<kDppMirror>(v);
-  if (n >= 32) v += __shfl_xor(v, 16, 64);
-  if (n >= 64) v += __shfl_xor(v, 32, 64);
-  return v;
-}
-__device__ __forceinline__ float sum16(float v) {
-  v += dpp<kDppSwap1>(v);
-  v += dpp<kDppSwap2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  v += dpp<kDppMirror>(v);
-  return v;
-}
-
 // Running state of a matvec piece: NC row sums and the (row block, column
 // block) of the next unit.
 template <int NC>
@@ -595,6 +566,32 @@ __device__ __forceinline__ bool stream_matvec(const Params& P, const Ctx& cx, in
   return true;
 }
 
+// One level of the merge of online-softmax states across lanes paired by xor
+// O; both lanes of a pair merge the same ordered pair of states.
+template <int O>
+__device__ __forceinline__ void att_merge_step(int G, float (&mv)[kMaxG], float (&lv)[kMaxG],
+                                               float (&av)[kMaxG][8]) {
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    if (h < G) {
+      float m1, m2, l1, l2;
+      xpair<O>(mv[h], m1, m2);
+      xpair<O>(lv[h], l1, l2);
+      const float M = fmaxf(m1, m2);
+      const float a1 = m1 == -INFINITY ? 0.f : expf(m1 - M);
+      const float a2 = m2 == -INFINITY ? 0.f : expf(m2 - M);
+      lv[h] = l1 * a1 + l2 * a2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x1, x2;
+        xpair<O>(av[h][e], x1, x2);
+        av[h][e] = x1 * a1 + x2 * a2;
+      }
+      mv[h] = M;
+    }
+  }
+}
+
 // Attention piece of stream wave s: lanes hold 8 dims of one position of a
 // block (D/8 lanes per position); each position group keeps an online-softmax
 // state per query head, merged across the wave at the end and stored as
@@ -648,24 +645,12 @@ __device__ __forceinline__ bool stream_att(const Params& P, const Ctx& cx, int s
     }
   }
   // merge the position groups of the wave (lanes with equal dims)
-  for (int o = lpp; o < 64; o <<= 1) {
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-      if (h < G) {
-        const float m2 = __shfl_xor(mv[h], o, 64), l2 = __shfl_xor(lv[h], o, 64);
-        const float M = fmaxf(mv[h], m2);
-        const float a1 = mv[h] == -INFINITY ? 0.f : expf(mv[h] - M);
-        const float a2 = m2 == -INFINITY ? 0.f : expf(m2 - M);
-        lv[h] = lv[h] * a1 + l2 * a2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float o2 = __shfl_xor(av[h][e], o, 64);
-          av[h][e] = av[h][e] * a1 + o2 * a2;
-        }
-        mv[h] = M;
-      }
-    }
-  }
+  if (lpp <= 1) att_merge_step<1>(G, mv, lv, av);
+  if (lpp <= 2) att_merge_step<2>(G, mv, lv, av);
+  if (lpp <= 4) att_merge_step<4>(G, mv, lv, av);
+  if (lpp <= 8) att_merge_step<8>(G, mv, lv, av);
+  if (lpp <= 16) att_merge_step<16>(G, mv, lv, av);
+  if (lpp <= 32) att_merge_step<32>(G, mv, lv, av);
   const int stride = G * (D + 2);
   if (pg == 0) {
 #pragma unroll
