@@ -167,6 +167,35 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   }
   m->packed_bytes = off;
 
+  // --- stream records: the stream tasks of every queue, with staging slots --
+  std::vector<StreamRec> srec;
+  std::vector<int32_t> sptr(1, 0);
+  int srec_max = 0;
+  for (const auto& q : g.queues) {
+    if (q.size() > 65535) return fail(MK_EUNSUPPORTED, "mk_load_weights: a queue holds more than 65535 tasks");
+    int nsmall = 0;
+    const size_t first = srec.size();
+    for (size_t qp = 0; qp < q.size(); ++qp) {
+      const DevTask& x = dt[q[qp]];
+      const int slot = (x.type == T_D || x.type == T_COMB) ? 2 : (nsmall++ & 1);
+      const bool stream = x.type == T_QKV || x.type == T_ATT || x.type == T_O || x.type == T_GU ||
+                          x.type == T_D || x.type == T_LM;
+      if (!stream) continue;
+      if (x.b > 1023 || x.g > 65535 || x.layer > 65535 || x.chunk > 65535)
+        return fail(MK_EUNSUPPORTED, "mk_load_weights: task field out of the stream record's range");
+      StreamRec r{};
+      r.tsbg = uint32_t(x.type) | uint32_t(slot) << 4 | uint32_t(x.b) << 6 | uint32_t(x.g) << 16;
+      r.lc = uint32_t(x.layer) | uint32_t(x.chunk) << 16;
+      r.n_units = x.n_units;
+      r.kq = uint32_t(x.kb) | uint32_t(qp) << 16;
+      r.w_off = x.w_off;
+      srec.push_back(r);
+    }
+    for (size_t j = first; j < srec.size(); ++j) srec[j].flip = nsmall & 1;
+    srec_max = std::max(srec_max, static_cast<int>(srec.size()) - sptr.back());
+    sptr.push_back(static_cast<int32_t>(srec.size()));
+  }
+
   // --- LDS budget -------------------------------------------------------------
   const int D = d.head_dim;
   if (d.max_batch > kMaxCols)
@@ -200,14 +229,15 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   const int64_t big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
   const int64_t part_floats =
       (std::max<int64_t>(int64_t(kStreams) * ncap * max_vrows, int64_t(kStreams) * G * (D + 2)) + 3) & ~int64_t(3);
-  const size_t fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats);
+  const size_t fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
+                       size_t(srec_max) * sizeof(StreamRec);
   const size_t lds_max = 160 * 1024;
   // The rest holds the stream waves' rings of 2 KiB items; each slot is one
   // item in flight, and a few suffice to keep HBM busy (8 KiB in flight per
   // wave already streams near the HBM peak).
   const int64_t item_bytes = 2 * kUnitBytes;
   int64_t ring = std::min<int64_t>(kMaxDepth, (int64_t(lds_max) - int64_t(fixed)) / (kStreams * item_bytes));
-  ring = ring >= 8 ? 8 : ring >= 6 ? 6 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
+  ring = ring >= 8 ? 8 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
   if (ring < kMinDepth)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: staging needs " + std::to_string(fixed) +
                                      " bytes of LDS, leaving no room for the weight rings");
@@ -229,12 +259,15 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   int nlm = 0;
   for (const Task& t : g.tasks) nlm += t.type == T_LM;
   DevTask* d_tasks;
-  int32_t *d_qptr, *d_qids;
+  StreamRec* d_srec;
+  int32_t *d_qptr, *d_qids, *d_sptr;
   uint32_t *d_thr, *d_cnt;
   int rc;
   if ((rc = m->alloc(&d_tasks, dt.size(), "tasks")) || (rc = m->alloc(&d_qptr, g.queues.size() + 1, "queues")) ||
       (rc = m->alloc(&d_qids, g.tasks.size(), "queue ids")) || (rc = m->alloc(&d_thr, g.events.size(), "thresholds")) ||
-      (rc = m->alloc(&d_cnt, g.events.size() * kEventWords, "counters")))
+      (rc = m->alloc(&d_cnt, g.events.size() * kEventWords, "counters")) ||
+      (rc = m->alloc(&d_srec, std::max<size_t>(srec.size(), 1), "stream records")) ||
+      (rc = m->alloc(&d_sptr, sptr.size(), "stream record offsets")))
     return rc;
   std::vector<int32_t> qptr(1, 0), qids;
   for (const auto& q : g.queues) {
@@ -248,6 +281,9 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   }
   HIP_TRY(hipMemcpy(d_tasks, dt.data(), dt.size() * sizeof(DevTask), hipMemcpyHostToDevice), "copy tasks");
   HIP_TRY(hipMemcpy(d_qptr, qptr.data(), qptr.size() * 4, hipMemcpyHostToDevice), "copy queue offsets");
+  if (!srec.empty())
+    HIP_TRY(hipMemcpy(d_srec, srec.data(), srec.size() * sizeof(StreamRec), hipMemcpyHostToDevice), "copy stream records");
+  HIP_TRY(hipMemcpy(d_sptr, sptr.data(), sptr.size() * 4, hipMemcpyHostToDevice), "copy stream record offsets");
   HIP_TRY(hipMemcpy(d_qids, qids.data(), qids.size() * 4, hipMemcpyHostToDevice), "copy queues");
   HIP_TRY(hipMemcpy(d_thr, thr.data(), thr.size() * 4, hipMemcpyHostToDevice), "copy thresholds");
   HIP_TRY(hipMemset(d_cnt, 0, thr.size() * 4 * kEventWords), "clear counters");
@@ -320,6 +356,9 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   P.tasks = d_tasks;
   P.queue_ptr = d_qptr;
   P.queue_ids = d_qids;
+  P.srecs = d_srec;
+  P.srec_ptr = d_sptr;
+  P.srec_max = srec_max;
   P.thresholds = d_thr;
   P.counters = d_cnt;
   P.n_tasks = static_cast<int32_t>(g.tasks.size());

@@ -25,7 +25,7 @@ constexpr int kUnitRows = 4;
 constexpr int kCtlWaves = 2;
 constexpr int kStreams = 4;
 constexpr int kThreads = 64 * (kCtlWaves + kStreams);
-constexpr int kMaxDepth = 8;   // ring slots (2 KiB items) per stream wave: 4, 6 or 8
+constexpr int kMaxDepth = 8;   // ring slots (2 KiB items) per stream wave: 4 or 8
 constexpr int kMinDepth = 4;   // fewer cannot hide the copy latency
 constexpr int kMaxCols = 4;    // sequences a matvec task handles
 constexpr int kMaxG = 4;       // query heads per kv head
@@ -33,7 +33,7 @@ constexpr int kStripes = 8;    // event counter stripes (one per XCD)
 constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte line
 constexpr int kCtlBytes = 1024;             // control words + ring metadata (see kernels)
 constexpr int kWaves = kThreads / 64;
-constexpr int kWaitWords = 8;               // per-wave wait counters (mk_set_wait_counters)
+constexpr int kWaitWords = 16;              // per-wave wait counters (mk_set_wait_counters)
 
 // status word bits (device)
 constexpr int32_t kStatusBadToken = 1;
@@ -51,11 +51,28 @@ struct DevTask {
   int64_t w_off;     // byte offset of the task's units in the packed weights
 };
 
+// A streamed task (weight or KV units) as the stream waves walk it: one per
+// such task of a workgroup's queue, in queue order, held in LDS.
+struct StreamRec {
+  uint32_t tsbg;     // type | slot << 4 | b << 6 | g << 16  (staging slot in the first step:
+                     // 0, 1 small, 2 big)
+  uint32_t lc;       // layer | chunk << 16
+  int32_t n_units;   // weight units (matvec)
+  uint32_t kq;       // column blocks | queue position << 16
+  int64_t w_off;     // packed weight offset (matvec)
+  int32_t flip;      // 1: the small slots swap from one step to the next (odd count per step)
+  int32_t pad;
+};
+static_assert(sizeof(StreamRec) == 32, "stream records are two 16-byte words");
+
 struct Params {
   // graph
   const DevTask* tasks;
   const int32_t* queue_ptr;   // [num_cus + 1]
   const int32_t* queue_ids;
+  const StreamRec* srecs;     // stream records of all queues
+  const int32_t* srec_ptr;    // [num_cus + 1]
+  int32_t srec_max;           // most records of one queue (LDS holds them)
   const uint32_t* thresholds;
   uint32_t* counters;         // [n_events][kEventWords]
   int32_t n_tasks;

@@ -47,7 +47,8 @@ constexpr int kHdr = 32;           // floats of header at the start of a slot
 
 // LDS control words (ints)
 enum { C_STAGED = 0, C_RETIRED = 1, C_DONE = 2 /* 3 slots */, C_STEPOK = 5, C_ABORT = 6, kCtlWords = 64 };
-static_assert(kCtlWords * 4 <= kCtlBytes, "control area");
+// then the waves' wait counters (kWaitWords each)
+static_assert((kCtlWords + kWaves * kWaitWords) * 4 <= kCtlBytes, "control area");
 // slot header fields (as int)
 enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11 };
 
@@ -221,6 +222,8 @@ struct Ctx {
   float* parts;    // three partial-sum areas
   int small_floats, part_floats;
   uint8_t* ring;   // [kStreams][ring_slots][2 KiB]
+  StreamRec* recs; // this queue's stream records (LDS)
+  int nrec;
   int cu;          // stripe / profile id
   int single;      // >= 0: the one task this workgroup runs (per-operator mode)
   int q0, q1;      // queue range
@@ -260,8 +263,9 @@ __device__ __forceinline__ int chunk_bound(int c, int64_t len, int Nc) {
 
 __device__ __forceinline__ bool is_big(int type) { return type == T_D || type == T_COMB; }
 // Staging slot of the next task: 2 for down-projection and merge tasks, else
-// the two small slots alternate. Every role walks the queue and calls this
-// for every task, so all agree.
+// the two small slots alternate over the whole walk of the queue (across
+// steps). The stream waves' records carry the assignment of the first step
+// and whether it flips from one step to the next.
 __device__ __forceinline__ int next_slot(int& nsmall, int type) {
   if (is_big(type)) return 2;
   return (nsmall++) & 1;
@@ -292,29 +296,34 @@ __device__ __forceinline__ bool spin_ctl(const Params& P, const Ctx& cx, int w, 
   return true;
 }
 
-// Optional per-wave wait accounting: four counters (100 MHz ticks or counts)
-// and the wave's lifetime, added into P.waits when the wave finishes.
+// Optional per-wave wait accounting (diagnostics): counters of 100 MHz ticks
+// (or counts) kept in this wave's words of the LDS control area, so that they
+// hold no registers; added into P.waits when the wave finishes.
 struct Waits {
-  uint64_t c[6];  // words 0-3, then 5-6 (word 4: lifetime)
-  uint64_t t0;
+  uint32_t* c;  // kWaitWords words; word 4 holds the start time, then the lifetime
   bool on;
 };
-__device__ __forceinline__ void waits_init(const Params& P, Waits& w) {
+__device__ __forceinline__ uint32_t* waits_area(const Ctx& cx) {
+  return reinterpret_cast<uint32_t*>(cx.ctl) + kCtlWords + (threadIdx.x >> 6) * kWaitWords;
+}
+__device__ __forceinline__ void waits_init(const Params& P, const Ctx& cx, Waits& w) {
   w.on = P.waits != nullptr;
-  w.c[0] = w.c[1] = w.c[2] = w.c[3] = w.c[4] = w.c[5] = 0;
-  w.t0 = w.on ? wall_clock64() : 0;
+  w.c = waits_area(cx);
+  if (w.on && cx.lane == 0) w.c[4] = (uint32_t)wall_clock64();
 }
 __device__ __forceinline__ uint64_t waits_now(const Waits& w) { return w.on ? wall_clock64() : 0; }
+__device__ __forceinline__ void waits_count(Waits& w, int j, uint32_t n) {
+  if (w.on && (threadIdx.x & 63) == 0) w.c[j] += n;
+}
 __device__ __forceinline__ void waits_add(Waits& w, int j, uint64_t since) {
-  if (w.on) w.c[j] += wall_clock64() - since;
+  if (w.on) waits_count(w, j, (uint32_t)(wall_clock64() - since));
 }
 __device__ __forceinline__ void waits_put(const Params& P, const Ctx& cx, const Waits& w) {
   if (!w.on || cx.lane != 0) return;
   uint64_t* o = P.waits + ((size_t)cx.cu * kWaves + (threadIdx.x >> 6)) * kWaitWords;
-#pragma unroll
-  for (int j = 0; j < 6; ++j)
-    __hip_atomic_fetch_add(&o[j < 4 ? j : j + 1], w.c[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_fetch_add(&o[4], wall_clock64() - w.t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t life = (uint32_t)wall_clock64() - w.c[4];
+  for (int j = 0; j < kWaitWords; ++j)
+    __hip_atomic_fetch_add(&o[j], (uint64_t)(j == 4 ? life : w.c[j]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ bool has_stream(int type) {
@@ -357,21 +366,41 @@ __device__ __forceinline__ void stage_copy(const Ctx& cx, const float* src, floa
   wait_all();
 }
 
-__device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, const DevTask& T, int slot) {
+// Work of a matvec task that does not depend on its event, done while the
+// stager waits for it: clear the slot's partial sums and, for tasks whose
+// input is RMS-normalised, load this lane's gains.
+struct StagePre {
+  uint2 g[16];  // bf16 gains of columns (lane + 64 t) * 4 .. +4 (hidden <= 4096)
+};
+__device__ __forceinline__ bool is_normed(int type) { return type == T_QKV || type == T_GU || type == T_LM; }
+
+__device__ __forceinline__ void stage_matvec_pre(const Params& P, const Ctx& cx, const DevTask& T, int slot,
+                                                 StagePre& pre) {
+  const int lane = cx.lane;
+  float4* pz = reinterpret_cast<float4*>(part_ptr(cx, slot));
+  for (int k = lane; k < P.part_floats / 4; k += 64) pz[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (is_normed(T.type)) {
+    const uint16_t* gain = P.gains + (T.type == T_LM ? (size_t)P.L * 2 * P.H
+                                                     : ((size_t)T.layer * 2 + (T.type == T_GU)) * P.H);
+    const int K = T.kdim;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int k0 = (lane + 64 * t) * 4;
+      pre.g[t] = k0 < K ? *reinterpret_cast<const uint2*>(gain + k0) : make_uint2(0u, 0u);
+    }
+  }
+}
+
+__device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, const DevTask& T, int slot,
+                                             const StagePre& pre) {
   float* hdr = slot_ptr(cx, slot);
   const int kp = slot_kp(P, slot);
   float* in = hdr + kHdr;
   float* res = in + (size_t)P.ncap * kp;
   const int lane = cx.lane;
-  {  // clear this slot's partial sums
-    float4* pz = reinterpret_cast<float4*>(part_ptr(cx, slot));
-    for (int k = lane; k < P.part_floats / 4; k += 64) pz[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   const int ncols = P.batch;
   const int K = T.kdim;
-  if (T.type == T_QKV || T.type == T_GU || T.type == T_LM) {
-    const uint16_t* gain = P.gains + (T.type == T_LM ? (size_t)P.L * 2 * P.H
-                                                     : ((size_t)T.layer * 2 + (T.type == T_GU)) * P.H);
+  if (is_normed(T.type)) {
     for (int c = 0; c < ncols; ++c) {
       const rsrc_t r = make_rsrc(P.x + (size_t)c * P.H, (uint32_t)P.H * 4);
       const int nl = (K + 255) / 256;  // <= 16 (H <= 4096)
@@ -389,7 +418,7 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
           v.z = __uint_as_float(buf[t].z); v.w = __uint_as_float(buf[t].w);
           if (k0 < K) {
             ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss); ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
-            const uint2 gg = *reinterpret_cast<const uint2*>(gain + k0);
+            const uint2 gg = pre.g[t];
             v.x *= bf2f(gg.x & 0xffffu); v.y *= bf2f(gg.x >> 16); v.z *= bf2f(gg.y & 0xffffu); v.w *= bf2f(gg.y >> 16);
           } else {
             v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -404,11 +433,17 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
     }
   } else {  // O (attention output) or D (SiLU*up), plus the residual rows
     const float* src = T.type == T_O ? P.attn : P.mlp;
+    const int R = T.row1 - T.row0;
     for (int c = 0; c < ncols; ++c) {
-      stage_copy(cx, src + (size_t)c * K, in + (size_t)c * kp, K);
+      // the residual rows travel with the input copy: one round trip
+      float rv = 0.f;
+      if (lane < R) rv = ld_coh(P.x + (size_t)c * P.H + T.row0 + lane);
+      const int nl = (K + 255) / 256;
+      for (int t = 0; t < nl; ++t) dma16<kAuxCoherent>(src + (size_t)c * K + t * 256 + lane * 4, in + (size_t)c * kp + t * 256);
+      wait_all();
       for (int k = K + lane; k < kp; k += 64) in[(size_t)c * kp + k] = 0.f;
-      const int R = T.row1 - T.row0;
-      for (int r = lane; r < R; r += 64) res[(size_t)c * P.vrow_stride + r] = ld_coh(P.x + (size_t)c * P.H + T.row0 + r);
+      if (lane < R) res[(size_t)c * P.vrow_stride + lane] = rv;
+      for (int r = 64 + lane; r < R; r += 64) res[(size_t)c * P.vrow_stride + r] = ld_coh(P.x + (size_t)c * P.H + T.row0 + r);
     }
   }
 }
@@ -470,7 +505,8 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
 // offset of the second staged array of merge / argmax tasks
 __device__ __forceinline__ int second_off(int n) { return (n + 255) & ~255; }
 
-__device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
+__device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step,
+                                           const StagePre& pre) {
   float* hdr = slot_ptr(cx, slot);
   float* data = hdr + kHdr;
   const int lane = cx.lane;
@@ -503,7 +539,7 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
                  P.n_lm);
       break;
     }
-    default: stage_matvec(P, cx, T, slot); break;
+    default: stage_matvec(P, cx, T, slot, pre); break;
   }
 }
 
@@ -511,7 +547,7 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
   int last0 = -1, last1 = -1, last2 = -1;  // last task staged into each slot
   Waits wt;  // slot free, dependency event, staging, tasks
-  waits_init(P, wt);
+  waits_init(P, cx, wt);
   for (int step = 0; step < P.n_steps; ++step) {
     const uint32_t epoch = P.epoch0 + (uint32_t)step;
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
@@ -523,17 +559,21 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
       if (prev >= 0 && !spin_ctl(P, cx, C_RETIRED, prev + 1)) return;
       waits_add(wt, 0, s0);
       if (slot == 0) last0 = i; else if (slot == 1) last1 = i; else last2 = i;
+      StagePre pre;
+      if (T.type == T_QKV || T.type == T_O || T.type == T_GU || T.type == T_D || T.type == T_LM)
+        stage_matvec_pre(P, cx, T, slot, pre);
       s0 = waits_now(wt);
       if (P.use_events) {
         const uint32_t mult = T.type == T_EMB ? epoch : epoch + 1;
-        if (!wait_event(P, cx, T.dep, P.thresholds[T.dep] * mult)) return;
+        const uint32_t thr = (uint32_t)ld_uniform(reinterpret_cast<const int32_t*>(P.thresholds), T.dep);
+        if (!wait_event(P, cx, T.dep, thr * mult)) return;
       }
       waits_add(wt, 1, s0);
       if (qi == cx.q0) lds_st(&cx.ctl[C_STEPOK], step + 1);
       s0 = waits_now(wt);
-      stage_task(P, cx, T, slot, step);
+      stage_task(P, cx, T, slot, step, pre);
       waits_add(wt, 2, s0);
-      ++wt.c[3];
+      waits_count(wt, 3, 1);
       lds_st(&cx.ctl[C_STAGED], i + 1);
     }
   }
@@ -749,7 +789,7 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
 __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
   Waits wt;  // staged, computed, epilogue, tasks
-  waits_init(P, wt);
+  waits_init(P, cx, wt);
   for (int step = 0; step < P.n_steps; ++step) {
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
       const int id = task_at(P, cx, qi);
@@ -761,11 +801,11 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
       const uint64_t t_staged = wall_clock64();
       if (has_stream(T.type) && !spin_ctl(P, cx, C_DONE + slot, kStreams)) return;
       const uint64_t t_computed = wall_clock64();
-      if (wt.on) wt.c[1] += t_computed - t_staged;
+      waits_count(wt, 1, (uint32_t)(t_computed - t_staged));
       retire_task(P, cx, T, slot, step);
       wait_all();  // every store of the epilogue has completed
       waits_add(wt, 2, t_computed);
-      ++wt.c[3];
+      waits_count(wt, 3, 1);
       if (cx.lane == 0) {
         if (P.use_events && id != P.drop_task)
           __hip_atomic_fetch_add(&P.counters[(size_t)T.trig * kEventWords + (cx.cu & (kStripes - 1)) * 32], 1u,
@@ -811,14 +851,36 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
     cx.q1 = ld_uniform(P.queue_ptr, cu + 1);
   }
   cx.lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) cx.ctl[threadIdx.x] = 0;
+  cx.recs = reinterpret_cast<StreamRec*>(cx.ring + (size_t)kStreams * P.ring_slots * 2 * kUnitBytes);
+  for (int j = threadIdx.x; j < kCtlBytes / 4; j += blockDim.x) cx.ctl[j] = 0;
+  if (single < 0) {
+    const int r0 = ld_uniform(P.srec_ptr, cu), r1 = ld_uniform(P.srec_ptr, cu + 1);
+    cx.nrec = r1 - r0;
+    const int32_t* src = reinterpret_cast<const int32_t*>(P.srecs + r0);
+    int32_t* dst = reinterpret_cast<int32_t*>(cx.recs);
+    for (int j = threadIdx.x; j < cx.nrec * 8; j += blockDim.x) dst[j] = src[j];
+  } else {
+    // one task: its record, in the slot the first task of a queue gets
+    const DevTask T = ld_task(P, single);
+    cx.nrec = has_stream(T.type) ? 1 : 0;
+    if (threadIdx.x == 0 && cx.nrec) {
+      StreamRec r;
+      r.tsbg = (uint32_t)T.type | (uint32_t)(is_big(T.type) ? 2 : 0) << 4 | (uint32_t)T.b << 6 | (uint32_t)T.g << 16;
+      r.lc = (uint32_t)T.layer | (uint32_t)T.chunk << 16;
+      r.n_units = T.n_units;
+      r.kq = (uint32_t)T.kb;
+      r.w_off = T.w_off;
+      r.flip = 0;
+      r.pad = 0;
+      cx.recs[0] = r;
+    }
+  }
   __syncthreads();
   // wave index as a wave-uniform value: every role's control flow is scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) run_stager(P, cx);
   else if (wave == 1) run_retirer(P, cx);
   else if (P.ring_slots >= 8) run_stream<8>(P, cx, wave - kCtlWaves);
-  else if (P.ring_slots >= 6) run_stream<6>(P, cx, wave - kCtlWaves);
   else run_stream<4>(P, cx, wave - kCtlWaves);
 }
 

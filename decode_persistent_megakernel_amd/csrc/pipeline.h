@@ -9,233 +9,48 @@
 // the K block and the V block of one group of positions.
 //
 // A stream wave feeds itself: it copies its items from HBM straight into a
-// private LDS ring of D slots (LDS DMA), D items ahead of the one it computes,
-// running ahead across task boundaries so weights keep arriving while the
-// workgroup waits on an event. Copies complete in issue order, so "item k has
-// landed" is a wait for the vector-memory counter to drop to twice the number
-// of younger items. The wave's LDS reads and writes are written as inline
-// assembly: the compiler cannot tell them apart from the LDS the copies are
-// writing and would otherwise wait for every copy in flight before each of
-// them. (Each asm block that loads waits for its own loads before it ends.)
-//
+// private LDS ring of DEPTH slots (LDS DMA), DEPTH items ahead of the one it
+// computes, running ahead across task boundaries so weights keep arriving
+// while the workgroup waits on an event. Copies complete in issue order, so
+// "item k has landed" is a wait for the vector-memory counter to drop to twice
+// the number of younger items. The copies are issued as inline assembly: the
+// compiler then leaves the wave's own LDS reads alone (it would otherwise wait
+// for every copy in flight before each of them, not knowing which LDS bytes
+// a copy writes) and schedules them freely; the explicit counter waits order
+// every read after the copy that fills its slot.
+
 // Attention items of a step read KV entries appended in earlier steps, so
 // they are copied only after the stager has passed the step's first
 // dependency (C_STEPOK); weight items never wait for anything but a free slot.
 
 // ---------------------------------------------------------------------------
-// LDS access for the stream waves (invisible to the compiler's memory model)
+// copies for the stream waves
 // ---------------------------------------------------------------------------
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));  // asm operand type of 16 bytes
-
-__device__ __forceinline__ void lds_write_b32(uint32_t addr, float v) {
-  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+// 1 KiB per wave: lane l copies 16 bytes from its own address src into LDS
+// byte address lds + 16*l (lds is wave-uniform; it goes in M0, which this
+// wave's code uses for nothing else). nt: streamed once; sc1: device-coherent.
+__device__ __forceinline__ void copy_nt(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds)
+               : "memory", "m0");
 }
-__device__ __forceinline__ void lds_write_b128(uint32_t addr, f32x4 v) {
-  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
-}
-__device__ __forceinline__ void lds_add_raw(uint32_t addr, int v) {
-  asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
-}
-__device__ __forceinline__ void lds_read_2x128(uint32_t a, uint32_t b, f32x4& x, f32x4& y) {
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x), "=&v"(y)
-      : "v"(a), "v"(b)
-      : "memory");
-}
-// An item (two 1 KiB halves at `item` and item+1024) and, for NC columns, the
-// activations of the item's two units (unit A at ha[c], unit B at hb[c]; each
-// 4 floats at +0 and 4 floats at +256 bytes).
-template <int NC>
-struct ItemRegs {
-  u32x4 w0, w1;
-  f32x4 a[NC][2], b[NC][2];
-};
-__device__ __forceinline__ void lds_item(uint32_t item, const uint32_t (&ha)[1], const uint32_t (&hb)[1],
-                                         ItemRegs<1>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %6 offset:1024\n\t"
-      "ds_read_b128 %2, %7\n\t"
-      "ds_read_b128 %3, %7 offset:256\n\t"
-      "ds_read_b128 %4, %8\n\t"
-      "ds_read_b128 %5, %8 offset:256\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.w0), "=&v"(r.w1), "=&v"(r.a[0][0]), "=&v"(r.a[0][1]), "=&v"(r.b[0][0]), "=&v"(r.b[0][1])
-      : "v"(item), "v"(ha[0]), "v"(hb[0])
-      : "memory");
-}
-__device__ __forceinline__ void lds_item(uint32_t item, const uint32_t (&ha)[2], const uint32_t (&hb)[2],
-                                         ItemRegs<2>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %10\n\t"
-      "ds_read_b128 %1, %10 offset:1024\n\t"
-      "ds_read_b128 %2, %11\n\t"
-      "ds_read_b128 %3, %11 offset:256\n\t"
-      "ds_read_b128 %4, %12\n\t"
-      "ds_read_b128 %5, %12 offset:256\n\t"
-      "ds_read_b128 %6, %13\n\t"
-      "ds_read_b128 %7, %13 offset:256\n\t"
-      "ds_read_b128 %8, %14\n\t"
-      "ds_read_b128 %9, %14 offset:256\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.w0), "=&v"(r.w1), "=&v"(r.a[0][0]), "=&v"(r.a[0][1]), "=&v"(r.b[0][0]), "=&v"(r.b[0][1]),
-        "=&v"(r.a[1][0]), "=&v"(r.a[1][1]), "=&v"(r.b[1][0]), "=&v"(r.b[1][1])
-      : "v"(item), "v"(ha[0]), "v"(hb[0]), "v"(ha[1]), "v"(hb[1])
-      : "memory");
-}
-__device__ __forceinline__ void lds_item(uint32_t item, const uint32_t (&ha)[3], const uint32_t (&hb)[3],
-                                         ItemRegs<3>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %14\n\t"
-      "ds_read_b128 %1, %14 offset:1024\n\t"
-      "ds_read_b128 %2, %15\n\t"
-      "ds_read_b128 %3, %15 offset:256\n\t"
-      "ds_read_b128 %4, %16\n\t"
-      "ds_read_b128 %5, %16 offset:256\n\t"
-      "ds_read_b128 %6, %17\n\t"
-      "ds_read_b128 %7, %17 offset:256\n\t"
-      "ds_read_b128 %8, %18\n\t"
-      "ds_read_b128 %9, %18 offset:256\n\t"
-      "ds_read_b128 %10, %19\n\t"
-      "ds_read_b128 %11, %19 offset:256\n\t"
-      "ds_read_b128 %12, %20\n\t"
-      "ds_read_b128 %13, %20 offset:256\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.w0), "=&v"(r.w1), "=&v"(r.a[0][0]), "=&v"(r.a[0][1]), "=&v"(r.b[0][0]), "=&v"(r.b[0][1]),
-        "=&v"(r.a[1][0]), "=&v"(r.a[1][1]), "=&v"(r.b[1][0]), "=&v"(r.b[1][1]), "=&v"(r.a[2][0]),
-        "=&v"(r.a[2][1]), "=&v"(r.b[2][0]), "=&v"(r.b[2][1])
-      : "v"(item), "v"(ha[0]), "v"(hb[0]), "v"(ha[1]), "v"(hb[1]), "v"(ha[2]), "v"(hb[2])
-      : "memory");
-}
-__device__ __forceinline__ void lds_item(uint32_t item, const uint32_t (&ha)[4], const uint32_t (&hb)[4],
-                                         ItemRegs<4>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %18\n\t"
-      "ds_read_b128 %1, %18 offset:1024\n\t"
-      "ds_read_b128 %2, %19\n\t"
-      "ds_read_b128 %3, %19 offset:256\n\t"
-      "ds_read_b128 %4, %20\n\t"
-      "ds_read_b128 %5, %20 offset:256\n\t"
-      "ds_read_b128 %6, %21\n\t"
-      "ds_read_b128 %7, %21 offset:256\n\t"
-      "ds_read_b128 %8, %22\n\t"
-      "ds_read_b128 %9, %22 offset:256\n\t"
-      "ds_read_b128 %10, %23\n\t"
-      "ds_read_b128 %11, %23 offset:256\n\t"
-      "ds_read_b128 %12, %24\n\t"
-      "ds_read_b128 %13, %24 offset:256\n\t"
-      "ds_read_b128 %14, %25\n\t"
-      "ds_read_b128 %15, %25 offset:256\n\t"
-      "ds_read_b128 %16, %26\n\t"
-      "ds_read_b128 %17, %26 offset:256\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.w0), "=&v"(r.w1), "=&v"(r.a[0][0]), "=&v"(r.a[0][1]), "=&v"(r.b[0][0]), "=&v"(r.b[0][1]),
-        "=&v"(r.a[1][0]), "=&v"(r.a[1][1]), "=&v"(r.b[1][0]), "=&v"(r.b[1][1]), "=&v"(r.a[2][0]),
-        "=&v"(r.a[2][1]), "=&v"(r.b[2][0]), "=&v"(r.b[2][1]), "=&v"(r.a[3][0]), "=&v"(r.a[3][1]),
-        "=&v"(r.b[3][0]), "=&v"(r.b[3][1])
-      : "v"(item), "v"(ha[0]), "v"(hb[0]), "v"(ha[1]), "v"(hb[1]), "v"(ha[2]), "v"(hb[2]), "v"(ha[3]),
-        "v"(hb[3])
-      : "memory");
-}
-// Two items (in slots at i0 and i1) and, for NC columns, the activations of
-// their four units u = 0..3 at h[u][c].
-template <int NC>
-struct Item2Regs {
-  u32x4 w[4];
-  f32x4 h[4][NC][2];
-};
-__device__ __forceinline__ void lds_item2(uint32_t i0, uint32_t i1, const uint32_t (&h)[4][1], Item2Regs<1>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %12 offset:1024\n\t"
-      "ds_read_b128 %2, %13\n\t"
-      "ds_read_b128 %3, %13 offset:1024\n\t"
-      "ds_read_b128 %4, %14\n\t"
-      "ds_read_b128 %5, %14 offset:256\n\t"
-      "ds_read_b128 %6, %15\n\t"
-      "ds_read_b128 %7, %15 offset:256\n\t"
-      "ds_read_b128 %8, %16\n\t"
-      "ds_read_b128 %9, %16 offset:256\n\t"
-      "ds_read_b128 %10, %17\n\t"
-      "ds_read_b128 %11, %17 offset:256\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.w[0]), "=&v"(r.w[1]), "=&v"(r.w[2]), "=&v"(r.w[3]), "=&v"(r.h[0][0][0]), "=&v"(r.h[0][0][1]),
-        "=&v"(r.h[1][0][0]), "=&v"(r.h[1][0][1]), "=&v"(r.h[2][0][0]), "=&v"(r.h[2][0][1]), "=&v"(r.h[3][0][0]),
-        "=&v"(r.h[3][0][1])
-      : "v"(i0), "v"(i1), "v"(h[0][0]), "v"(h[1][0]), "v"(h[2][0]), "v"(h[3][0])
-      : "memory");
-}
-__device__ __forceinline__ void lds_item2(uint32_t i0, uint32_t i1, const uint32_t (&h)[4][2], Item2Regs<2>& r) {
-  asm volatile(
-      "ds_read_b128 %0, %20\n\t"
-      "ds_read_b128 %1, %20 offset:1024\n\t"
-      "ds_read_b128 %2, %21\n\t"
-      "ds_read_b128 %3, %21 offset:1024\n\t"
-      "ds_read_b128 %4, %22\n\t"
-      "ds_read_b128 %5, %22 offset:256\n\t"
-      "ds_read_b128 %6, %23\n\t"
-      "ds_read_b128 %7, %23 offset:256\n\t"
-      "ds_read_b128 %8, %24\n\t"
-      "ds_read_b128 %9, %24 offset:256\n\t"
-      "ds_read_b128 %10, %25\n\t"
-      "ds_read_b128 %11, %25 offset:256\n\t"
-      "ds_read_b128 %12, %26\n\t"
-      "ds_read_b128 %13, %26 offset:256\n\t"
-      "ds_read_b128 %14, %27\n\t"
-      "ds_read_b128 %15, %27 offset:256\n\t"
-      "ds_read_b128 %16, %28\n\t"
-      "ds_read_b128 %17, %28 offset:256\n\t"
-      "ds_read_b128 %18, %29\n\t"
-      "ds_read_b128 %19, %29 offset:256\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.w[0]), "=&v"(r.w[1]), "=&v"(r.w[2]), "=&v"(r.w[3]), "=&v"(r.h[0][0][0]), "=&v"(r.h[0][0][1]),
-        "=&v"(r.h[0][1][0]), "=&v"(r.h[0][1][1]), "=&v"(r.h[1][0][0]), "=&v"(r.h[1][0][1]), "=&v"(r.h[1][1][0]),
-        "=&v"(r.h[1][1][1]), "=&v"(r.h[2][0][0]), "=&v"(r.h[2][0][1]), "=&v"(r.h[2][1][0]), "=&v"(r.h[2][1][1]),
-        "=&v"(r.h[3][0][0]), "=&v"(r.h[3][0][1]), "=&v"(r.h[3][1][0]), "=&v"(r.h[3][1][1])
-      : "v"(i0), "v"(i1), "v"(h[0][0]), "v"(h[0][1]), "v"(h[1][0]), "v"(h[1][1]), "v"(h[2][0]), "v"(h[2][1]),
-        "v"(h[3][0]), "v"(h[3][1])
-      : "memory");
-}
-__device__ __forceinline__ void lds_item_kv(uint32_t item, u32x4& k, u32x4& v) {
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %2 offset:1024\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k), "=&v"(v)
-      : "v"(item)
-      : "memory");
+__device__ __forceinline__ void copy_sc1(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" : : "v"(src), "s"(lds)
+               : "memory", "m0");
 }
 
-// Spin until ctl[word] >= v (asm reads; bounded by the watchdog).
-__device__ __forceinline__ bool spin_raw(const Params& P, const Ctx& cx, int word, int v) {
-  if (lds_ld_raw(&cx.ctl[word]) >= v) return true;
-  const uint64_t t0 = wall_clock64();
-  for (;;) {
-    __builtin_amdgcn_s_sleep(1);
-    if (lds_ld_raw(&cx.ctl[word]) >= v) return true;
-    if (lds_ld_raw(&cx.ctl[C_ABORT])) return false;
-    if (wall_clock64() - t0 > P.timeout_ticks) {
-      raise_abort(P, cx, kStatusTimeout);
-      return false;
-    }
-  }
-}
+__device__ __forceinline__ u32x4 ld_u32x4(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 // ---------------------------------------------------------------------------
 // task walking
 // ---------------------------------------------------------------------------
 
 // Walks the stream tasks (those with weight or KV units) of this workgroup's
-// queue, across steps, for stream wave s, keeping the slot assignment of every
-// task.
+// queue, across steps, for stream wave s: the queue's stream records in LDS.
 struct Walker {
-  int step, qi, i;   // i: global task counter of the current task (all tasks)
-  int nsmall, slot;
-  int id, type, layer, b, g;
+  int step, r, i;    // r: record; i: global task counter of the task (all tasks)
+  int slot, type, layer, b, g;
   int nu;            // matvec: units of wave s; attention: position blocks of wave s
   int n;             // items of wave s in the task (may be 0)
   int u0;            // matvec: first unit of wave s; attention: first position block
@@ -247,11 +62,9 @@ struct Walker {
 
 __device__ __forceinline__ void walker_init(Walker& w, const Ctx& cx) {
   w.step = 0;
-  w.qi = cx.q0 - 1;
-  w.i = -1;
-  w.nsmall = 0;
+  w.r = -1;
+  w.i = 0;
   w.slot = 0;
-  w.id = 0;
   w.type = -1;
   w.layer = w.b = w.g = 0;
   w.nu = w.n = w.u0 = 0;
@@ -267,55 +80,54 @@ __device__ __forceinline__ void piece(int n, int s, int& a0, int& a1) {
   a1 = (int)((uint32_t)n * (uint32_t)(s + 1) / kStreams);
 }
 
+__device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ void walker_next(const Params& P, Walker& w, const Ctx& cx, int s) {
-  for (;;) {
-    ++w.qi;
-    ++w.i;
-    if (w.qi >= cx.q1) {
-      w.qi = cx.q0;
-      ++w.step;
-    }
-    if (w.step >= P.n_steps || cx.q0 >= cx.q1) {
-      w.done = true;
-      return;
-    }
-    w.id = task_at(P, cx, w.qi);
-    const DevTask T = ld_task(P, w.id);
-    w.type = T.type;
-    w.slot = next_slot(w.nsmall, w.type);
-    if (!has_stream(w.type)) continue;
-    w.layer = T.layer;
-    w.b = T.b;
-    w.g = T.g;
-    w.nu = 0;
-    w.u0 = 0;
-    if (w.type == T_ATT) {
-      w.lo = w.end = 0;
-      if (w.b < P.batch) {
-        const int pos = ld_uniform(P.pos_in, w.b) + w.step;
-        if (pos >= 0 && pos < P.S) {
-          const int64_t len = (int64_t)pos + 1;
-          w.lo = chunk_bound(T.chunk, len, P.Nc);
-          w.end = min(chunk_bound(T.chunk + 1, len, P.Nc), pos);
-          const int ppu = 512 / P.D;  // positions per unit
-          const int npu = w.end > w.lo ? (w.end - w.lo + ppu - 1) / ppu : 0;
-          int j1;
-          piece(npu, s, w.u0, j1);
-          w.nu = j1 - w.u0;
-        }
-      }
-      w.n = w.nu;
-    } else {
-      const int U = T.n_units;
-      int i0, i1;
-      piece((U + 1) / 2, s, i0, i1);
-      w.u0 = 2 * i0;
-      w.nu = max(min(2 * i1, U) - w.u0, 0);
-      w.n = i1 - i0;
-      w.KB = T.kb;
-      w.woff = T.w_off;
-    }
+  if (++w.r >= cx.nrec) {
+    w.r = 0;
+    ++w.step;
+  }
+  if (w.step >= P.n_steps || cx.nrec == 0) {
+    w.done = true;
     return;
+  }
+  const StreamRec R = cx.recs[w.r];
+  const uint32_t tsbg = rfl(R.tsbg), lc = rfl(R.lc), kq = rfl(R.kq);
+  w.type = tsbg & 15;
+  w.slot = (tsbg >> 4) & 3;
+  if (w.slot < 2) w.slot ^= (int)rfl((uint32_t)R.flip) & w.step;
+  w.b = (tsbg >> 6) & 1023;
+  w.g = tsbg >> 16;
+  w.layer = lc & 0xffff;
+  const int chunk = lc >> 16;
+  w.i = w.step * (cx.q1 - cx.q0) + (int)(kq >> 16);
+  w.nu = 0;
+  w.u0 = 0;
+  if (w.type == T_ATT) {
+    w.lo = w.end = 0;
+    if (w.b < P.batch) {
+      const int pos = ld_uniform(P.pos_in, w.b) + w.step;
+      if (pos >= 0 && pos < P.S) {
+        const int64_t len = (int64_t)pos + 1;
+        w.lo = chunk_bound(chunk, len, P.Nc);
+        w.end = min(chunk_bound(chunk + 1, len, P.Nc), pos);
+        const int ppu = 512 / P.D;  // positions per unit
+        const int npu = w.end > w.lo ? (w.end - w.lo + ppu - 1) / ppu : 0;
+        int j1;
+        piece(npu, s, w.u0, j1);
+        w.nu = j1 - w.u0;
+      }
+    }
+    w.n = w.nu;
+  } else {
+    const int U = (int)rfl((uint32_t)R.n_units);
+    int i0, i1;
+    piece((U + 1) / 2, s, i0, i1);
+    w.u0 = 2 * i0;
+    w.nu = max(min(2 * i1, U) - w.u0, 0);
+    w.n = i1 - i0;
+    w.KB = kq & 0xffff;
+    w.woff = (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
   }
 }
 
@@ -338,7 +150,6 @@ struct Fetch {
   Walker w;            // the task of the next item to copy
   int t;               // its item within that task
   int issued;          // items copied so far
-  int slot;            // ring slot of the next item
   bool kv;             // the task is attention (KV blocks), else a matvec
   const uint8_t* src;  // matvec: this lane's 16 bytes of the next item's first unit
 };
@@ -352,94 +163,93 @@ __device__ __forceinline__ void fetch_next_task(const Params& P, const Ctx& cx, 
   F.src = P.wpack + F.w.woff + (int64_t)F.w.u0 * kUnitBytes + cx.lane * 16;
 }
 
+// Ring of a stream wave: DEPTH (a power of two) slots of 2 KiB; item k sits in
+// slot k % DEPTH. Byte address of item k (LDS) for the copies; pointer for reads.
+template <int DEPTH>
+__device__ __forceinline__ uint32_t ring_slot(uint32_t ring, int k) {
+  return ring + (uint32_t)(k & (DEPTH - 1)) * kItemBytes;
+}
+
 // Copy items until `limit` have been issued, the task sequence ends, or the
 // next item is a KV block of a step the stager has not opened yet. A matvec
 // item is the next 2 KiB of the task's packed weights.
 template <int DEPTH>
 __device__ __forceinline__ void fetch_upto(const Params& P, const Ctx& cx, int s, Fetch& F, int limit,
-                                           uint8_t* ring) {
+                                           uint32_t ring) {
   while (F.issued < limit && !F.w.done) {
-    uint8_t* dst = ring + F.slot * kItemBytes;
+    const uint32_t dst = ring_slot<DEPTH>(ring, F.issued);
     if (!F.kv) {
-      dma16<kAuxStream>(F.src, dst);
+      copy_nt(F.src, dst);
       // the second unit of a piece's last item may not exist: copy the first again
-      dma16<kAuxStream>(2 * F.t + 1 < F.w.nu ? F.src + kUnitBytes : F.src, dst + kUnitBytes);
+      copy_nt(2 * F.t + 1 < F.w.nu ? F.src + kUnitBytes : F.src, dst + kUnitBytes);
       F.src += kItemBytes;
     } else {
-      if (F.t == 0 && lds_ld_raw(&cx.ctl[C_STEPOK]) < F.w.step + 1) return;
+      if (F.t == 0 && lds_ld(&cx.ctl[C_STEPOK]) < F.w.step + 1) return;
       const int lane = cx.lane;
       const int D8 = P.D / 8, ppu = 64 / D8;
       const int pos = min(F.w.lo + (F.w.u0 + F.t) * ppu + lane / D8, F.w.end - 1);
       const size_t off =
           ((((size_t)F.w.layer * P.B + F.w.b) * P.Hkv + F.w.g) * (size_t)P.S + pos) * P.D + (lane % D8) * 8;
-      dma16<kAuxCoherent>(P.kcache + off, dst);
-      dma16<kAuxCoherent>(P.vcache + off, dst + kUnitBytes);
+      copy_sc1(P.kcache + off, dst);
+      copy_sc1(P.vcache + off, dst + kUnitBytes);
     }
     ++F.issued;
-    F.slot = F.slot + 1 == DEPTH ? 0 : F.slot + 1;
     if (++F.t == F.w.n) fetch_next_task(P, cx, s, F);
   }
 }
 
-// The consuming side: item k (a count over the wave's whole item sequence)
-// is next; it sits in ring slot `slot`.
-struct Feed {
-  int k, slot;
-  uint8_t* ring;
-};
-
-// Make sure item f.k has been copied (waiting for its step to open if needed)
-// and has landed.
-template <int DEPTH>
-__device__ __forceinline__ bool feed_item(const Params& P, const Ctx& cx, int s, Fetch& F, Feed& f, Waits& wt) {
-  if (F.issued <= f.k) {
-    const uint64_t s0 = waits_now(wt);
-    while (F.issued <= f.k) {
-      if (!spin_raw(P, cx, C_STEPOK, F.w.step + 1)) return false;
-      fetch_upto<DEPTH>(P, cx, s, F, f.k + DEPTH, f.ring);
-    }
-    waits_add(wt, 0, s0);
-  }
-  // Steady state: DEPTH - 1 younger items in flight. Fewer only at the end
-  // of the sequence or behind a KV step not yet open: then wait for all.
+// Wait until the oldest `n` not yet consumed items (from item k on) have
+// landed. Steady state: DEPTH - n younger items in flight; fewer only at the
+// end of the sequence or behind a KV step not yet open: then wait for all.
+template <int DEPTH, int N>
+__device__ __forceinline__ void wait_landed(const Fetch& F, int k) {
   cbar();
-  if (F.issued - f.k - 1 == DEPTH - 1) wait_vmcnt<2 * (DEPTH - 1)>();
+  if (F.issued - k == DEPTH) wait_vmcnt<2 * (DEPTH - N)>();
   else wait_vmcnt<0>();
   cbar();
+}
+
+// Make sure items k .. k+n-1 have been copied (waiting for a KV step to open
+// if needed). false = leave the kernel.
+template <int DEPTH>
+__device__ __forceinline__ bool ensure_copied(const Params& P, const Ctx& cx, int s, Fetch& F, int k, int n,
+                                              uint32_t ring, Waits& wt) {
+  if (F.issued >= k + n) return true;
+  const uint64_t s0 = waits_now(wt);
+  while (F.issued < k + n) {
+    if (!spin_ctl(P, cx, C_STEPOK, F.w.step + 1)) return false;
+    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
+  }
+  waits_add(wt, 0, s0);
   return true;
 }
 
-// Items f.k and f.k+1 (both already copied) have landed.
+// Items before k have been read: refill their slots, up to item k + DEPTH - 1.
+// In the steady state that is two whole items of the matvec task being
+// copied: four copies of consecutive 1 KiB.
 template <int DEPTH>
-__device__ __forceinline__ void feed_wait2(const Fetch& F, const Feed& f) {
-  cbar();
-  if (F.issued - f.k - 2 == DEPTH - 2) wait_vmcnt<2 * (DEPTH - 2)>();
-  else wait_vmcnt<0>();
-  cbar();
-}
-
-// Item f.k has been read into registers: its slot takes item k + DEPTH. In
-// the steady state that is one copy, of the matvec task being copied.
-template <int DEPTH>
-__device__ __forceinline__ void feed_done(const Params& P, const Ctx& cx, int s, Fetch& F, Feed& f) {
-  ++f.k;
-  f.slot = f.slot + 1 == DEPTH ? 0 : f.slot + 1;
-  if (F.issued == f.k + DEPTH - 1 && !F.kv && F.t + 1 < F.w.n) {
-    uint8_t* dst = f.ring + F.slot * kItemBytes;
-    dma16<kAuxStream>(F.src, dst);
-    dma16<kAuxStream>(2 * F.t + 1 < F.w.nu ? F.src + kUnitBytes : F.src, dst + kUnitBytes);
-    F.src += kItemBytes;
-    ++F.issued;
-    F.slot = F.slot + 1 == DEPTH ? 0 : F.slot + 1;
-    ++F.t;
+__device__ __forceinline__ void refill(const Params& P, const Ctx& cx, int s, Fetch& F, int k, uint32_t ring) {
+  wait_lgkm();  // the reads of the slots being refilled have completed
+  if (F.issued == k + DEPTH - 2 && !F.kv && F.t + 2 < F.w.n && 2 * F.t + 3 < F.w.nu) {
+    const uint32_t d0 = ring_slot<DEPTH>(ring, F.issued), d1 = ring_slot<DEPTH>(ring, F.issued + 1);
+    copy_nt(F.src, d0);
+    copy_nt(F.src + kUnitBytes, d0 + kUnitBytes);
+    copy_nt(F.src + 2 * kUnitBytes, d1);
+    copy_nt(F.src + 3 * kUnitBytes, d1 + kUnitBytes);
+    F.src += 2 * kItemBytes;
+    F.issued += 2;
+    F.t += 2;
   } else {
-    fetch_upto<DEPTH>(P, cx, s, F, f.k + DEPTH, f.ring);
+    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
   }
 }
 
 // ---------------------------------------------------------------------------
-// arithmetic
+// matvec
 // ---------------------------------------------------------------------------
+
+// the column block after b in a row block of KB
+__device__ __forceinline__ int next_cb(int b, int KB) { return b + 1 == KB ? 0 : b + 1; }
 
 // Running state of a matvec piece: NC row sums and the (row block, column
 // block) of the next unit.
@@ -451,20 +261,20 @@ struct MvState {
 };
 
 // Reduce the row sums over the 16 lanes of each row and store them as this
-// wave's partial sums of row block r (pout: LDS byte address of this lane's
-// row in column 0; cs: byte stride between columns).
+// wave's partial sums of row block r (pout: this lane's row in column 0;
+// cs: floats between columns).
 template <int NC>
-__device__ __forceinline__ void mv_flush(MvState<NC>& st, uint32_t pout, uint32_t cs, int icol, int r) {
+__device__ __forceinline__ void mv_flush(MvState<NC>& st, float* pout, int cs, int icol, int r) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const float v = sum16(st.acc[c]);
-    if (icol == 0) lds_write_b32(pout + c * cs + r * 16, v);
+    if (icol == 0) pout[(size_t)c * cs + r * 4] = v;
     st.acc[c] = 0.f;
   }
 }
 
 template <int NC>
-__device__ __forceinline__ void mv_add(MvState<NC>& st, const float (&d)[NC], int KB, uint32_t pout, uint32_t cs,
+__device__ __forceinline__ void mv_add(MvState<NC>& st, const float (&d)[NC], int KB, float* pout, int cs,
                                        int icol) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) st.acc[c] += d[c];
@@ -479,16 +289,20 @@ __device__ __forceinline__ void mv_add(MvState<NC>& st, const float (&d)[NC], in
   }
 }
 
+// Dot products of one unit's 8 weights (this lane) with NC activation columns
+// (lane 16*jrow + icol: columns 4*icol.. and 64 + 4*icol.. of column block b).
 template <int NC>
-__device__ __forceinline__ void mv_dot(const u32x4 wv, const f32x4 (&h)[NC][2], float (&d)[NC]) {
+__device__ __forceinline__ void mv_unit(const u32x4 wv, const float* hl, int kp, int b, float (&d)[NC]) {
   float x[8];
   unpack8(wv, x);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    float a = x[0] * h[c][0].x;
-    a = fmaf(x[1], h[c][0].y, a); a = fmaf(x[2], h[c][0].z, a); a = fmaf(x[3], h[c][0].w, a);
-    a = fmaf(x[4], h[c][1].x, a); a = fmaf(x[5], h[c][1].y, a);
-    a = fmaf(x[6], h[c][1].z, a); a = fmaf(x[7], h[c][1].w, a);
+    const float* q = hl + (size_t)c * kp + b * kUnitCols;
+    const float4 h0 = ld_f4(q), h1 = ld_f4(q + 64);
+    float a = x[0] * h0.x;
+    a = fmaf(x[1], h0.y, a); a = fmaf(x[2], h0.z, a); a = fmaf(x[3], h0.w, a);
+    a = fmaf(x[4], h1.x, a); a = fmaf(x[5], h1.y, a);
+    a = fmaf(x[6], h1.z, a); a = fmaf(x[7], h1.w, a);
     d[c] = a;
   }
 }
@@ -497,18 +311,18 @@ __device__ __forceinline__ void mv_dot(const u32x4 wv, const f32x4 (&h)[NC][2], 
 // row jrow of a unit's row block over its 8 columns; a row block's sums are
 // reduced over the 16 lanes of the row and stored as this wave's partial sums.
 // Unit layout: lane 16*jrow + icol holds columns [4*icol, +4) and
-// [64 + 4*icol, +4) of its row.
+// [64 + 4*icol, +4) of its row. Items go two at a time (four units).
 template <int DEPTH, int NC>
 __device__ __forceinline__ bool stream_matvec(const Params& P, const Ctx& cx, int s, const Walker& w, Fetch& F,
-                                              Feed& f, Waits& wt, const float* hin, int kp, float* part) {
+                                              int& k, uint32_t ring, Waits& wt, const float* hin, int kp,
+                                              float* part) {
   const int lane = cx.lane;
   const int jrow = lane >> 4, icol = lane & 15;
   const int KB = w.KB;
-  const uint32_t hl = lds_addr(hin + icol * 4);
-  const uint32_t cstride = (uint32_t)kp * 4;
-  const uint32_t pout = lds_addr(part + (size_t)s * P.ncap * P.vrow_stride + jrow);
-  const uint32_t pcs = (uint32_t)P.vrow_stride * 4;
-  const uint32_t ring = lds_addr(f.ring) + lane * 16;
+  const float* hl = hin + icol * 4;
+  float* pout = part + (size_t)s * P.ncap * P.vrow_stride + jrow;
+  const int pcs = P.vrow_stride;
+  const uint8_t* rp = reinterpret_cast<const uint8_t*>(cx.ring) - lds_addr(cx.ring) + lane * 16;  // LDS address -> pointer
   MvState<NC> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) st.acc[c] = 0.f;
@@ -516,55 +330,52 @@ __device__ __forceinline__ bool stream_matvec(const Params& P, const Ctx& cx, in
   st.kb = w.u0 - st.rb * KB;
   st.pend = false;
   int t = 0;
-  if constexpr (NC <= 2) {
-    // two items (four units) at a time while both are copied and whole
-    while (t + 1 < w.n && 2 * t + 3 < w.nu && F.issued >= f.k + 2) {
-      feed_wait2<DEPTH>(F, f);
-      uint32_t h[4][NC];
-      int b = st.kb;
+  for (; t + 1 < w.n && 2 * t + 3 < w.nu; t += 2) {
+    if (!ensure_copied<DEPTH>(P, cx, s, F, k, 2, ring, wt)) return false;
+    wait_landed<DEPTH, 2>(F, k);
+    const uint8_t* i0 = rp + ring_slot<DEPTH>(ring, k);
+    const uint8_t* i1 = rp + ring_slot<DEPTH>(ring, k + 1);
+    const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
+    const u32x4 w2 = ld_u32x4(i1), w3 = ld_u32x4(i1 + kUnitBytes);
+    const int b0 = st.kb, b1 = next_cb(b0, KB), b2 = next_cb(b1, KB), b3 = next_cb(b2, KB);
+    float d[4][NC];
+    mv_unit<NC>(w0, hl, kp, b0, d[0]);
+    mv_unit<NC>(w1, hl, kp, b1, d[1]);
+    mv_unit<NC>(w2, hl, kp, b2, d[2]);
+    mv_unit<NC>(w3, hl, kp, b3, d[3]);
+    k += 2;
+    refill<DEPTH>(P, cx, s, F, k, ring);
+    if (st.kb + 4 < KB) {  // the row block goes on past these four units
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) h[u][c] = hl + c * cstride + b * (kUnitCols * 4);
-        b = b + 1 == KB ? 0 : b + 1;
-      }
-      const int s1 = f.slot + 1 == DEPTH ? 0 : f.slot + 1;
-      Item2Regs<NC> r;
-      lds_item2(ring + f.slot * kItemBytes, ring + s1 * kItemBytes, h, r);
-      feed_done<DEPTH>(P, cx, s, F, f);
-      feed_done<DEPTH>(P, cx, s, F, f);
-      float d[4][NC];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) mv_dot<NC>(r.w[u], r.h[u], d[u]);
+      for (int c = 0; c < NC; ++c) st.acc[c] += (d[0][c] + d[1][c]) + (d[2][c] + d[3][c]);
+      st.kb += 4;
+      st.pend = true;
+    } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u) mv_add<NC>(st, d[u], KB, pout, pcs, icol);
-      t += 2;
     }
   }
   for (; t < w.n; ++t) {
-    if (!feed_item<DEPTH>(P, cx, s, F, f, wt)) return false;
-    const int kb1 = st.kb + 1 == KB ? 0 : st.kb + 1;
-    uint32_t ha[NC], hb[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      ha[c] = hl + c * cstride + st.kb * (kUnitCols * 4);
-      hb[c] = hl + c * cstride + kb1 * (kUnitCols * 4);
-    }
-    ItemRegs<NC> r;
-    lds_item(ring + f.slot * kItemBytes, ha, hb, r);
-    feed_done<DEPTH>(P, cx, s, F, f);
-    float d0[NC];
-    mv_dot<NC>(r.w0, r.a, d0);
+    if (!ensure_copied<DEPTH>(P, cx, s, F, k, 1, ring, wt)) return false;
+    wait_landed<DEPTH, 1>(F, k);
+    const uint8_t* i0 = rp + ring_slot<DEPTH>(ring, k);
+    const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
+    float d0[NC], d1[NC];
+    mv_unit<NC>(w0, hl, kp, st.kb, d0);
+    mv_unit<NC>(w1, hl, kp, next_cb(st.kb, KB), d1);
+    k += 1;
+    wait_lgkm();  // the item's slot has been read
+    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
     mv_add<NC>(st, d0, KB, pout, pcs, icol);
-    if (2 * t + 1 < w.nu) {
-      float d1[NC];
-      mv_dot<NC>(r.w1, r.b, d1);
-      mv_add<NC>(st, d1, KB, pout, pcs, icol);
-    }
+    if (2 * t + 1 < w.nu) mv_add<NC>(st, d1, KB, pout, pcs, icol);
   }
   if (st.pend) mv_flush<NC>(st, pout, pcs, icol, st.rb);
   return true;
 }
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
 
 // One level of the merge of online-softmax states across lanes paired by xor
 // O; both lanes of a pair merge the same ordered pair of states.
@@ -598,31 +409,37 @@ __device__ __forceinline__ void att_merge_step(int G, float (&mv)[kMaxG], float 
 // {acc[D], m, l} per head.
 template <int DEPTH>
 __device__ __forceinline__ bool stream_att(const Params& P, const Ctx& cx, int s, const Walker& w, Fetch& F,
-                                           Feed& f, Waits& wt, const float* hin, float* part) {
+                                           int& k, uint32_t ring, Waits& wt, const float* hin, float* part) {
   const int lane = cx.lane;
   const int D = P.D, lpp = D / 8, ppu = 64 / lpp;
   const int pg = lane / lpp, de = (lane % lpp) * 8;
   const int G = P.G;
   const float scale = P.attn_scale;
-  const uint32_t ring = lds_addr(f.ring) + lane * 16;
+  const uint8_t* rp = reinterpret_cast<const uint8_t*>(cx.ring) - lds_addr(cx.ring) + lane * 16;
   float qv[kMaxG][8], av[kMaxG][8], mv[kMaxG], lv[kMaxG];
   const float* q = hin + att_raw_floats(P);
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     mv[h] = -INFINITY;
     lv[h] = 0.f;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = x;
-    if (h < G) lds_read_2x128(lds_addr(q + h * D + de), lds_addr(q + h * D + de + 4), x, y);
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+    if (h < G) {
+      x = ld_f4(q + h * D + de);
+      y = ld_f4(q + h * D + de + 4);
+    }
     qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
     qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
 #pragma unroll
     for (int e = 0; e < 8; ++e) av[h][e] = 0.f;
   }
   for (int t = 0; t < w.n; ++t) {
-    if (!feed_item<DEPTH>(P, cx, s, F, f, wt)) return false;
-    u32x4 wk, wv;
-    lds_item_kv(ring + f.slot * kItemBytes, wk, wv);
-    feed_done<DEPTH>(P, cx, s, F, f);
+    if (!ensure_copied<DEPTH>(P, cx, s, F, k, 1, ring, wt)) return false;
+    wait_landed<DEPTH, 1>(F, k);
+    const uint8_t* it = rp + ring_slot<DEPTH>(ring, k);
+    const u32x4 wk = ld_u32x4(it), wv = ld_u32x4(it + kUnitBytes);
+    k += 1;
+    wait_lgkm();  // the item's slot has been read
+    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
     const bool valid = w.lo + (w.u0 + t) * ppu + pg < w.end;
     float kf[8], vf[8];
     unpack8(wk, kf);
@@ -657,13 +474,11 @@ __device__ __forceinline__ bool stream_att(const Params& P, const Ctx& cx, int s
     for (int h = 0; h < kMaxG; ++h) {
       if (h < G) {
         float* dst = part + s * stride + h * (D + 2);
-        const f32x4 lo = {av[h][0], av[h][1], av[h][2], av[h][3]};
-        const f32x4 hi = {av[h][4], av[h][5], av[h][6], av[h][7]};
-        lds_write_b128(lds_addr(dst + de), lo);
-        lds_write_b128(lds_addr(dst + de + 4), hi);
+        *reinterpret_cast<float4*>(dst + de) = make_float4(av[h][0], av[h][1], av[h][2], av[h][3]);
+        *reinterpret_cast<float4*>(dst + de + 4) = make_float4(av[h][4], av[h][5], av[h][6], av[h][7]);
         if (lane == 0) {
-          lds_write_b32(lds_addr(dst + D), mv[h]);
-          lds_write_b32(lds_addr(dst + D + 1), lv[h]);
+          dst[D] = mv[h];
+          dst[D + 1] = lv[h];
         }
       }
     }
@@ -678,26 +493,27 @@ __device__ __forceinline__ bool stream_att(const Params& P, const Ctx& cx, int s
 template <int DEPTH>
 __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s) {
   Waits wt;  // KV step not open, -, task staged, items
-  waits_init(P, wt);
-  Feed f;
-  f.k = 0;
-  f.slot = 0;
-  f.ring = cx.ring + (size_t)s * DEPTH * kItemBytes;
+  waits_init(P, cx, wt);
+  const uint32_t ring = lds_addr(cx.ring) + (uint32_t)s * DEPTH * kItemBytes;
   Fetch F;
   walker_init(F.w, cx);
   F.issued = 0;
-  F.slot = 0;
   fetch_next_task(P, cx, s, F);
-  fetch_upto<DEPTH>(P, cx, s, F, DEPTH, f.ring);
+  fetch_upto<DEPTH>(P, cx, s, F, DEPTH, ring);
+  int k = 0;  // items consumed
   Walker w;
   walker_init(w, cx);
   const int ncols = P.batch;
   for (;;) {
-    walker_next(P, w, cx, s);
+    {
+      const uint64_t s0 = waits_now(wt);
+      walker_next(P, w, cx, s);
+      waits_add(wt, 7, s0);
+    }
     if (w.done) break;
     {
       const uint64_t s0 = waits_now(wt);
-      if (!spin_raw(P, cx, C_STAGED, w.i + 1)) return;
+      if (!spin_ctl(P, cx, C_STAGED, w.i + 1)) return;
       waits_add(wt, 2, s0);
     }
     const float* hin = slot_ptr(cx, w.slot) + kHdr;
@@ -705,20 +521,23 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
     const uint64_t s1 = waits_now(wt);
     bool ok;
     if (w.type == T_ATT) {
-      ok = stream_att<DEPTH>(P, cx, s, w, F, f, wt, hin, part);
+      ok = stream_att<DEPTH>(P, cx, s, w, F, k, ring, wt, hin, part);
     } else {
       const int kp = slot_kp(P, w.slot);
       switch (ncols) {
-        case 1: ok = stream_matvec<DEPTH, 1>(P, cx, s, w, F, f, wt, hin, kp, part); break;
-        case 2: ok = stream_matvec<DEPTH, 2>(P, cx, s, w, F, f, wt, hin, kp, part); break;
-        case 3: ok = stream_matvec<DEPTH, 3>(P, cx, s, w, F, f, wt, hin, kp, part); break;
-        default: ok = stream_matvec<DEPTH, 4>(P, cx, s, w, F, f, wt, hin, kp, part); break;
+        case 1: ok = stream_matvec<DEPTH, 1>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
+        case 2: ok = stream_matvec<DEPTH, 2>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
+        case 3: ok = stream_matvec<DEPTH, 3>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
+        default: ok = stream_matvec<DEPTH, 4>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
       }
     }
     if (!ok) return;
     if (w.type == T_LM) waits_add(wt, 5, s1);
-    wt.c[3] += w.n;
-    if (cx.lane == 0) lds_add_raw(lds_addr(&cx.ctl[C_DONE + w.slot]), 1);
+    else waits_add(wt, 8, s1);
+    waits_count(wt, 3, w.n);
+    const uint64_t s2 = waits_now(wt);
+    lds_add(&cx.ctl[C_DONE + w.slot], 1);
+    waits_add(wt, 9, s2);
   }
   wait_all();
   waits_put(P, cx, wt);

@@ -162,20 +162,18 @@ int mk_debug_drop_signal(mk_model *m, int32_t task_id);
  * NULL disables. MK_EINVAL if bytes is too small for one step. */
 int mk_set_profile_buffer(mk_model *m, void *d_buf, size_t bytes);
 
-/* Optional wait accounting of the megakernel's waves. d_buf: zeroed device
- * buffer of at least num_cus * 8 * 8 uint64 words; later megakernel calls add,
- * for workgroup c and wave v, into words [(c * 8 + v) * 8 + j]:
- *   wave 0 (stager):   j0 waiting for a free staging slot, j1 waiting for the
- *                      dependent event, j2 staging, j3 tasks;
- *   wave 1 (retirer):  j0 waiting for staging, j1 waiting for the compute
- *                      waves, j2 epilogue, j3 tasks;
- *   waves 2-4 (loaders): j0 ring full, j1 copies in flight, j2 waiting for the
- *                      previous step's first dependency, j3 items;
- *   waves 5-7 (compute): j0 waiting for loaded items, j1 waiting for staging,
- *                      j3 items;
- *   j4: the wave's lifetime; loaders: j5 copies in flight and j6 ring full
- *   during LM-head tasks; compute waves: j5 waiting for loaded items during LM-head tasks,
- *   j6 time inside LM-head tasks. Times are 100 MHz ticks. NULL disables. */
+/* Optional wait accounting of the megakernel's waves (diagnostics). d_buf:
+ * zeroed device buffer of at least num_cus * 6 * 16 uint64 words; later
+ * megakernel calls add, for workgroup c and wave v, into words
+ * [(c * 6 + v) * 16 + j] (times in 100 MHz ticks, j4: the wave's lifetime):
+ *   wave 0 (stager):  j0 waiting for a free staging slot, j1 waiting for the
+ *                     dependent event, j2 staging, j3 tasks;
+ *   wave 1 (retirer): j0 waiting for staging, j1 waiting for the stream
+ *                     waves, j2 epilogue, j3 tasks;
+ *   waves 2-5 (stream): j0 waiting for a KV step to open, j2 waiting for
+ *                     staging, j3 items, j5 inside LM-head tasks, j7 finding
+ *                     the next task, j8 inside other tasks, j9 signalling.
+ * NULL disables. */
 int mk_set_wait_counters(mk_model *m, void *d_buf, size_t bytes);
 
 /* Device bytes the model reads per step for its weights (packed copy, padding
