@@ -4,9 +4,11 @@ persistent decode megakernel on one MI355X.
 Workload (default): the Llama-3.2-1B-shaped decoder at batch 1, seeded random
 bf16 weights, a 39-token prompt consumed untimed, then K greedy decode steps
 inside ONE persistent launch (mk_generate), timed with HIP events on the
-launch stream. Also timed, for context: the same steps with one launch per
-operator (the baseline built from the same task bodies), and the CPU oracle on
-a bounded sample.
+launch stream. The prompt and the W warm-up steps run on the per-operator
+path, so the timed launch is the run's only mk_persistent dispatch (a
+profiler's average for that kernel is the timed launch). Also timed, for
+context: the same steps with one launch per operator (the baseline built from
+the same task bodies), and the CPU oracle on a bounded sample.
 
 Prints one JSON line (rank 0). `--gpus N` with N > 1 exits: this build runs on
 one GPU.
@@ -40,6 +42,29 @@ def algorithmic_bytes(shape, positions) -> int:
     w = L * per_layer + V * H * 2 + H * 2 + len(positions) * H * 2
     kv_per_pos = L * Hkv * D * 2 * 2
     return w + sum((p + 1) * kv_per_pos for p in positions)
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mk_persistent_llama3.2-1b-shape_b1_hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc", f)
+                  for f in ("kernels.hip", "pipeline.h", "device.h")]
+
+
+def recorded_traffic(workload_name: str, steps: int, batch: int):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy of known size), if recorded for this
+    workload and step count with the kernel sources as they are now; else None."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    if (rec.get("kernel_source_sha256") != h.hexdigest() or rec.get("workload") != workload_name
+            or rec.get("steps") != steps or rec.get("batch") != batch):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, weights, seconds: float = 15.0):
@@ -79,6 +104,9 @@ def main():
     ap.add_argument("--oplaunch-steps", type=int, default=32, help="steps timed for the per-operator baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (a plain copy of known size, to scale "
+                         "hardware byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -86,6 +114,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": n}), flush=True)
+        return
     import workload
     from decode_persistent_megakernel_amd import MK_MODE_OPLAUNCH
     from decode_persistent_megakernel_amd.session import Session
@@ -105,15 +142,17 @@ def main():
     if P - 1 + max(K, W) > wl.max_seq:
         raise SystemExit("steps exceed max_seq")
     for p in range(P - 1):
-        ss.decode_step([int(prompt[p])], [p], logits=False)
+        ss.decode_step([int(prompt[p])], [p], mode=MK_MODE_OPLAUNCH, logits=False)
     torch.cuda.synchronize()
     ss.check()
     log("prompt prefilled")
 
     stream = torch.cuda.current_stream()
-    out = torch.zeros((max(K, W, 1), 1), dtype=torch.int32, device="cuda")
-    if W > 0:
-        ss.generate([int(prompt[-1])], [P - 1], W, out=out[:W])
+    out = torch.zeros((max(K, 1), 1), dtype=torch.int32, device="cuda")
+    tok = int(prompt[-1])
+    for k in range(W):  # warm-up steps (positions P-1.. are written again by the timed launch)
+        nxt, _ = ss.decode_step([tok], [P - 1 + k], mode=MK_MODE_OPLAUNCH, logits=False)
+        tok = int(nxt[0])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -156,15 +195,16 @@ def main():
         log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads")
 
     rec = {
-        "metric": "decode us/token at batch 1 + achieved HBM GB/s as % of roofline",
-        "value": round(us_tok, 3), "unit": "us/token", "n_gpus": 1, "steps": K, "warmup": W,
+        "metric": "decode \u00b5s/token at batch 1 + achieved HBM GB/s as % of roofline",
+        "value": round(us_tok, 3), "unit": "\u00b5s/token", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms / K, 6), "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16 weights, fp32 arithmetic", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "global_batch": wl.batch, "seq_len": P - 1 + K,
                    "prompt": P, "decode_steps": K, "parallelism": "none (1 GPU)"},
         "achieved_gbs": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic(wl.name, K, wl.batch),
                      "kernel": "mk_persistent", "launch_ms": round(ms, 4),
                      "bytes_per_launch": bytes_launch},
         "oplaunch_baseline_us_per_token": round(us_b, 3),
