@@ -133,9 +133,11 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   HIP_TRY(hipGetDeviceProperties(&prop, m->device), "hipGetDeviceProperties");
 
   // --- task descriptors and packed-weight offsets ---------------------------
-  const int kb_h = static_cast<int>(cdiv(d.hidden, kUnitCols));
-  const int kb_qd = static_cast<int>(cdiv(int64_t(d.n_q_heads) * d.head_dim, kUnitCols));
-  const int kb_f = static_cast<int>(cdiv(d.ffn, kUnitCols));
+  // column blocks per row block, rounded up to even (zero weights pad K): a
+  // streamed item is two units of one row block
+  const int kb_h = static_cast<int>(cdiv(d.hidden, 2 * kUnitCols) * 2);
+  const int kb_qd = static_cast<int>(cdiv(int64_t(d.n_q_heads) * d.head_dim, 2 * kUnitCols) * 2);
+  const int kb_f = static_cast<int>(cdiv(d.ffn, 2 * kUnitCols) * 2);
   std::vector<DevTask> dt(g.tasks.size());
   std::vector<PackJob> jobs;
   uint64_t off = 0;
@@ -189,6 +191,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
       r.n_units = x.n_units;
       r.kq = uint32_t(x.kb) | uint32_t(qp) << 16;
       r.w_off = x.w_off;
+      r.id = q[qp];
       srec.push_back(r);
     }
     for (size_t j = first; j < srec.size(); ++j) srec[j].flip = nsmall & 1;
@@ -203,7 +206,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   if (G > kMaxG) return fail(MK_EUNSUPPORTED, "mk_load_weights: more than 4 query heads per kv head");
   if (64 % (D / 8) != 0) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim/8 must divide 64");
   if (d.hidden > 4096) return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden above 4096");
-  if (std::max({kb_h, kb_qd, kb_f}) > 255) return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32640");
+  if (std::max({kb_h, kb_qd, kb_f}) > 254) return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32512");
   if (int64_t(g.opts.attn_chunks) * (int64_t(d.max_seq) + 1) >= (int64_t(1) << 32))
     return fail(MK_EUNSUPPORTED, "mk_load_weights: attn_chunks * (max_seq + 1) must stay below 2^32");
   if (d.hidden % 4 || (d.n_q_heads * d.head_dim) % 4 || d.ffn % 4)
@@ -245,7 +248,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   m->lds_bytes = static_cast<int>(lds);
   HIP_TRY(set_lds_limit(m->lds_bytes), "hipFuncSetAttribute(max dynamic LDS)");
   int per_cu = 0;
-  HIP_TRY(persistent_occupancy(m->lds_bytes, &per_cu), "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  HIP_TRY(persistent_occupancy(m->lds_bytes, static_cast<int>(ring), &per_cu), "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   if (int64_t(per_cu) * prop.multiProcessorCount < g.opts.num_cus)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: num_cus=" + std::to_string(g.opts.num_cus) +
                                      " workgroups cannot be co-resident (" + std::to_string(prop.multiProcessorCount) +
@@ -424,7 +427,7 @@ static int run_megakernel(mk_model* m, const int32_t* tok, const int32_t* pos, i
   P.use_events = 1;
   P.timeout_ticks = m->timeout_ticks;
   P.drop_task = m->drop_task;
-  P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * 32) ? m->profile : nullptr;
+  P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * mk::kProfWords * 8) ? m->profile : nullptr;
   P.waits = m->waits;
   HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
   m->epoch += static_cast<uint32_t>(n_steps);
@@ -493,7 +496,7 @@ int mk_debug_drop_signal(mk_model* m, int32_t task_id) {
 
 int mk_set_profile_buffer(mk_model* m, void* d_buf, size_t bytes) {
   if (!m) return fail(MK_EINVAL, "mk_set_profile_buffer: NULL model");
-  if (d_buf && bytes < m->g.tasks.size() * 32) return fail(MK_EINVAL, "mk_set_profile_buffer: buffer too small");
+  if (d_buf && bytes < m->g.tasks.size() * mk::kProfWords * 8) return fail(MK_EINVAL, "mk_set_profile_buffer: buffer too small");
   m->profile = static_cast<uint64_t*>(d_buf);
   m->profile_bytes = d_buf ? bytes : 0;
   return MK_OK;

@@ -34,6 +34,7 @@ constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte l
 constexpr int kCtlBytes = 1024;             // control words + ring metadata (see kernels)
 constexpr int kWaves = kThreads / 64;
 constexpr int kWaitWords = 16;              // per-wave wait counters (mk_set_wait_counters)
+constexpr int kProfWords = 12;              // uint64 words per task in the profile buffer
 
 // status word bits (device)
 constexpr int32_t kStatusBadToken = 1;
@@ -61,7 +62,7 @@ struct StreamRec {
   uint32_t kq;       // column blocks | queue position << 16
   int64_t w_off;     // packed weight offset (matvec)
   int32_t flip;      // 1: the small slots swap from one step to the next (odd count per step)
-  int32_t pad;
+  int32_t id;        // global task id
 };
 static_assert(sizeof(StreamRec) == 32, "stream records are two 16-byte words");
 
@@ -117,7 +118,7 @@ struct Params {
   uint32_t epoch0;
   int32_t use_events;         // 0: single-task workgroups ordered by the stream
   uint64_t timeout_ticks;     // 100 MHz constant clock
-  uint64_t* profile;          // null or [n_steps][n_tasks][4]
+  uint64_t* profile;          // null or [n_steps][n_tasks][kProfWords]
   int32_t drop_task;          // fault injection: this task never signals (-1: off)
   uint64_t* waits;            // null or [grid][kWaves][kWaitWords] wait-time counters
 };

@@ -47,8 +47,10 @@ constexpr int kHdr = 32;           // floats of header at the start of a slot
 
 // LDS control words (ints)
 enum { C_STAGED = 0, C_RETIRED = 1, C_DONE = 2 /* 3 slots */, C_STEPOK = 5, C_ABORT = 6, kCtlWords = 64 };
-// then the waves' wait counters (kWaitWords each)
-static_assert((kCtlWords + kWaves * kWaitWords) * 4 <= kCtlBytes, "control area");
+// then the waves' wait counters (kWaitWords each), then the stream waves'
+// per-task timestamps for the profile (3 slots x kStreams x {start, first item, end})
+constexpr int kProfCtl = kCtlWords + kWaves * kWaitWords;
+static_assert((kProfCtl + 3 * kStreams * 3) * 4 <= kCtlBytes, "control area");
 // slot header fields (as int)
 enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11 };
 
@@ -200,6 +202,22 @@ __device__ __forceinline__ void lds_add(int* p, int v) {
   if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   wait_lgkm();
 }
+// The same without a lane-dependent branch, for loops whose control must stay
+// uniform: the add runs with only lane 0 enabled (exec set and restored inside
+// the block), after this wave's earlier LDS accesses, and completes in it.
+__device__ __forceinline__ void lds_add_lane0(int* p, int v) {
+  uint64_t saved;
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "ds_add_u32 %1, %2\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p), "v"(v)
+      : "memory");
+}
 
 // LDS word access for the loader waves. Their LDS DMA is tracked by vmcnt and
 // the compiler would otherwise drain it before every LDS access; these blocks
@@ -299,6 +317,8 @@ __device__ __forceinline__ bool spin_ctl(const Params& P, const Ctx& cx, int w, 
 // Optional per-wave wait accounting (diagnostics): counters of 100 MHz ticks
 // (or counts) kept in this wave's words of the LDS control area, so that they
 // hold no registers; added into P.waits when the wave finishes.
+__device__ __forceinline__ uint32_t rfl32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 struct Waits {
   uint32_t* c;  // kWaitWords words; word 4 holds the start time, then the lifetime
   bool on;
@@ -309,11 +329,16 @@ __device__ __forceinline__ uint32_t* waits_area(const Ctx& cx) {
 __device__ __forceinline__ void waits_init(const Params& P, const Ctx& cx, Waits& w) {
   w.on = P.waits != nullptr;
   w.c = waits_area(cx);
-  if (w.on && cx.lane == 0) w.c[4] = (uint32_t)wall_clock64();
+  if (w.on) w.c[4] = rfl32((uint32_t)wall_clock64());
 }
 __device__ __forceinline__ uint64_t waits_now(const Waits& w) { return w.on ? wall_clock64() : 0; }
+// every lane reads and stores the same value (no lane-dependent branch)
 __device__ __forceinline__ void waits_count(Waits& w, int j, uint32_t n) {
-  if (w.on && (threadIdx.x & 63) == 0) w.c[j] += n;
+  if (w.on) {
+    const uint32_t v = rfl32(w.c[j]) + n;
+    wait_lgkm();
+    w.c[j] = v;
+  }
 }
 __device__ __forceinline__ void waits_add(Waits& w, int j, uint64_t since) {
   if (w.on) waits_count(w, j, (uint32_t)(wall_clock64() - since));
@@ -324,6 +349,10 @@ __device__ __forceinline__ void waits_put(const Params& P, const Ctx& cx, const 
   const uint32_t life = (uint32_t)wall_clock64() - w.c[4];
   for (int j = 0; j < kWaitWords; ++j)
     __hip_atomic_fetch_add(&o[j], (uint64_t)(j == 4 ? life : w.c[j]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t* prof_words(const Ctx& cx, int slot, int s) {
+  return reinterpret_cast<uint32_t*>(cx.ctl) + kProfCtl + (slot * kStreams + s) * 3;
 }
 
 __device__ __forceinline__ bool has_stream(int type) {
@@ -569,6 +598,7 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
         if (!wait_event(P, cx, T.dep, thr * mult)) return;
       }
       waits_add(wt, 1, s0);
+      if (P.profile && cx.lane == 0) P.profile[((size_t)step * P.n_tasks + id) * kProfWords] = wall_clock64();
       if (qi == cx.q0) lds_st(&cx.ctl[C_STEPOK], step + 1);
       s0 = waits_now(wt);
       stage_task(P, cx, T, slot, step, pre);
@@ -811,11 +841,16 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
           __hip_atomic_fetch_add(&P.counters[(size_t)T.trig * kEventWords + (cx.cu & (kStripes - 1)) * 32], 1u,
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (P.profile) {
-          uint64_t* rec = P.profile + ((size_t)step * P.n_tasks + id) * 4;
-          rec[0] = (uint64_t)(uint32_t)id | ((uint64_t)(uint32_t)cx.cu << 32);
+          uint64_t* rec = P.profile + ((size_t)step * P.n_tasks + id) * kProfWords;
           rec[1] = t_staged;
           rec[2] = t_computed;
           rec[3] = wall_clock64();
+          if (has_stream(T.type))
+            for (int w = 0; w < kStreams; ++w) {
+              const uint32_t* pw = prof_words(cx, slot, w);
+              rec[4 + w] = (uint64_t)pw[0] << 32 | pw[2];
+              rec[8 + w] = pw[1];
+            }
         }
         __hip_atomic_store(&cx.ctl[C_DONE + slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
@@ -831,6 +866,7 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
 // kernels
 // ---------------------------------------------------------------------------
 
+template <int NC, int DEPTH>
 __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   extern __shared__ __align__(16) char smem[];
   Ctx cx;
@@ -871,7 +907,7 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
       r.kq = (uint32_t)T.kb;
       r.w_off = T.w_off;
       r.flip = 0;
-      r.pad = 0;
+      r.id = single;
       cx.recs[0] = r;
     }
   }
@@ -880,15 +916,38 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) run_stager(P, cx);
   else if (wave == 1) run_retirer(P, cx);
-  else if (P.ring_slots >= 8) run_stream<8>(P, cx, wave - kCtlWaves);
-  else run_stream<4>(P, cx, wave - kCtlWaves);
+  else run_stream<DEPTH, NC>(P, cx, wave - kCtlWaves);
 }
 
-extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent(Params P) { run(P, blockIdx.x, -1); }
+// One kernel per (staged columns, ring depth): each holds the code of its own
+// variant only, which keeps the instruction working set of a workgroup small.
+#define MK_KERNELS(NC, DEPTH)                                                                           \
+  extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent_b##NC##_d##DEPTH(Params P) {     \
+    run<NC, DEPTH>(P, blockIdx.x, -1);                                                                 \
+  }                                                                                                    \
+  extern "C" __global__ void __launch_bounds__(kThreads) mk_oplaunch_b##NC##_d##DEPTH(Params P, int first) { \
+    run<NC, DEPTH>(P, blockIdx.x, first + blockIdx.x);                                                 \
+  }
+MK_KERNELS(1, 8)
+MK_KERNELS(2, 8)
+MK_KERNELS(3, 8)
+MK_KERNELS(4, 8)
+MK_KERNELS(1, 4)
+MK_KERNELS(2, 4)
+MK_KERNELS(3, 4)
+MK_KERNELS(4, 4)
+#undef MK_KERNELS
 
-extern "C" __global__ void __launch_bounds__(kThreads) mk_oplaunch(Params P, int first) {
-  run(P, blockIdx.x, first + blockIdx.x);
-}
+typedef void (*PersistentFn)(Params);
+typedef void (*OpFn)(Params, int);
+// [ring depth 8, 4][columns - 1]
+__device__ __host__ constexpr int depth_index(int depth) { return depth >= 8 ? 0 : 1; }
+static const PersistentFn kPersistent[2][kMaxCols] = {
+    {mk_persistent_b1_d8, mk_persistent_b2_d8, mk_persistent_b3_d8, mk_persistent_b4_d8},
+    {mk_persistent_b1_d4, mk_persistent_b2_d4, mk_persistent_b3_d4, mk_persistent_b4_d4}};
+static const OpFn kOplaunch[2][kMaxCols] = {
+    {mk_oplaunch_b1_d8, mk_oplaunch_b2_d8, mk_oplaunch_b3_d8, mk_oplaunch_b4_d8},
+    {mk_oplaunch_b1_d4, mk_oplaunch_b2_d4, mk_oplaunch_b3_d4, mk_oplaunch_b4_d4}};
 
 // ---------------------------------------------------------------------------
 // weight packing
@@ -946,27 +1005,43 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack(const PackJob* jobs, c
 // ---------------------------------------------------------------------------
 
 hipError_t set_lds_limit(int bytes) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_oplaunch),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  for (int d = 0; d < 2; ++d)
+    for (int c = 0; c < kMaxCols; ++c) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistent[d][c]),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kOplaunch[d][c]),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
 }
 
-hipError_t persistent_occupancy(int lds, int* blocks_per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, reinterpret_cast<const void*>(&mk_persistent),
-                                                      kThreads, lds);
+hipError_t persistent_occupancy(int lds, int depth, int* blocks_per_cu) {
+  int worst = 1 << 30;
+  for (int c = 0; c < kMaxCols; ++c) {
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, reinterpret_cast<const void*>(kPersistent[depth_index(depth)][c]), kThreads, lds);
+    if (e != hipSuccess) return e;
+    worst = n < worst ? n : worst;
+  }
+  *blocks_per_cu = worst;
+  return hipSuccess;
 }
 
+// The variant for the call: staged columns = the call's batch, the model's ring depth.
 hipError_t launch_persistent(const Params& P, int grid, int lds, hipStream_t s) {
+  if (P.batch < 1 || P.batch > kMaxCols) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mk_persistent), dim3(grid), dim3(kThreads), args,
-                                    lds, s);
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kPersistent[depth_index(P.ring_slots)][P.batch - 1]),
+                                    dim3(grid), dim3(kThreads), args, lds, s);
 }
 
 hipError_t launch_op(const Params& P, int first, int count, int lds, hipStream_t s) {
-  hipLaunchKernelGGL(mk_oplaunch, dim3(count), dim3(kThreads), lds, s, P, first);
+  if (P.batch < 1 || P.batch > kMaxCols) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kOplaunch[depth_index(P.ring_slots)][P.batch - 1], dim3(count), dim3(kThreads), lds, s, P, first);
   return hipGetLastError();
 }
 

@@ -3,139 +3,50 @@
 //
 // Every streamed task (a matvec over packed weight units, or attention over a
 // chunk of the KV cache) is cut into kStreams contiguous pieces, one per
-// stream wave: a matvec task's units (packed order: row block major, column
-// block minor) in whole items of two units, an attention task's position
-// blocks, one item each. An item is 2 KiB: two consecutive weight units, or
-// the K block and the V block of one group of positions.
+// stream wave. A piece is a run of 2 KiB items: two weight units of one row
+// block (column blocks 2j and 2j+1; the packing makes the number of column
+// blocks even), or the K block and the V block of one group of positions.
 //
 // A stream wave feeds itself: it copies its items from HBM straight into a
 // private LDS ring of DEPTH slots (LDS DMA), DEPTH items ahead of the one it
 // computes, running ahead across task boundaries so weights keep arriving
 // while the workgroup waits on an event. Copies complete in issue order, so
 // "item k has landed" is a wait for the vector-memory counter to drop to twice
-// the number of younger items. The copies are issued as inline assembly: the
-// compiler then leaves the wave's own LDS reads alone (it would otherwise wait
-// for every copy in flight before each of them, not knowing which LDS bytes
-// a copy writes) and schedules them freely; the explicit counter waits order
-// every read after the copy that fills its slot.
-
+// the number of younger items; the wave issues no other vector-memory
+// operation while it streams. The copies are inline assembly: the compiler
+// then leaves the wave's own LDS reads alone (it would otherwise wait for
+// every copy in flight before each of them, not knowing which LDS bytes a copy
+// writes).
+//
+// The wave is one loop over items with two cursors over the same task list:
+// the copy cursor (ahead) and the compute cursor. Each cursor's task change is
+// a single, rarely taken path and the per-item work is straight-line code, so
+// the role stays small in the instruction cache and light on registers.
+//
 // Attention items of a step read KV entries appended in earlier steps, so
 // they are copied only after the stager has passed the step's first
 // dependency (C_STEPOK); weight items never wait for anything but a free slot.
 
 // ---------------------------------------------------------------------------
-// copies for the stream waves
+// copies
 // ---------------------------------------------------------------------------
 
 // 1 KiB per wave: lane l copies 16 bytes from its own address src into LDS
 // byte address lds + 16*l (lds is wave-uniform; it goes in M0, which this
 // wave's code uses for nothing else). nt: streamed once; sc1: device-coherent.
 __device__ __forceinline__ void copy_nt(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 __device__ __forceinline__ void copy_sc1(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" : : "v"(src), "s"(lds)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" : : "v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 
 __device__ __forceinline__ u32x4 ld_u32x4(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-
-// ---------------------------------------------------------------------------
-// task walking
-// ---------------------------------------------------------------------------
-
-// Walks the stream tasks (those with weight or KV units) of this workgroup's
-// queue, across steps, for stream wave s: the queue's stream records in LDS.
-struct Walker {
-  int step, r, i;    // r: record; i: global task counter of the task (all tasks)
-  int slot, type, layer, b, g;
-  int nu;            // matvec: units of wave s; attention: position blocks of wave s
-  int n;             // items of wave s in the task (may be 0)
-  int u0;            // matvec: first unit of wave s; attention: first position block
-  int lo, end;       // attention: positions [lo, end) come from the cache
-  int KB;            // matvec: column blocks
-  int64_t woff;      // matvec: packed weight offset of the task
-  bool done;
-};
-
-__device__ __forceinline__ void walker_init(Walker& w, const Ctx& cx) {
-  w.step = 0;
-  w.r = -1;
-  w.i = 0;
-  w.slot = 0;
-  w.type = -1;
-  w.layer = w.b = w.g = 0;
-  w.nu = w.n = w.u0 = 0;
-  w.lo = w.end = 0;
-  w.KB = 1;
-  w.woff = 0;
-  w.done = false;
-}
-
-// [a0, a1): piece s of n things cut into kStreams nearly equal contiguous pieces
-__device__ __forceinline__ void piece(int n, int s, int& a0, int& a1) {
-  a0 = (int)((uint32_t)n * (uint32_t)s / kStreams);
-  a1 = (int)((uint32_t)n * (uint32_t)(s + 1) / kStreams);
-}
-
-__device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ void walker_next(const Params& P, Walker& w, const Ctx& cx, int s) {
-  if (++w.r >= cx.nrec) {
-    w.r = 0;
-    ++w.step;
-  }
-  if (w.step >= P.n_steps || cx.nrec == 0) {
-    w.done = true;
-    return;
-  }
-  const StreamRec R = cx.recs[w.r];
-  const uint32_t tsbg = rfl(R.tsbg), lc = rfl(R.lc), kq = rfl(R.kq);
-  w.type = tsbg & 15;
-  w.slot = (tsbg >> 4) & 3;
-  if (w.slot < 2) w.slot ^= (int)rfl((uint32_t)R.flip) & w.step;
-  w.b = (tsbg >> 6) & 1023;
-  w.g = tsbg >> 16;
-  w.layer = lc & 0xffff;
-  const int chunk = lc >> 16;
-  w.i = w.step * (cx.q1 - cx.q0) + (int)(kq >> 16);
-  w.nu = 0;
-  w.u0 = 0;
-  if (w.type == T_ATT) {
-    w.lo = w.end = 0;
-    if (w.b < P.batch) {
-      const int pos = ld_uniform(P.pos_in, w.b) + w.step;
-      if (pos >= 0 && pos < P.S) {
-        const int64_t len = (int64_t)pos + 1;
-        w.lo = chunk_bound(chunk, len, P.Nc);
-        w.end = min(chunk_bound(chunk + 1, len, P.Nc), pos);
-        const int ppu = 512 / P.D;  // positions per unit
-        const int npu = w.end > w.lo ? (w.end - w.lo + ppu - 1) / ppu : 0;
-        int j1;
-        piece(npu, s, w.u0, j1);
-        w.nu = j1 - w.u0;
-      }
-    }
-    w.n = w.nu;
-  } else {
-    const int U = (int)rfl((uint32_t)R.n_units);
-    int i0, i1;
-    piece((U + 1) / 2, s, i0, i1);
-    w.u0 = 2 * i0;
-    w.nu = max(min(2 * i1, U) - w.u0, 0);
-    w.n = i1 - i0;
-    w.KB = kq & 0xffff;
-    w.woff = (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
-  }
-}
-
-// ---------------------------------------------------------------------------
-// the copy side of a stream wave
-// ---------------------------------------------------------------------------
-
-constexpr int kItemBytes = 2 * kUnitBytes;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -144,400 +55,463 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
-
-
-struct Fetch {
-  Walker w;            // the task of the next item to copy
-  int t;               // its item within that task
-  int issued;          // items copied so far
-  bool kv;             // the task is attention (KV blocks), else a matvec
-  const uint8_t* src;  // matvec: this lane's 16 bytes of the next item's first unit
-};
-
-__device__ __forceinline__ void fetch_next_task(const Params& P, const Ctx& cx, int s, Fetch& F) {
-  do {
-    walker_next(P, F.w, cx, s);
-  } while (!F.w.done && F.w.n == 0);
-  F.t = 0;
-  F.kv = F.w.type == T_ATT;
-  F.src = P.wpack + F.w.woff + (int64_t)F.w.u0 * kUnitBytes + cx.lane * 16;
-}
-
-// Ring of a stream wave: DEPTH (a power of two) slots of 2 KiB; item k sits in
-// slot k % DEPTH. Byte address of item k (LDS) for the copies; pointer for reads.
+// Wait until the item with `younger` items issued after it has landed: at most
+// 2*younger copies may still be in flight. Counts below the steady state
+// round down (a longer wait, never a shorter one).
 template <int DEPTH>
-__device__ __forceinline__ uint32_t ring_slot(uint32_t ring, int k) {
-  return ring + (uint32_t)(k & (DEPTH - 1)) * kItemBytes;
-}
-
-// Copy items until `limit` have been issued, the task sequence ends, or the
-// next item is a KV block of a step the stager has not opened yet. A matvec
-// item is the next 2 KiB of the task's packed weights.
-template <int DEPTH>
-__device__ __forceinline__ void fetch_upto(const Params& P, const Ctx& cx, int s, Fetch& F, int limit,
-                                           uint32_t ring) {
-  while (F.issued < limit && !F.w.done) {
-    const uint32_t dst = ring_slot<DEPTH>(ring, F.issued);
-    if (!F.kv) {
-      copy_nt(F.src, dst);
-      // the second unit of a piece's last item may not exist: copy the first again
-      copy_nt(2 * F.t + 1 < F.w.nu ? F.src + kUnitBytes : F.src, dst + kUnitBytes);
-      F.src += kItemBytes;
-    } else {
-      if (F.t == 0 && lds_ld(&cx.ctl[C_STEPOK]) < F.w.step + 1) return;
-      const int lane = cx.lane;
-      const int D8 = P.D / 8, ppu = 64 / D8;
-      const int pos = min(F.w.lo + (F.w.u0 + F.t) * ppu + lane / D8, F.w.end - 1);
-      const size_t off =
-          ((((size_t)F.w.layer * P.B + F.w.b) * P.Hkv + F.w.g) * (size_t)P.S + pos) * P.D + (lane % D8) * 8;
-      copy_sc1(P.kcache + off, dst);
-      copy_sc1(P.vcache + off, dst + kUnitBytes);
-    }
-    ++F.issued;
-    if (++F.t == F.w.n) fetch_next_task(P, cx, s, F);
-  }
-}
-
-// Wait until the oldest `n` not yet consumed items (from item k on) have
-// landed. Steady state: DEPTH - n younger items in flight; fewer only at the
-// end of the sequence or behind a KV step not yet open: then wait for all.
-template <int DEPTH, int N>
-__device__ __forceinline__ void wait_landed(const Fetch& F, int k) {
+__device__ __forceinline__ void wait_item(int younger) {
   cbar();
-  if (F.issued - k == DEPTH) wait_vmcnt<2 * (DEPTH - N)>();
+  if (younger >= DEPTH - 1) wait_vmcnt<2 * (DEPTH - 1)>();
+  else if (younger >= DEPTH / 2) wait_vmcnt<DEPTH>();
+  else if (younger >= 2) wait_vmcnt<4>();
+  else if (younger == 1) wait_vmcnt<2>();
   else wait_vmcnt<0>();
   cbar();
 }
 
-// Make sure items k .. k+n-1 have been copied (waiting for a KV step to open
-// if needed). false = leave the kernel.
-template <int DEPTH>
-__device__ __forceinline__ bool ensure_copied(const Params& P, const Ctx& cx, int s, Fetch& F, int k, int n,
-                                              uint32_t ring, Waits& wt) {
-  if (F.issued >= k + n) return true;
-  const uint64_t s0 = waits_now(wt);
-  while (F.issued < k + n) {
-    if (!spin_ctl(P, cx, C_STEPOK, F.w.step + 1)) return false;
-    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
-  }
-  waits_add(wt, 0, s0);
-  return true;
+__device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// [a0, a1): piece s of n things cut into kStreams nearly equal contiguous pieces
+__device__ __forceinline__ void piece(int n, int s, int& a0, int& a1) {
+  a0 = (int)((uint32_t)n * (uint32_t)s / kStreams);
+  a1 = (int)((uint32_t)n * (uint32_t)(s + 1) / kStreams);
 }
 
-// Items before k have been read: refill their slots, up to item k + DEPTH - 1.
-// In the steady state that is two whole items of the matvec task being
-// copied: four copies of consecutive 1 KiB.
-template <int DEPTH>
-__device__ __forceinline__ void refill(const Params& P, const Ctx& cx, int s, Fetch& F, int k, uint32_t ring) {
-  wait_lgkm();  // the reads of the slots being refilled have completed
-  if (F.issued == k + DEPTH - 2 && !F.kv && F.t + 2 < F.w.n && 2 * F.t + 3 < F.w.nu) {
-    const uint32_t d0 = ring_slot<DEPTH>(ring, F.issued), d1 = ring_slot<DEPTH>(ring, F.issued + 1);
-    copy_nt(F.src, d0);
-    copy_nt(F.src + kUnitBytes, d0 + kUnitBytes);
-    copy_nt(F.src + 2 * kUnitBytes, d1);
-    copy_nt(F.src + 3 * kUnitBytes, d1 + kUnitBytes);
-    F.src += 2 * kItemBytes;
-    F.issued += 2;
-    F.t += 2;
-  } else {
-    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
-  }
-}
+constexpr int kItemBytes = 2 * kUnitBytes;
 
 // ---------------------------------------------------------------------------
-// matvec
+// the copy cursor
 // ---------------------------------------------------------------------------
 
-// the column block after b in a row block of KB
-__device__ __forceinline__ int next_cb(int b, int KB) { return b + 1 == KB ? 0 : b + 1; }
-
-// Running state of a matvec piece: NC row sums and the (row block, column
-// block) of the next unit.
-template <int NC>
-struct MvState {
-  float acc[NC];
-  int rb, kb;
-  bool pend;  // acc holds sums of an unfinished row block
+struct Fetch {
+  int r, step;        // stream record and step of the task being copied
+  int t, n;           // next item of this wave in the task, and its item count
+  bool kv, done;
+  int pos0, last;     // attention: this lane's position in the piece's first block; last cached position
+  int ppi;            // attention: positions per item
+  const uint8_t* src; // matvec: this lane's 16 bytes of the next item; attention: the (layer, b, g) K rows
+  int issued;         // items copied so far (all tasks)
 };
 
-// Reduce the row sums over the 16 lanes of each row and store them as this
-// wave's partial sums of row block r (pout: this lane's row in column 0;
-// cs: floats between columns).
-template <int NC>
-__device__ __forceinline__ void mv_flush(MvState<NC>& st, float* pout, int cs, int icol, int r) {
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const float v = sum16(st.acc[c]);
-    if (icol == 0) pout[(size_t)c * cs + r * 4] = v;
-    st.acc[c] = 0.f;
-  }
-}
-
-template <int NC>
-__device__ __forceinline__ void mv_add(MvState<NC>& st, const float (&d)[NC], int KB, float* pout, int cs,
-                                       int icol) {
-#pragma unroll
-  for (int c = 0; c < NC; ++c) st.acc[c] += d[c];
-  if (st.kb == KB - 1) {
-    mv_flush<NC>(st, pout, cs, icol, st.rb);
-    st.kb = 0;
-    ++st.rb;
-    st.pend = false;
-  } else {
-    ++st.kb;
-    st.pend = true;
-  }
-}
-
-// Dot products of one unit's 8 weights (this lane) with NC activation columns
-// (lane 16*jrow + icol: columns 4*icol.. and 64 + 4*icol.. of column block b).
-template <int NC>
-__device__ __forceinline__ void mv_unit(const u32x4 wv, const float* hl, int kp, int b, float (&d)[NC]) {
-  float x[8];
-  unpack8(wv, x);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const float* q = hl + (size_t)c * kp + b * kUnitCols;
-    const float4 h0 = ld_f4(q), h1 = ld_f4(q + 64);
-    float a = x[0] * h0.x;
-    a = fmaf(x[1], h0.y, a); a = fmaf(x[2], h0.z, a); a = fmaf(x[3], h0.w, a);
-    a = fmaf(x[4], h1.x, a); a = fmaf(x[5], h1.y, a);
-    a = fmaf(x[6], h1.z, a); a = fmaf(x[7], h1.w, a);
-    d[c] = a;
-  }
-}
-
-// Matvec piece of stream wave s with NC staged columns: each lane accumulates
-// row jrow of a unit's row block over its 8 columns; a row block's sums are
-// reduced over the 16 lanes of the row and stored as this wave's partial sums.
-// Unit layout: lane 16*jrow + icol holds columns [4*icol, +4) and
-// [64 + 4*icol, +4) of its row. Items go two at a time (four units).
-template <int DEPTH, int NC>
-__device__ __forceinline__ bool stream_matvec(const Params& P, const Ctx& cx, int s, const Walker& w, Fetch& F,
-                                              int& k, uint32_t ring, Waits& wt, const float* hin, int kp,
-                                              float* part) {
-  const int lane = cx.lane;
-  const int jrow = lane >> 4, icol = lane & 15;
-  const int KB = w.KB;
-  const float* hl = hin + icol * 4;
-  float* pout = part + (size_t)s * P.ncap * P.vrow_stride + jrow;
-  const int pcs = P.vrow_stride;
-  const uint8_t* rp = reinterpret_cast<const uint8_t*>(cx.ring) - lds_addr(cx.ring) + lane * 16;  // LDS address -> pointer
-  MvState<NC> st;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) st.acc[c] = 0.f;
-  st.rb = w.u0 / KB;
-  st.kb = w.u0 - st.rb * KB;
-  st.pend = false;
-  int t = 0;
-  for (; t + 1 < w.n && 2 * t + 3 < w.nu; t += 2) {
-    if (!ensure_copied<DEPTH>(P, cx, s, F, k, 2, ring, wt)) return false;
-    wait_landed<DEPTH, 2>(F, k);
-    const uint8_t* i0 = rp + ring_slot<DEPTH>(ring, k);
-    const uint8_t* i1 = rp + ring_slot<DEPTH>(ring, k + 1);
-    const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
-    const u32x4 w2 = ld_u32x4(i1), w3 = ld_u32x4(i1 + kUnitBytes);
-    const int b0 = st.kb, b1 = next_cb(b0, KB), b2 = next_cb(b1, KB), b3 = next_cb(b2, KB);
-    float d[4][NC];
-    mv_unit<NC>(w0, hl, kp, b0, d[0]);
-    mv_unit<NC>(w1, hl, kp, b1, d[1]);
-    mv_unit<NC>(w2, hl, kp, b2, d[2]);
-    mv_unit<NC>(w3, hl, kp, b3, d[3]);
-    k += 2;
-    refill<DEPTH>(P, cx, s, F, k, ring);
-    if (st.kb + 4 < KB) {  // the row block goes on past these four units
-#pragma unroll
-      for (int c = 0; c < NC; ++c) st.acc[c] += (d[0][c] + d[1][c]) + (d[2][c] + d[3][c]);
-      st.kb += 4;
-      st.pend = true;
+// Move to the next task (in queue order, across steps) that has items for
+// wave s. A matvec piece is whole items; an attention piece is a run of
+// position blocks of the chunk's cached positions [lo, end).
+__device__ __forceinline__ void fetch_next_task(const Params& P, const Ctx& cx, int s, Fetch& F) {
+  F.t = 0;
+  F.n = 0;
+  for (;;) {
+    if (++F.r >= cx.nrec) {
+      F.r = 0;
+      ++F.step;
+    }
+    if (F.step >= P.n_steps || cx.nrec == 0) {
+      F.done = true;
+      return;
+    }
+    const StreamRec R = cx.recs[F.r];
+    const uint32_t tsbg = rfl(R.tsbg);
+    F.kv = (tsbg & 15) == T_ATT;
+    if (F.kv) {
+      const int b = (tsbg >> 6) & 1023;
+      if (b >= P.batch) continue;
+      const int pos = ld_uniform(P.pos_in, b) + F.step;
+      if (pos < 0 || pos >= P.S) continue;
+      const uint32_t lc = rfl(R.lc);
+      const int layer = lc & 0xffff, chunk = lc >> 16, g = tsbg >> 16;
+      const int64_t len = (int64_t)pos + 1;
+      const int lo = chunk_bound(chunk, len, P.Nc);
+      const int end = min(chunk_bound(chunk + 1, len, P.Nc), pos);
+      const int lpp = P.D / 8;
+      F.ppi = 64 / lpp;
+      const int nb = end > lo ? (end - lo + F.ppi - 1) / F.ppi : 0;
+      int j0, j1;
+      piece(nb, s, j0, j1);
+      F.n = j1 - j0;
+      F.pos0 = lo + j0 * F.ppi + cx.lane / lpp;
+      F.last = end - 1;
+      F.src = reinterpret_cast<const uint8_t*>(P.kcache + (((size_t)layer * P.B + b) * P.Hkv + g) * (size_t)P.S * P.D) +
+              (cx.lane % lpp) * 16;
     } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) mv_add<NC>(st, d[u], KB, pout, pcs, icol);
+      const int items = (int)rfl((uint32_t)R.n_units) / 2;
+      int i0, i1;
+      piece(items, s, i0, i1);
+      F.n = i1 - i0;
+      const int64_t woff =
+          (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
+      F.src = P.wpack + woff + (int64_t)i0 * kItemBytes + cx.lane * 16;
     }
-  }
-  for (; t < w.n; ++t) {
-    if (!ensure_copied<DEPTH>(P, cx, s, F, k, 1, ring, wt)) return false;
-    wait_landed<DEPTH, 1>(F, k);
-    const uint8_t* i0 = rp + ring_slot<DEPTH>(ring, k);
-    const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
-    float d0[NC], d1[NC];
-    mv_unit<NC>(w0, hl, kp, st.kb, d0);
-    mv_unit<NC>(w1, hl, kp, next_cb(st.kb, KB), d1);
-    k += 1;
-    wait_lgkm();  // the item's slot has been read
-    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
-    mv_add<NC>(st, d0, KB, pout, pcs, icol);
-    if (2 * t + 1 < w.nu) mv_add<NC>(st, d1, KB, pout, pcs, icol);
-  }
-  if (st.pend) mv_flush<NC>(st, pout, pcs, icol, st.rb);
-  return true;
-}
-
-// ---------------------------------------------------------------------------
-// attention
-// ---------------------------------------------------------------------------
-
-// One level of the merge of online-softmax states across lanes paired by xor
-// O; both lanes of a pair merge the same ordered pair of states.
-template <int O>
-__device__ __forceinline__ void att_merge_step(int G, float (&mv)[kMaxG], float (&lv)[kMaxG],
-                                               float (&av)[kMaxG][8]) {
-#pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
-    if (h < G) {
-      float m1, m2, l1, l2;
-      xpair<O>(mv[h], m1, m2);
-      xpair<O>(lv[h], l1, l2);
-      const float M = fmaxf(m1, m2);
-      const float a1 = m1 == -INFINITY ? 0.f : expf(m1 - M);
-      const float a2 = m2 == -INFINITY ? 0.f : expf(m2 - M);
-      lv[h] = l1 * a1 + l2 * a2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x1, x2;
-        xpair<O>(av[h][e], x1, x2);
-        av[h][e] = x1 * a1 + x2 * a2;
-      }
-      mv[h] = M;
-    }
+    if (F.n > 0) return;
   }
 }
 
-// Attention piece of stream wave s: lanes hold 8 dims of one position of a
-// block (D/8 lanes per position); each position group keeps an online-softmax
-// state per query head, merged across the wave at the end and stored as
-// {acc[D], m, l} per head.
+// Copy items until `limit` have been issued, the task sequence ends, or the
+// next item is a KV block of a step the stager has not opened yet.
 template <int DEPTH>
-__device__ __forceinline__ bool stream_att(const Params& P, const Ctx& cx, int s, const Walker& w, Fetch& F,
-                                           int& k, uint32_t ring, Waits& wt, const float* hin, float* part) {
-  const int lane = cx.lane;
-  const int D = P.D, lpp = D / 8, ppu = 64 / lpp;
-  const int pg = lane / lpp, de = (lane % lpp) * 8;
-  const int G = P.G;
-  const float scale = P.attn_scale;
-  const uint8_t* rp = reinterpret_cast<const uint8_t*>(cx.ring) - lds_addr(cx.ring) + lane * 16;
-  float qv[kMaxG][8], av[kMaxG][8], mv[kMaxG], lv[kMaxG];
-  const float* q = hin + att_raw_floats(P);
+__device__ __forceinline__ void fetch_upto(const Params& P, const Ctx& cx, int s, Fetch& F, int limit,
+                                           uint32_t ring) {
+  while (F.issued < limit) {
+    if (F.t == F.n) {
+      fetch_next_task(P, cx, s, F);
+      if (F.done) return;
+    }
+    const uint32_t dst = ring + ((uint32_t)F.issued % DEPTH) * kItemBytes;
+    if (!F.kv) {
+      copy_nt(F.src, dst);
+      copy_nt(F.src + kUnitBytes, dst + kUnitBytes);
+      F.src += kItemBytes;
+    } else {
+      if (F.t == 0 && lds_ld(&cx.ctl[C_STEPOK]) < F.step + 1) return;
+      const int pos = min(F.pos0 + F.t * F.ppi, F.last);
+      const uint8_t* kb = F.src + (size_t)pos * P.D * 2;
+      copy_sc1(kb, dst);
+      copy_sc1(kb + (reinterpret_cast<const uint8_t*>(P.vcache) - reinterpret_cast<const uint8_t*>(P.kcache)),
+               dst + kUnitBytes);
+    }
+    ++F.issued;
+    ++F.t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// compute
+// ---------------------------------------------------------------------------
+
+struct Comp {
+  int r, step;     // stream record and step of the task being computed
+  int slot, type;  // type -1: none
+  int left;        // items of this wave left in the task
+  int rb, kb, KB;  // matvec: row block and column block of the next item, column blocks
+  bool pend;       // matvec: sums of an unfinished row block are held
+  int t, lo, end;  // attention: next block, cached positions [lo, end) of the chunk
+  int u0;          // attention: first block of this wave
+};
+
+template <int NC>
+struct Acc {
+  float a[NC];
+};
+
+// Dot product of 8 bf16 weights (packed in w) with 8 activations.
+__device__ __forceinline__ float dot8(const u32x4 w, const float4 x, const float4 y) {
+  float a = __uint_as_float(w.x << 16) * x.x;
+  a = fmaf(__uint_as_float(w.x & 0xffff0000u), x.y, a);
+  a = fmaf(__uint_as_float(w.y << 16), x.z, a);
+  a = fmaf(__uint_as_float(w.y & 0xffff0000u), x.w, a);
+  float b = __uint_as_float(w.z << 16) * y.x;
+  b = fmaf(__uint_as_float(w.z & 0xffff0000u), y.y, b);
+  b = fmaf(__uint_as_float(w.w << 16), y.z, b);
+  b = fmaf(__uint_as_float(w.w & 0xffff0000u), y.w, b);
+  return a + b;
+}
+
+// The row sums of row block rb, reduced over the 16 lanes of each row, as
+// this wave's partial sums. Every lane of row j holds the sum and all of them
+// store it to row j's word: no lane-dependent branch in the stream loop (a
+// divergent branch there would make the loop's own control divergent).
+template <int NC>
+__device__ __forceinline__ void mv_flush(Acc<NC>& A, float* pout, int cs, int rb, int icol) {
+  (void)icol;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    pout[c * cs + rb * 4] = sum16(A.a[c]);
+    A.a[c] = 0.f;
+  }
+}
+
+// Attention state of one wave over its piece: G query heads, this lane's 8
+// dims of the query and of the output accumulator, and the running maximum and
+// denominator shared by the whole wave (one maximum for all lanes, so the
+// lanes' outputs only need adding at the end).
+struct AttState {
+  float q[kMaxG][8], acc[kMaxG][8], m[kMaxG], l[kMaxG];
+};
+
+// Reduce over the position groups of a wave (lanes equal modulo lpp): max or sum.
+template <bool MAX>
+__device__ __forceinline__ float across_groups(float v, int lpp) {
+  float lo, hi;
+  if (lpp <= 4) { xpair<4>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
+  if (lpp <= 8) { xpair<8>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
+  if (lpp <= 16) { xpair<16>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
+  xpair<32>(v, lo, hi);
+  return MAX ? fmaxf(lo, hi) : lo + hi;
+}
+
+// One item (position block) of attention: scores of the G heads, the block's
+// maximum, the rescale of the running state and the weighted values.
+__device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32x4 wk, const u32x4 wv, bool valid,
+                                         int lpp) {
+  float kf[8], vf[8];
+  unpack8(wk, kf);
+  unpack8(wv, vf);
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
-    mv[h] = -INFINITY;
-    lv[h] = 0.f;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
-    if (h < G) {
-      x = ld_f4(q + h * D + de);
-      y = ld_f4(q + h * D + de + 4);
-    }
-    qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
-    qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) av[h][e] = 0.f;
-  }
-  for (int t = 0; t < w.n; ++t) {
-    if (!ensure_copied<DEPTH>(P, cx, s, F, k, 1, ring, wt)) return false;
-    wait_landed<DEPTH, 1>(F, k);
-    const uint8_t* it = rp + ring_slot<DEPTH>(ring, k);
-    const u32x4 wk = ld_u32x4(it), wv = ld_u32x4(it + kUnitBytes);
-    k += 1;
-    wait_lgkm();  // the item's slot has been read
-    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
-    const bool valid = w.lo + (w.u0 + t) * ppu + pg < w.end;
-    float kf[8], vf[8];
-    unpack8(wk, kf);
-    unpack8(wv, vf);
-    // heads past G hold zero queries; their state is never stored
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
+    if (h < P.G) {
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qv[h][e], kf[e], d);
+      for (int e = 0; e < 8; ++e) d = fmaf(S.q[h][e], kf[e], d);
       d = group_sum(d, lpp);
-      const float sc = valid ? d * scale : -INFINITY;
-      const float mn = fmaxf(mv[h], sc);
-      const float al = mn == -INFINITY ? 1.f : expf(mv[h] - mn);
-      const float pe = sc == -INFINITY ? 0.f : expf(sc - mn);
-      lv[h] = fmaf(lv[h], al, pe);
+      const float sc = valid ? d * P.attn_scale : -INFINITY;
+      const float mn = fmaxf(S.m[h], across_groups<true>(sc, lpp));
+      const float al = mn == -INFINITY ? 1.f : expf(S.m[h] - mn);
+      const float pe = valid ? expf(sc - mn) : 0.f;
+      // pe is equal on the lanes of a group, so the sum over groups of any
+      // one lane's pe is the block's denominator share, in every lane
+      S.l[h] = fmaf(S.l[h], al, across_groups<false>(pe, lpp));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) av[h][e] = fmaf(pe, vf[e], av[h][e] * al);
-      mv[h] = mn;
+      for (int e = 0; e < 8; ++e) S.acc[h][e] = fmaf(pe, vf[e], S.acc[h][e] * al);
+      S.m[h] = mn;
     }
   }
-  // merge the position groups of the wave (lanes with equal dims)
-  if (lpp <= 1) att_merge_step<1>(G, mv, lv, av);
-  if (lpp <= 2) att_merge_step<2>(G, mv, lv, av);
-  if (lpp <= 4) att_merge_step<4>(G, mv, lv, av);
-  if (lpp <= 8) att_merge_step<8>(G, mv, lv, av);
-  if (lpp <= 16) att_merge_step<16>(G, mv, lv, av);
-  if (lpp <= 32) att_merge_step<32>(G, mv, lv, av);
-  const int stride = G * (D + 2);
-  if (pg == 0) {
+}
+
+// End of a wave's attention piece: add the lanes' outputs over the position
+// groups and store {acc[D], m, l} per head as this wave's partial.
+__device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* part, int s, int lane, int lpp) {
+  (void)lane;
+  const int D = P.D, stride = P.G * (D + 2), de = (lane % lpp) * 8;
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-      if (h < G) {
-        float* dst = part + s * stride + h * (D + 2);
-        *reinterpret_cast<float4*>(dst + de) = make_float4(av[h][0], av[h][1], av[h][2], av[h][3]);
-        *reinterpret_cast<float4*>(dst + de + 4) = make_float4(av[h][4], av[h][5], av[h][6], av[h][7]);
-        if (lane == 0) {
-          dst[D] = mv[h];
-          dst[D + 1] = lv[h];
-        }
+  for (int h = 0; h < kMaxG; ++h) {
+    if (h < P.G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) S.acc[h][e] = across_groups<false>(S.acc[h][e], lpp);
+      // every lane holds the sums of its dims (and the wave's m, l): lanes with
+      // equal dims store equal values to the same words
+      float* dst = part + s * stride + h * (D + 2);
+      *reinterpret_cast<float4*>(dst + de) = make_float4(S.acc[h][0], S.acc[h][1], S.acc[h][2], S.acc[h][3]);
+      *reinterpret_cast<float4*>(dst + de + 4) = make_float4(S.acc[h][4], S.acc[h][5], S.acc[h][6], S.acc[h][7]);
+      dst[D] = S.m[h];
+      dst[D + 1] = S.l[h];
+    }
+  }
+}
+
+// Items of a matvec piece, two at a time while both have landed, refilling
+// the ring from the same copy task; returns to the caller (which owns the
+// slow paths) when the compute task ends, the next item is not copied yet, or
+// the copy cursor reaches the end of its task.
+template <int DEPTH, int NC>
+__device__ __forceinline__ void matvec_run(const Params& P, Comp& C, Fetch& F, int& k, uint32_t ring,
+                                           const uint8_t* rp, const float* hin, int kp, float* pout, int icol,
+                                           Acc<NC>& A, uint32_t& t_first, bool prof) {
+  const int KB = C.KB;
+  const float* h = hin + icol * 4;
+  for (;;) {
+    const int ready = F.issued - k;
+    if (ready >= 2 && C.left >= 2) {
+      wait_item<DEPTH>(ready - 2);
+      if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
+      const uint8_t* i0 = rp + ((uint32_t)k % DEPTH) * kItemBytes;
+      const uint8_t* i1 = rp + ((uint32_t)(k + 1) % DEPTH) * kItemBytes;
+      const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
+      const u32x4 w2 = ld_u32x4(i1), w3 = ld_u32x4(i1 + kUnitBytes);
+      const int kb1 = C.kb + 2 == KB ? 0 : C.kb + 2;
+      float d0[NC], d1[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float* ha = h + c * kp + C.kb * kUnitCols;
+        const float* hb = h + c * kp + kb1 * kUnitCols;
+        d0[c] = dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
+        d1[c] = dot8(w2, ld_f4(hb), ld_f4(hb + 64)) + dot8(w3, ld_f4(hb + kUnitCols), ld_f4(hb + kUnitCols + 64));
       }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) A.a[c] += d0[c];
+      C.kb += 2;
+      if (C.kb == KB) {
+        mv_flush<NC>(A, pout, P.vrow_stride, C.rb, icol);
+        C.kb = 0;
+        ++C.rb;
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) A.a[c] += d1[c];
+      C.kb += 2;
+      C.pend = true;
+      if (C.kb == KB) {
+        mv_flush<NC>(A, pout, P.vrow_stride, C.rb, icol);
+        C.kb = 0;
+        ++C.rb;
+        C.pend = false;
+      }
+      k += 2;
+      C.left -= 2;
+    } else if (ready >= 1) {
+      wait_item<DEPTH>(ready - 1);
+      if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
+      const uint8_t* i0 = rp + ((uint32_t)k % DEPTH) * kItemBytes;
+      const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float* ha = h + c * kp + C.kb * kUnitCols;
+        A.a[c] += dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
+      }
+      C.kb += 2;
+      C.pend = true;
+      if (C.kb == KB) {
+        mv_flush<NC>(A, pout, P.vrow_stride, C.rb, icol);
+        C.kb = 0;
+        ++C.rb;
+        C.pend = false;
+      }
+      k += 1;
+      C.left -= 1;
+    } else {
+      return;
     }
+    // refill the read slots from the current copy task (weights only)
+    if (F.kv) return;
+    wait_lgkm();
+    while (F.issued < k + DEPTH && F.t < F.n) {
+      const uint32_t dst = ring + ((uint32_t)F.issued % DEPTH) * kItemBytes;
+      copy_nt(F.src, dst);
+      copy_nt(F.src + kUnitBytes, dst + kUnitBytes);
+      F.src += kItemBytes;
+      ++F.issued;
+      ++F.t;
+    }
+    if (C.left == 0 || F.issued < k + DEPTH) return;
   }
-  return true;
 }
 
 // ---------------------------------------------------------------------------
 // stream wave
 // ---------------------------------------------------------------------------
 
-template <int DEPTH>
+template <int DEPTH, int NC>
 __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s) {
-  Waits wt;  // KV step not open, -, task staged, items
-  waits_init(P, cx, wt);
+  const int lane = cx.lane, jrow = lane >> 4, icol = lane & 15;
   const uint32_t ring = lds_addr(cx.ring) + (uint32_t)s * DEPTH * kItemBytes;
+  const uint8_t* rp = cx.ring + (size_t)s * DEPTH * kItemBytes + lane * 16;  // this lane's bytes of slot 0
+  const bool prof = P.profile != nullptr;
+  const int lpp = P.D / 8, ppi = 64 / lpp;
+  Waits wt;  // j0: KV step not open; j2: task not staged; j3: items
+  waits_init(P, cx, wt);
+
   Fetch F;
-  walker_init(F.w, cx);
+  F.r = -1;
+  F.step = 0;
+  F.t = F.n = 0;
   F.issued = 0;
-  fetch_next_task(P, cx, s, F);
-  fetch_upto<DEPTH>(P, cx, s, F, DEPTH, ring);
+  F.done = false;
+
+  Comp C;
+  C.r = -1;
+  C.step = 0;
+  C.left = 0;
+  C.type = -1;
+  C.slot = 0;
   int k = 0;  // items consumed
-  Walker w;
-  walker_init(w, cx);
-  const int ncols = P.batch;
+  const float* hin = nullptr;
+  float* part = nullptr;
+  int kp = 0;
+  Acc<NC> A;
+  AttState S;
+  uint32_t t_first = 0;
+
   for (;;) {
-    {
-      const uint64_t s0 = waits_now(wt);
-      walker_next(P, w, cx, s);
-      waits_add(wt, 7, s0);
-    }
-    if (w.done) break;
-    {
-      const uint64_t s0 = waits_now(wt);
-      if (!spin_ctl(P, cx, C_STAGED, w.i + 1)) return;
-      waits_add(wt, 2, s0);
-    }
-    const float* hin = slot_ptr(cx, w.slot) + kHdr;
-    float* part = part_ptr(cx, w.slot);
-    const uint64_t s1 = waits_now(wt);
-    bool ok;
-    if (w.type == T_ATT) {
-      ok = stream_att<DEPTH>(P, cx, s, w, F, k, ring, wt, hin, part);
-    } else {
-      const int kp = slot_kp(P, w.slot);
-      switch (ncols) {
-        case 1: ok = stream_matvec<DEPTH, 1>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
-        case 2: ok = stream_matvec<DEPTH, 2>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
-        case 3: ok = stream_matvec<DEPTH, 3>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
-        default: ok = stream_matvec<DEPTH, 4>(P, cx, s, w, F, k, ring, wt, hin, kp, part); break;
+    // refill every slot whose item has been read
+    wait_lgkm();
+    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
+
+    if (C.left == 0) {
+      // ---- the compute cursor's task change: finish the task, start the next
+      if (C.type >= 0) {
+        if (C.type == T_ATT) {
+          att_finish(P, S, part, s, lane, lpp);
+        } else if (C.pend) {
+          mv_flush<NC>(A, part + (size_t)s * P.ncap * P.vrow_stride + jrow, P.vrow_stride, C.rb, icol);
+        }
+        if (prof) {
+          uint32_t* pw = prof_words(cx, C.slot, s);
+          pw[1] = t_first;
+          pw[2] = rfl((uint32_t)wall_clock64());
+        }
+        lds_add_lane0(&cx.ctl[C_DONE + C.slot], 1);
+        C.type = -1;
       }
+      if (++C.r >= cx.nrec) {
+        C.r = 0;
+        ++C.step;
+      }
+      if (C.step >= P.n_steps || cx.nrec == 0) break;
+      const StreamRec R = cx.recs[C.r];
+      const uint32_t tsbg = rfl(R.tsbg), kq = rfl(R.kq);
+      C.type = tsbg & 15;
+      C.slot = (tsbg >> 4) & 3;
+      if (C.slot < 2) C.slot ^= (int)rfl((uint32_t)R.flip) & C.step;
+      {
+        const uint64_t s0 = waits_now(wt);
+        if (!spin_ctl(P, cx, C_STAGED, C.step * (cx.q1 - cx.q0) + (int)(kq >> 16) + 1)) return;
+        waits_add(wt, 2, s0);
+      }
+      t_first = 0;
+      if (prof) prof_words(cx, C.slot, s)[0] = rfl((uint32_t)wall_clock64());
+      hin = slot_ptr(cx, C.slot) + kHdr;
+      part = part_ptr(cx, C.slot);
+      if (C.type == T_ATT) {
+        const int* ih = reinterpret_cast<const int*>(slot_ptr(cx, C.slot));
+        const int flags = lds_ld(&ih[H_FLAGS]);
+        C.lo = lds_ld(&ih[H_LO]);
+        C.end = lds_ld(&ih[H_END]);
+        const int nb = (flags & 1) && C.end > C.lo ? (C.end - C.lo + ppi - 1) / ppi : 0;
+        int j1;
+        piece(nb, s, C.u0, j1);
+        C.left = j1 - C.u0;
+        C.t = 0;
+        const float* q = hin + att_raw_floats(P);
+        const int de = (lane % lpp) * 8;
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+          S.m[h] = -INFINITY;
+          S.l[h] = 0.f;
+          float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+          if (h < P.G) {
+            x = ld_f4(q + h * P.D + de);
+            y = ld_f4(q + h * P.D + de + 4);
+          }
+          S.q[h][0] = x.x; S.q[h][1] = x.y; S.q[h][2] = x.z; S.q[h][3] = x.w;
+          S.q[h][4] = y.x; S.q[h][5] = y.y; S.q[h][6] = y.z; S.q[h][7] = y.w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) S.acc[h][e] = 0.f;
+        }
+      } else {
+        const int items = (int)rfl((uint32_t)R.n_units) / 2;
+        int i0, i1;
+        piece(items, s, i0, i1);
+        C.left = i1 - i0;
+        C.KB = kq & 0xffff;
+        C.rb = (2 * i0) / C.KB;
+        C.kb = 2 * i0 - C.rb * C.KB;
+        C.pend = false;
+        kp = slot_kp(P, C.slot);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) A.a[c] = 0.f;
+      }
+      waits_count(wt, 3, C.left);
+      continue;  // the new task may have no items for this wave
     }
-    if (!ok) return;
-    if (w.type == T_LM) waits_add(wt, 5, s1);
-    else waits_add(wt, 8, s1);
-    waits_count(wt, 3, w.n);
-    const uint64_t s2 = waits_now(wt);
-    lds_add(&cx.ctl[C_DONE + w.slot], 1);
-    waits_add(wt, 9, s2);
+
+    // ---- item k
+    if (F.issued <= k) {
+      // not copied yet: a KV block of a step the stager has not opened
+      const uint64_t s0 = waits_now(wt);
+      if (!spin_ctl(P, cx, C_STEPOK, F.step + 1)) return;
+      waits_add(wt, 0, s0);
+      continue;
+    }
+    if (C.type == T_ATT) {
+      wait_item<DEPTH>(F.issued - k - 1);
+      if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
+      const uint8_t* it = rp + ((uint32_t)k % DEPTH) * kItemBytes;
+      const u32x4 w0 = ld_u32x4(it), w1 = ld_u32x4(it + kUnitBytes);
+      const bool valid = C.lo + (C.u0 + C.t) * ppi + lane / lpp < C.end;
+      att_item(P, S, w0, w1, valid, lpp);
+      ++C.t;
+      ++k;
+      --C.left;
+    } else {
+      matvec_run<DEPTH, NC>(P, C, F, k, ring, rp, hin, kp, part + (size_t)s * P.ncap * P.vrow_stride + jrow, icol,
+                            A, t_first, prof);
+    }
   }
   wait_all();
   waits_put(P, cx, wt);

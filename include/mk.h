@@ -157,9 +157,16 @@ int mk_debug_drop_signal(mk_model *m, int32_t task_id);
 
 /* Optional per-task timeline (MPK walk-through 3.3.1: profiler_tensor).
  * d_buf: device buffer of `bytes` bytes receiving, for each executed task of
- * the last megakernel call, 4 x uint64 {task_id | cu << 32, t_ready, t_start,
- * t_end} in 100 MHz constant-clock ticks, slot = step * n_tasks + task id.
- * NULL disables. MK_EINVAL if bytes is too small for one step. */
+ * the last megakernel call, 12 x uint64 {t_event, t_staged, t_computed,
+ * t_signal, w0, w1, w2, w3, f0, f1, f2, f3} in 100 MHz constant-clock ticks: when its
+ * dependent event was seen complete, when its inputs were staged, when its
+ * compute finished and when its epilogue finished (just before it counts its
+ * triggering event); for a task with weight or KV units, w_s holds stream
+ * wave s's start (high 32 bits) and end (low 32 bits) of its piece, as the
+ * low 32 bits of the same clock, and f_s when its first item had landed;
+ * slot = step * n_tasks + task id. The task's compute unit is the one its queue
+ * names. Written only when the buffer holds n_steps * n_tasks slots; NULL
+ * disables. MK_EINVAL if bytes is too small for one step. */
 int mk_set_profile_buffer(mk_model *m, void *d_buf, size_t bytes);
 
 /* Optional wait accounting of the megakernel's waves (diagnostics). d_buf:
@@ -171,8 +178,7 @@ int mk_set_profile_buffer(mk_model *m, void *d_buf, size_t bytes);
  *   wave 1 (retirer): j0 waiting for staging, j1 waiting for the stream
  *                     waves, j2 epilogue, j3 tasks;
  *   waves 2-5 (stream): j0 waiting for a KV step to open, j2 waiting for
- *                     staging, j3 items, j5 inside LM-head tasks, j7 finding
- *                     the next task, j8 inside other tasks, j9 signalling.
+ *                     staging, j3 items.
  * NULL disables. */
 int mk_set_wait_counters(mk_model *m, void *d_buf, size_t bytes);
 
