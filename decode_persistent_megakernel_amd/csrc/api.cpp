@@ -204,7 +204,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   if (d.max_batch > kMaxCols)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: max_batch above 4 is not supported by the VALU task bodies");
   if (G > kMaxG) return fail(MK_EUNSUPPORTED, "mk_load_weights: more than 4 query heads per kv head");
-  if (64 % (D / 8) != 0) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim/8 must divide 64");
+  if (D != 64 && D != 128) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim must be 64 or 128");
   if (d.hidden > 4096) return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden above 4096");
   if (std::max({kb_h, kb_qd, kb_f}) > 254) return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32512");
   if (int64_t(g.opts.attn_chunks) * (int64_t(d.max_seq) + 1) >= (int64_t(1) << 32))

@@ -673,13 +673,15 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
   const int flags = ih[H_FLAGS];
   if (!(flags & 4)) return;  // sequence not in this call's batch
   const bool owner = flags & 2;
-  const int G = P.G, D = P.D;
+  const int G = P.G, D = P.D, D4 = D / 4;
   const float* q = hdr + kHdr + att_raw_floats(P);
   const float* kf = q + G * D;
   const float* vf = kf + D;
   const uint32_t* kvw = reinterpret_cast<const uint32_t*>(vf + D);
   const float* part = part_ptr(cx, slot);
+  const float* pml = part + kStreams * G * D;  // (m, l) of [wave][head]
   const int lane = cx.lane, p = ih[H_P];
+  // score of the new position (its key and value are the staged ones)
   float sp[kMaxG];
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
@@ -690,33 +692,49 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
       sp[h] = wave_sum(a) * P.attn_scale;
     }
   }
-  const int stride = G * (D + 2);
-  for (int idx = lane; idx < G * D; idx += 64) {
-    const int h = idx / D, d = idx - h * D;
+  // merge of the stream waves' partials and the new position: each lane owns
+  // four dims of one head
+  const size_t chunk0 = ((size_t)T.b * P.Hq + (size_t)T.g * G) * P.Nc + T.chunk;  // head 0 of the group
+  const rsrc_t racc = make_rsrc(P.part_acc, 0xffffffffu);
+  for (int qd = lane; qd < G * D4; qd += 64) {
+    const int h = qd / D4, d = (qd - h * D4) * 4;
     float s_new = sp[0];
 #pragma unroll
     for (int hh = 1; hh < kMaxG; ++hh)
       if (h == hh) s_new = sp[hh];
-    float M = s_new;
-    for (int w = 0; w < kStreams; ++w) M = fmaxf(M, part[w * stride + h * (D + 2) + D]);
-    float l = 0.f, a = 0.f;
+    float mw[kStreams], lw[kStreams];
+    float4 aw[kStreams];
+#pragma unroll
     for (int w = 0; w < kStreams; ++w) {
-      const float mw = part[w * stride + h * (D + 2) + D];
-      if (mw == -INFINITY) continue;
-      const float e = expf(mw - M);
-      l = fmaf(part[w * stride + h * (D + 2) + D + 1], e, l);
-      a = fmaf(part[w * stride + h * (D + 2) + d], e, a);
+      mw[w] = pml[(w * G + h) * 2];
+      lw[w] = pml[(w * G + h) * 2 + 1];
+      aw[w] = *reinterpret_cast<const float4*>(part + (size_t)(w * G + h) * D + d);
+    }
+    float M = s_new;
+#pragma unroll
+    for (int w = 0; w < kStreams; ++w) M = fmaxf(M, mw[w]);
+    float l = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kStreams; ++w) {
+      const float e = mw[w] == -INFINITY ? 0.f : expf(mw[w] - M);
+      l = fmaf(lw[w], e, l);
+      a.x = fmaf(aw[w].x, e, a.x); a.y = fmaf(aw[w].y, e, a.y);
+      a.z = fmaf(aw[w].z, e, a.z); a.w = fmaf(aw[w].w, e, a.w);
     }
     if (owner) {
       const float e = expf(s_new - M);
       l += e;
-      a = fmaf(e, vf[d], a);
+      a.x = fmaf(e, vf[d], a.x); a.y = fmaf(e, vf[d + 1], a.y);
+      a.z = fmaf(e, vf[d + 2], a.z); a.w = fmaf(e, vf[d + 3], a.w);
     }
-    const size_t slot_idx = ((size_t)T.b * P.Hq + (size_t)T.g * G + h) * P.Nc + T.chunk;
-    st_coh(P.part_acc + slot_idx * D + d, a);
+    const size_t ci = chunk0 + (size_t)h * P.Nc;
+    u32x4 v;
+    v.x = __float_as_uint(a.x); v.y = __float_as_uint(a.y); v.z = __float_as_uint(a.z); v.w = __float_as_uint(a.w);
+    __builtin_amdgcn_raw_buffer_store_b128(v, racc, (uint32_t)((ci * D + d) * 4), 0, kAuxCoherent);
     if (d == 0) {
-      st_coh(P.part_ml + slot_idx * 2, M);
-      st_coh(P.part_ml + slot_idx * 2 + 1, l);
+      st_coh(P.part_ml + ci * 2, M);
+      st_coh(P.part_ml + ci * 2 + 1, l);
     }
   }
   if (owner) {
@@ -776,20 +794,38 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
           }
         wait_lgkm();
       }
-      // weighted sum over chunks, eight independent chains so the LDS reads overlap
-      for (int idx = lane; idx < G * D; idx += 64) {
-        const int h = idx / D, d = idx - h * D;
+      // weighted sum over chunks: each lane owns four dims of one head (16-byte
+      // LDS reads, eight chunks in flight) and stores them as one 16-byte word
+      const int D4 = D / 4;
+      const rsrc_t r = make_rsrc(P.attn + (size_t)T.b * P.Hq * D + (size_t)T.g * G * D, (uint32_t)(G * D) * 4);
+      for (int q = lane; q < G * D4; q += 64) {
+        const int h = q / D4, d = (q - h * D4) * 4;
         const float* wc = ml + h * Nc * 2;
         const float* ac = acc + (size_t)h * Nc * D + d;
-        float n[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float4 n = make_float4(0.f, 0.f, 0.f, 0.f);
         int c = 0;
         for (; c + 8 <= Nc; c += 8) {
+          float4 a[8];
+          float w[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) n[j] = fmaf(wc[(c + j) * 2], ac[(size_t)(c + j) * D], n[j]);
+          for (int j = 0; j < 8; ++j) {
+            a[j] = *reinterpret_cast<const float4*>(ac + (size_t)(c + j) * D);
+            w[j] = wc[(c + j) * 2];
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            n.x = fmaf(w[j], a[j].x, n.x); n.y = fmaf(w[j], a[j].y, n.y);
+            n.z = fmaf(w[j], a[j].z, n.z); n.w = fmaf(w[j], a[j].w, n.w);
+          }
         }
-        for (; c < Nc; ++c) n[0] = fmaf(wc[c * 2], ac[(size_t)c * D], n[0]);
-        const float num = ((n[0] + n[1]) + (n[2] + n[3])) + ((n[4] + n[5]) + (n[6] + n[7]));
-        st_coh(P.attn + (size_t)T.b * P.Hq * D + ((size_t)T.g * G + h) * D + d, num);
+        for (; c < Nc; ++c) {
+          const float4 a = *reinterpret_cast<const float4*>(ac + (size_t)c * D);
+          const float w = wc[c * 2];
+          n.x = fmaf(w, a.x, n.x); n.y = fmaf(w, a.y, n.y); n.z = fmaf(w, a.z, n.z); n.w = fmaf(w, a.w, n.w);
+        }
+        u32x4 v;
+        v.x = __float_as_uint(n.x); v.y = __float_as_uint(n.y); v.z = __float_as_uint(n.z); v.w = __float_as_uint(n.w);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (h * D + d) * 4, 0, kAuxCoherent);
       }
       break;
     }

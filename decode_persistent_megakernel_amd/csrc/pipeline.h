@@ -225,22 +225,35 @@ __device__ __forceinline__ void mv_flush(Acc<NC>& A, float* pout, int cs, int rb
 struct AttState {
   float q[kMaxG][8], acc[kMaxG][8], m[kMaxG], l[kMaxG];
 };
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
-// Reduce over the position groups of a wave (lanes equal modulo lpp): max or sum.
-template <bool MAX>
-__device__ __forceinline__ float across_groups(float v, int lpp) {
+// Reduce over the position groups of a wave (lanes equal modulo LPP): max or sum.
+template <bool MAX, int LPP>
+__device__ __forceinline__ float across_groups(float v) {
   float lo, hi;
-  if (lpp <= 4) { xpair<4>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
-  if (lpp <= 8) { xpair<8>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
-  if (lpp <= 16) { xpair<16>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
+  if constexpr (LPP <= 8) { xpair<8>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
+  if constexpr (LPP <= 16) { xpair<16>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
   xpair<32>(v, lo, hi);
   return MAX ? fmaxf(lo, hi) : lo + hi;
 }
 
+// Sum over the LPP lanes of a position group.
+template <int LPP>
+__device__ __forceinline__ float in_group(float v) {
+  v += dpp<kDppSwap1>(v);
+  v += dpp<kDppSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  if constexpr (LPP == 16) v += dpp<kDppMirror>(v);
+  return v;
+}
+
 // One item (position block) of attention: scores of the G heads, the block's
-// maximum, the rescale of the running state and the weighted values.
-__device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32x4 wk, const u32x4 wv, bool valid,
-                                         int lpp) {
+// maximum, the rescale of the running state and the weighted values. Scores
+// are in base-2 units (the queries carry scale * log2(e)), so the
+// exponentials are the hardware's exp2.
+template <int LPP>
+__device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32x4 wk, const u32x4 wv, bool valid) {
   float kf[8], vf[8];
   unpack8(wk, kf);
   unpack8(wv, vf);
@@ -250,14 +263,13 @@ __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(S.q[h][e], kf[e], d);
-      d = group_sum(d, lpp);
-      const float sc = valid ? d * P.attn_scale : -INFINITY;
-      const float mn = fmaxf(S.m[h], across_groups<true>(sc, lpp));
-      const float al = mn == -INFINITY ? 1.f : expf(S.m[h] - mn);
-      const float pe = valid ? expf(sc - mn) : 0.f;
+      const float sc = valid ? in_group<LPP>(d) : -INFINITY;
+      const float mn = fmaxf(S.m[h], across_groups<true, LPP>(sc));
+      const float al = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(S.m[h] - mn);
+      const float pe = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
       // pe is equal on the lanes of a group, so the sum over groups of any
       // one lane's pe is the block's denominator share, in every lane
-      S.l[h] = fmaf(S.l[h], al, across_groups<false>(pe, lpp));
+      S.l[h] = fmaf(S.l[h], al, across_groups<false, LPP>(pe));
 #pragma unroll
       for (int e = 0; e < 8; ++e) S.acc[h][e] = fmaf(pe, vf[e], S.acc[h][e] * al);
       S.m[h] = mn;
@@ -266,22 +278,27 @@ __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32
 }
 
 // End of a wave's attention piece: add the lanes' outputs over the position
-// groups and store {acc[D], m, l} per head as this wave's partial.
-__device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* part, int s, int lane, int lpp) {
-  (void)lane;
-  const int D = P.D, stride = P.G * (D + 2), de = (lane % lpp) * 8;
+// groups and store this wave's partial: acc[D] of each head (at [wave][head]),
+// then (m, l) of each head (at [wave][head] after all the accumulators), m in
+// natural-log units. A piece without items stores m = -inf, l = 0 and zeros.
+template <int LPP>
+__device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* part, int s, int lane, bool empty) {
+  const int D = P.D, G = P.G, de = (lane % LPP) * 8;
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
-    if (h < P.G) {
+    if (h < G) {
+      if (!empty) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) S.acc[h][e] = across_groups<false>(S.acc[h][e], lpp);
+        for (int e = 0; e < 8; ++e) S.acc[h][e] = across_groups<false, LPP>(S.acc[h][e]);
+      }
       // every lane holds the sums of its dims (and the wave's m, l): lanes with
       // equal dims store equal values to the same words
-      float* dst = part + s * stride + h * (D + 2);
+      float* dst = part + (size_t)(s * G + h) * D;
       *reinterpret_cast<float4*>(dst + de) = make_float4(S.acc[h][0], S.acc[h][1], S.acc[h][2], S.acc[h][3]);
       *reinterpret_cast<float4*>(dst + de + 4) = make_float4(S.acc[h][4], S.acc[h][5], S.acc[h][6], S.acc[h][7]);
-      dst[D] = S.m[h];
-      dst[D + 1] = S.l[h];
+      float* ml = part + (size_t)kStreams * G * D + (s * G + h) * 2;
+      ml[0] = S.m[h] * kLn2;
+      ml[1] = S.l[h];
     }
   }
 }
@@ -416,7 +433,8 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
       // ---- the compute cursor's task change: finish the task, start the next
       if (C.type >= 0) {
         if (C.type == T_ATT) {
-          att_finish(P, S, part, s, lane, lpp);
+          if (lpp == 8) att_finish<8>(P, S, part, s, lane, C.t == 0);
+          else att_finish<16>(P, S, part, s, lane, C.t == 0);
         } else if (C.pend) {
           mv_flush<NC>(A, part + (size_t)s * P.ncap * P.vrow_stride + jrow, P.vrow_stride, C.rb, icol);
         }
@@ -459,6 +477,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
         C.t = 0;
         const float* q = hin + att_raw_floats(P);
         const int de = (lane % lpp) * 8;
+        const float qs = P.attn_scale * kLog2e;  // scores in base-2 units
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) {
           S.m[h] = -INFINITY;
@@ -468,8 +487,8 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
             x = ld_f4(q + h * P.D + de);
             y = ld_f4(q + h * P.D + de + 4);
           }
-          S.q[h][0] = x.x; S.q[h][1] = x.y; S.q[h][2] = x.z; S.q[h][3] = x.w;
-          S.q[h][4] = y.x; S.q[h][5] = y.y; S.q[h][6] = y.z; S.q[h][7] = y.w;
+          S.q[h][0] = x.x * qs; S.q[h][1] = x.y * qs; S.q[h][2] = x.z * qs; S.q[h][3] = x.w * qs;
+          S.q[h][4] = y.x * qs; S.q[h][5] = y.y * qs; S.q[h][6] = y.z * qs; S.q[h][7] = y.w * qs;
 #pragma unroll
           for (int e = 0; e < 8; ++e) S.acc[h][e] = 0.f;
         }
@@ -504,7 +523,8 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
       const uint8_t* it = rp + ((uint32_t)k % DEPTH) * kItemBytes;
       const u32x4 w0 = ld_u32x4(it), w1 = ld_u32x4(it + kUnitBytes);
       const bool valid = C.lo + (C.u0 + C.t) * ppi + lane / lpp < C.end;
-      att_item(P, S, w0, w1, valid, lpp);
+      if (lpp == 8) att_item<8>(P, S, w0, w1, valid);
+      else att_item<16>(P, S, w0, w1, valid);
       ++C.t;
       ++k;
       --C.left;
