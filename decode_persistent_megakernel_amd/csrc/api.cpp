@@ -141,7 +141,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   std::vector<DevTask> dt(g.tasks.size());
   std::vector<PackJob> jobs;
   uint64_t off = 0;
-  int max_vrows = 4;
+  int max_vrows = 4, wave_vrows = 4, max_res = 4;
   std::vector<int32_t> ordinal_in_op(g.tasks.size());
   for (const auto& op : g.ops)
     for (int32_t i = op.first; i < op.second; ++i) ordinal_in_op[i] = i - op.first;
@@ -164,6 +164,14 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
     x.kdim = K;
     x.w_off = static_cast<int64_t>(off);
     max_vrows = std::max(max_vrows, n_vrb * kUnitRows);
+    if (t.type == T_O || t.type == T_D) max_res = std::max(max_res, t.row1 - t.row0);
+    {  // rows of the row blocks each stream wave's piece touches (its partial sums)
+      const int items = x.n_units / 2;
+      for (int w = 0; w < kStreams; ++w) {
+        const int i0 = int(int64_t(items) * w / kStreams), i1 = int(int64_t(items) * (w + 1) / kStreams);
+        if (i1 > i0) wave_vrows = std::max(wave_vrows, ((2 * i1 - 1) / KB - (2 * i0) / KB + 1) * kUnitRows);
+      }
+    }
     jobs.push_back(PackJob{x.w_off, t.type, t.layer, t.g, t.row0, t.row1, K, KB, n_vrb});
     off += uint64_t(x.n_units) * kUnitBytes;
   }
@@ -222,16 +230,17 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   int nlm_tasks = 0;
   for (const Task& t : g.tasks) nlm_tasks += t.type == T_LM;
   const int64_t Ncx = g.opts.attn_chunks;
-  const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * max_vrows;
+  const int res_stride = (max_res + 3) & ~3;
+  const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * res_stride;
   const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D;
   const int64_t need_arg = r256(nlm_tasks) * 2;
   const int64_t need_emb = r256(d.hidden / 2 + 1);
-  const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * max_vrows;
+  const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
   const int64_t need_comb = r256(int64_t(G) * Ncx * 2) + r256(int64_t(G) * Ncx * D);
   const int64_t small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
   const int64_t big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
   const int64_t part_floats =
-      (std::max<int64_t>(int64_t(kStreams) * ncap * max_vrows, int64_t(kStreams) * G * (D + 2)) + 3) & ~int64_t(3);
+      (std::max<int64_t>(int64_t(kStreams) * ncap * wave_vrows, int64_t(kStreams) * G * (D + 2)) + 3) & ~int64_t(3);
   const size_t fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
                        size_t(srec_max) * sizeof(StreamRec);
   const size_t lds_max = 160 * 1024;
@@ -240,7 +249,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   // wave already streams near the HBM peak).
   const int64_t item_bytes = 2 * kUnitBytes;
   int64_t ring = std::min<int64_t>(kMaxDepth, (int64_t(lds_max) - int64_t(fixed)) / (kStreams * item_bytes));
-  ring = ring >= 8 ? 8 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
+  ring = ring >= 11 ? 11 : ring >= 8 ? 8 : ring >= 6 ? 6 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
   if (ring < kMinDepth)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: staging needs " + std::to_string(fixed) +
                                      " bytes of LDS, leaving no room for the weight rings");
@@ -375,7 +384,8 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   P.part_floats = static_cast<int32_t>(part_floats);
   P.attn_scale = static_cast<float>(1.0 / std::sqrt(double(d.head_dim)));
   P.kp = kp;
-  P.vrow_stride = max_vrows;
+  P.wave_vrows = wave_vrows;
+  P.res_stride = res_stride;
   P.ncap = ncap;
   P.wpack = d_wpack;
   P.embed = d_embed;

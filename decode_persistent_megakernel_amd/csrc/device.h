@@ -25,7 +25,7 @@ constexpr int kUnitRows = 4;
 constexpr int kCtlWaves = 2;
 constexpr int kStreams = 4;
 constexpr int kThreads = 64 * (kCtlWaves + kStreams);
-constexpr int kMaxDepth = 8;   // ring slots (2 KiB items) per stream wave: 4 or 8
+constexpr int kMaxDepth = 11;  // ring slots (2 KiB items) per stream wave: 4, 6, 8 or 11
 constexpr int kMinDepth = 4;   // fewer cannot hide the copy latency
 constexpr int kMaxCols = 4;    // sequences a matvec task handles
 constexpr int kMaxG = 4;       // query heads per kv head
@@ -83,7 +83,8 @@ struct Params {
   float attn_scale;
   int32_t kp;           // staged floats per column in the small slots (K rounded up to 256)
   int32_t kp_big;       // staged floats per column in the big slot (FFN rounded up to 256)
-  int32_t vrow_stride;  // partial-sum rows per (wave, column)
+  int32_t wave_vrows;   // partial-sum rows per (stream wave, column): the row blocks its piece touches
+  int32_t res_stride;   // staged residual rows per column (projection tasks)
   int32_t ncap;         // staged columns = min(max_batch, kMaxCols)
   int32_t small_floats; // LDS staging slot size (two small slots)
   int32_t big_floats;   // LDS staging slot size for down-projection and merge tasks

@@ -48,9 +48,11 @@ constexpr int kHdr = 32;           // floats of header at the start of a slot
 // LDS control words (ints)
 enum { C_STAGED = 0, C_RETIRED = 1, C_DONE = 2 /* 3 slots */, C_STEPOK = 5, C_ABORT = 6, kCtlWords = 64 };
 // then the waves' wait counters (kWaitWords each), then the stream waves'
-// per-task timestamps for the profile (3 slots x kStreams x {start, first item, end})
+// per-task timestamps for the profile (3 slots x kStreams x {start, first item, end, -})
 constexpr int kProfCtl = kCtlWords + kWaves * kWaitWords;
-static_assert((kProfCtl + 3 * kStreams * 3) * 4 <= kCtlBytes, "control area");
+// then, per slot and stream wave, the row blocks its piece of the task touched
+constexpr int kPieceCtl = kProfCtl + 3 * kStreams * 4;
+static_assert((kPieceCtl + 3 * kStreams * 2) * 4 <= kCtlBytes, "control area");
 // slot header fields (as int)
 enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11 };
 
@@ -352,7 +354,11 @@ __device__ __forceinline__ void waits_put(const Params& P, const Ctx& cx, const 
 }
 
 __device__ __forceinline__ uint32_t* prof_words(const Ctx& cx, int slot, int s) {
-  return reinterpret_cast<uint32_t*>(cx.ctl) + kProfCtl + (slot * kStreams + s) * 3;
+  return reinterpret_cast<uint32_t*>(cx.ctl) + kProfCtl + (slot * kStreams + s) * 4;
+}
+
+__device__ __forceinline__ int* piece_words(const Ctx& cx, int slot, int s) {
+  return cx.ctl + kPieceCtl + (slot * kStreams + s) * 2;
 }
 
 __device__ __forceinline__ bool has_stream(int type) {
@@ -406,8 +412,7 @@ __device__ __forceinline__ bool is_normed(int type) { return type == T_QKV || ty
 __device__ __forceinline__ void stage_matvec_pre(const Params& P, const Ctx& cx, const DevTask& T, int slot,
                                                  StagePre& pre) {
   const int lane = cx.lane;
-  float4* pz = reinterpret_cast<float4*>(part_ptr(cx, slot));
-  for (int k = lane; k < P.part_floats / 4; k += 64) pz[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  (void)slot;
   if (is_normed(T.type)) {
     const uint16_t* gain = P.gains + (T.type == T_LM ? (size_t)P.L * 2 * P.H
                                                      : ((size_t)T.layer * 2 + (T.type == T_GU)) * P.H);
@@ -471,8 +476,8 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
       for (int t = 0; t < nl; ++t) dma16<kAuxCoherent>(src + (size_t)c * K + t * 256 + lane * 4, in + (size_t)c * kp + t * 256);
       wait_all();
       for (int k = K + lane; k < kp; k += 64) in[(size_t)c * kp + k] = 0.f;
-      if (lane < R) res[(size_t)c * P.vrow_stride + lane] = rv;
-      for (int r = 64 + lane; r < R; r += 64) res[(size_t)c * P.vrow_stride + r] = ld_coh(P.x + (size_t)c * P.H + T.row0 + r);
+      if (lane < R) res[(size_t)c * P.res_stride + lane] = rv;
+      for (int r = 64 + lane; r < R; r += 64) res[(size_t)c * P.res_stride + r] = ld_coh(P.x + (size_t)c * P.H + T.row0 + r);
     }
   }
 }
@@ -614,10 +619,29 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
 // retirer (wave 1)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float part_sum(const Params& P, const float* part, int c, int vrow) {
+// Row blocks [a[w], b[w]] that stream wave w's piece of a matvec task touches
+// (b < a: an empty piece); its partial sums hold rows of those blocks only.
+struct PieceRows {
+  int a[kStreams], b[kStreams];
+};
+__device__ __forceinline__ PieceRows piece_rows(const Ctx& cx, int slot) {
+  PieceRows pr;
+#pragma unroll
+  for (int w = 0; w < kStreams; ++w) {
+    const int* pw = piece_words(cx, slot, w);
+    pr.a[w] = lds_ld(pw);
+    pr.b[w] = lds_ld(pw + 1);
+  }
+  return pr;
+}
+// Sum of the stream waves' partials of row vrow (task-relative) in column c.
+__device__ __forceinline__ float part_sum(const Params& P, const PieceRows& pr, const float* part, int c, int vrow) {
+  const int rb = vrow >> 2;
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < kStreams; ++w) s += part[((size_t)w * P.ncap + c) * P.vrow_stride + vrow];
+  for (int w = 0; w < kStreams; ++w)
+    if (rb >= pr.a[w] && rb <= pr.b[w])
+      s += part[((size_t)w * P.ncap + c) * P.wave_vrows + (rb - pr.a[w]) * 4 + (vrow & 3)];
   return s;
 }
 
@@ -626,13 +650,14 @@ __device__ __forceinline__ void retire_matvec(const Params& P, const Ctx& cx, co
   const float* res = hdr + kHdr + (size_t)P.ncap * slot_kp(P, slot);
   const float* part = part_ptr(cx, slot);
   const int lane = cx.lane, ncols = P.batch, R = T.row1 - T.row0;
+  const PieceRows pr = piece_rows(cx, slot);
   if (T.type == T_LM) {
     const bool last = step == P.n_steps - 1;
     for (int c = 0; c < ncols; ++c) {
       float best = -INFINITY;
       int bi = 0x7fffffff;
       for (int r = lane; r < R; r += 64) {
-        const float v = part_sum(P, part, c, r) * hdr[c];
+        const float v = part_sum(P, pr, part, c, r) * hdr[c];
         if (last && P.logits_out) P.logits_out[(size_t)c * P.V + T.row0 + r] = v;
         if (v > best || (v == best && T.row0 + r < bi)) { best = v; bi = T.row0 + r; }
       }
@@ -648,17 +673,17 @@ __device__ __forceinline__ void retire_matvec(const Params& P, const Ctx& cx, co
     const int c = idx / R, r = idx - c * R;
     switch (T.type) {
       case T_QKV:
-        st_coh(P.qkv + ((size_t)c * P.Hkv + T.g) * (P.G + 2) * P.D + T.row0 + r, part_sum(P, part, c, r) * hdr[c]);
+        st_coh(P.qkv + ((size_t)c * P.Hkv + T.g) * (P.G + 2) * P.D + T.row0 + r, part_sum(P, pr, part, c, r) * hdr[c]);
         break;
       case T_GU: {
         const int vr = 8 * (r >> 2) + (r & 3);
-        const float gt = part_sum(P, part, c, vr) * hdr[c];
-        const float up = part_sum(P, part, c, vr + 4) * hdr[c];
+        const float gt = part_sum(P, pr, part, c, vr) * hdr[c];
+        const float up = part_sum(P, pr, part, c, vr + 4) * hdr[c];
         st_coh(P.mlp + (size_t)c * P.F + T.row0 + r, gt / (1.0f + expf(-gt)) * up);
         break;
       }
       default:  // O, D: residual add
-        st_coh(P.x + (size_t)c * P.H + T.row0 + r, res[(size_t)c * P.vrow_stride + r] + part_sum(P, part, c, r));
+        st_coh(P.x + (size_t)c * P.H + T.row0 + r, res[(size_t)c * P.res_stride + r] + part_sum(P, pr, part, c, r));
         break;
     }
   }
@@ -964,10 +989,18 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   extern "C" __global__ void __launch_bounds__(kThreads) mk_oplaunch_b##NC##_d##DEPTH(Params P, int first) { \
     run<NC, DEPTH>(P, blockIdx.x, first + blockIdx.x);                                                 \
   }
+MK_KERNELS(1, 11)
+MK_KERNELS(2, 11)
+MK_KERNELS(3, 11)
+MK_KERNELS(4, 11)
 MK_KERNELS(1, 8)
 MK_KERNELS(2, 8)
 MK_KERNELS(3, 8)
 MK_KERNELS(4, 8)
+MK_KERNELS(1, 6)
+MK_KERNELS(2, 6)
+MK_KERNELS(3, 6)
+MK_KERNELS(4, 6)
 MK_KERNELS(1, 4)
 MK_KERNELS(2, 4)
 MK_KERNELS(3, 4)
@@ -976,13 +1009,18 @@ MK_KERNELS(4, 4)
 
 typedef void (*PersistentFn)(Params);
 typedef void (*OpFn)(Params, int);
-// [ring depth 8, 4][columns - 1]
-__device__ __host__ constexpr int depth_index(int depth) { return depth >= 8 ? 0 : 1; }
-static const PersistentFn kPersistent[2][kMaxCols] = {
+// [ring depth 11, 8, 6, 4][columns - 1]
+constexpr int kDepths = 4;
+__device__ __host__ constexpr int depth_index(int depth) { return depth >= 11 ? 0 : depth >= 8 ? 1 : depth >= 6 ? 2 : 3; }
+static const PersistentFn kPersistent[kDepths][kMaxCols] = {
+    {mk_persistent_b1_d11, mk_persistent_b2_d11, mk_persistent_b3_d11, mk_persistent_b4_d11},
     {mk_persistent_b1_d8, mk_persistent_b2_d8, mk_persistent_b3_d8, mk_persistent_b4_d8},
+    {mk_persistent_b1_d6, mk_persistent_b2_d6, mk_persistent_b3_d6, mk_persistent_b4_d6},
     {mk_persistent_b1_d4, mk_persistent_b2_d4, mk_persistent_b3_d4, mk_persistent_b4_d4}};
-static const OpFn kOplaunch[2][kMaxCols] = {
+static const OpFn kOplaunch[kDepths][kMaxCols] = {
+    {mk_oplaunch_b1_d11, mk_oplaunch_b2_d11, mk_oplaunch_b3_d11, mk_oplaunch_b4_d11},
     {mk_oplaunch_b1_d8, mk_oplaunch_b2_d8, mk_oplaunch_b3_d8, mk_oplaunch_b4_d8},
+    {mk_oplaunch_b1_d6, mk_oplaunch_b2_d6, mk_oplaunch_b3_d6, mk_oplaunch_b4_d6},
     {mk_oplaunch_b1_d4, mk_oplaunch_b2_d4, mk_oplaunch_b3_d4, mk_oplaunch_b4_d4}};
 
 // ---------------------------------------------------------------------------
@@ -1041,7 +1079,7 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack(const PackJob* jobs, c
 // ---------------------------------------------------------------------------
 
 hipError_t set_lds_limit(int bytes) {
-  for (int d = 0; d < 2; ++d)
+  for (int d = 0; d < kDepths; ++d)
     for (int c = 0; c < kMaxCols; ++c) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistent[d][c]),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);

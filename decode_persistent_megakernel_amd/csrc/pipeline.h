@@ -62,7 +62,8 @@ template <int DEPTH>
 __device__ __forceinline__ void wait_item(int younger) {
   cbar();
   if (younger >= DEPTH - 1) wait_vmcnt<2 * (DEPTH - 1)>();
-  else if (younger >= DEPTH / 2) wait_vmcnt<DEPTH>();
+  else if (younger >= DEPTH - 2) wait_vmcnt<2 * (DEPTH - 2)>();
+  else if (younger >= DEPTH / 2) wait_vmcnt<2 * (DEPTH / 2)>();
   else if (younger >= 2) wait_vmcnt<4>();
   else if (younger == 1) wait_vmcnt<2>();
   else wait_vmcnt<0>();
@@ -91,7 +92,15 @@ struct Fetch {
   int ppi;            // attention: positions per item
   const uint8_t* src; // matvec: this lane's 16 bytes of the next item; attention: the (layer, b, g) K rows
   int issued;         // items copied so far (all tasks)
+  uint32_t soff;      // ring byte offset of the slot of item `issued`
 };
+
+// Ring slots are visited in order: the next slot's byte offset.
+template <int DEPTH>
+__device__ __forceinline__ uint32_t next_slot_off(uint32_t off) {
+  off += kItemBytes;
+  return off == (uint32_t)DEPTH * kItemBytes ? 0u : off;
+}
 
 // Move to the next task (in queue order, across steps) that has items for
 // wave s. A matvec piece is whole items; an attention piece is a run of
@@ -154,7 +163,7 @@ __device__ __forceinline__ void fetch_upto(const Params& P, const Ctx& cx, int s
       fetch_next_task(P, cx, s, F);
       if (F.done) return;
     }
-    const uint32_t dst = ring + ((uint32_t)F.issued % DEPTH) * kItemBytes;
+    const uint32_t dst = ring + F.soff;
     if (!F.kv) {
       copy_nt(F.src, dst);
       copy_nt(F.src + kUnitBytes, dst + kUnitBytes);
@@ -169,6 +178,7 @@ __device__ __forceinline__ void fetch_upto(const Params& P, const Ctx& cx, int s
     }
     ++F.issued;
     ++F.t;
+    F.soff = next_slot_off<DEPTH>(F.soff);
   }
 }
 
@@ -181,6 +191,8 @@ struct Comp {
   int slot, type;  // type -1: none
   int left;        // items of this wave left in the task
   int rb, kb, KB;  // matvec: row block and column block of the next item, column blocks
+  int rb0;         // matvec: first row block of this wave's piece (its partial sums start there)
+  int k0;          // items consumed before the task (profile)
   bool pend;       // matvec: sums of an unfinished row block are held
   int t, lo, end;  // attention: next block, cached positions [lo, end) of the chunk
   int u0;          // attention: first block of this wave
@@ -204,8 +216,53 @@ __device__ __forceinline__ float dot8(const u32x4 w, const float4 x, const float
   return a + b;
 }
 
-// The row sums of row block rb, reduced over the 16 lanes of each row, as
-// this wave's partial sums. Every lane of row j holds the sum and all of them
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 to_f4(const f32x4 v) { return make_float4(v.x, v.y, v.z, v.w); }
+
+// One column's LDS operands of two items at once: both items' weight units and
+// the activations of their column blocks, all twelve reads issued before one
+// wait (inside the block, so no read is in flight when it ends). w: the items'
+// slots (this lane's 16 bytes); ha, hb: the column blocks' activations (this
+// lane's first float).
+__device__ __forceinline__ void lds_two_items(uint32_t i0, uint32_t i1, uint32_t ha, uint32_t hb, u32x4 (&w)[4],
+                                              f32x4 (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %12 offset:1024\n\t"
+      "ds_read_b128 %2, %13\n\t"
+      "ds_read_b128 %3, %13 offset:1024\n\t"
+      "ds_read_b128 %4, %14\n\t"
+      "ds_read_b128 %5, %14 offset:256\n\t"
+      "ds_read_b128 %6, %14 offset:512\n\t"
+      "ds_read_b128 %7, %14 offset:768\n\t"
+      "ds_read_b128 %8, %15\n\t"
+      "ds_read_b128 %9, %15 offset:256\n\t"
+      "ds_read_b128 %10, %15 offset:512\n\t"
+      "ds_read_b128 %11, %15 offset:768\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
+        "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+      : "v"(i0), "v"(i1), "v"(ha), "v"(hb)
+      : "memory");
+}
+
+// The same for one item: its two weight units and its column blocks' activations.
+__device__ __forceinline__ void lds_one_item(uint32_t i0, uint32_t ha, u32x4 (&w)[2], f32x4 (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:1024\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %7 offset:256\n\t"
+      "ds_read_b128 %4, %7 offset:512\n\t"
+      "ds_read_b128 %5, %7 offset:768\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(i0), "v"(ha)
+      : "memory");
+}
+
+// The row sums of row block rb (counted from the piece's first), reduced over
+// the 16 lanes of each row, as this wave's partial sums. Every lane of row j holds the sum and all of them
 // store it to row j's word: no lane-dependent branch in the stream loop (a
 // divergent branch there would make the loop's own control divergent).
 template <int NC>
@@ -303,39 +360,52 @@ __device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* 
   }
 }
 
-// Items of a matvec piece, two at a time while both have landed, refilling
-// the ring from the same copy task; returns to the caller (which owns the
-// slow paths) when the compute task ends, the next item is not copied yet, or
-// the copy cursor reaches the end of its task.
+// Items of a matvec piece, two at a time while both have been copied,
+// refilling the ring from the same copy task; returns to the caller (which
+// owns the slow paths) when the compute task ends, the next item is not copied
+// yet, or the copy cursor reaches the end of its task. koff: ring byte offset
+// of item k's slot.
 template <int DEPTH, int NC>
-__device__ __forceinline__ void matvec_run(const Params& P, Comp& C, Fetch& F, int& k, uint32_t ring,
-                                           const uint8_t* rp, const float* hin, int kp, float* pout, int icol,
-                                           Acc<NC>& A, uint32_t& t_first, bool prof) {
+__device__ __forceinline__ void matvec_run(const Params& P, Comp& C, Fetch& F, int& k, uint32_t& koff,
+                                           uint32_t ring, const uint8_t* rp, const float* hin, int kp, float* pout,
+                                           int icol, Acc<NC>& A, uint32_t& t_first, bool prof) {
   const int KB = C.KB;
   const float* h = hin + icol * 4;
+  if (prof && t_first == 0 && F.issued > k) {
+    wait_item<DEPTH>(F.issued - k - 1);
+    t_first = rfl((uint32_t)wall_clock64());
+  }
   for (;;) {
     const int ready = F.issued - k;
     if (ready >= 2 && C.left >= 2) {
       wait_item<DEPTH>(ready - 2);
-      if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
-      const uint8_t* i0 = rp + ((uint32_t)k % DEPTH) * kItemBytes;
-      const uint8_t* i1 = rp + ((uint32_t)(k + 1) % DEPTH) * kItemBytes;
-      const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
-      const u32x4 w2 = ld_u32x4(i1), w3 = ld_u32x4(i1 + kUnitBytes);
+      const uint32_t k1off = next_slot_off<DEPTH>(koff);
+      const uint8_t* i0 = rp + koff;
+      const uint8_t* i1 = rp + k1off;
       const int kb1 = C.kb + 2 == KB ? 0 : C.kb + 2;
       float d0[NC], d1[NC];
+      if constexpr (NC == 1) {
+        u32x4 w[4];
+        f32x4 a[8];
+        lds_two_items(lds_addr(i0), lds_addr(i1), lds_addr(h + C.kb * kUnitCols), lds_addr(h + kb1 * kUnitCols), w, a);
+        d0[0] = dot8(w[0], to_f4(a[0]), to_f4(a[1])) + dot8(w[1], to_f4(a[2]), to_f4(a[3]));
+        d1[0] = dot8(w[2], to_f4(a[4]), to_f4(a[5])) + dot8(w[3], to_f4(a[6]), to_f4(a[7]));
+      } else {
+        const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
+        const u32x4 w2 = ld_u32x4(i1), w3 = ld_u32x4(i1 + kUnitBytes);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float* ha = h + c * kp + C.kb * kUnitCols;
-        const float* hb = h + c * kp + kb1 * kUnitCols;
-        d0[c] = dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
-        d1[c] = dot8(w2, ld_f4(hb), ld_f4(hb + 64)) + dot8(w3, ld_f4(hb + kUnitCols), ld_f4(hb + kUnitCols + 64));
+        for (int c = 0; c < NC; ++c) {
+          const float* ha = h + c * kp + C.kb * kUnitCols;
+          const float* hb = h + c * kp + kb1 * kUnitCols;
+          d0[c] = dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
+          d1[c] = dot8(w2, ld_f4(hb), ld_f4(hb + 64)) + dot8(w3, ld_f4(hb + kUnitCols), ld_f4(hb + kUnitCols + 64));
+        }
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) A.a[c] += d0[c];
       C.kb += 2;
       if (C.kb == KB) {
-        mv_flush<NC>(A, pout, P.vrow_stride, C.rb, icol);
+        mv_flush<NC>(A, pout, P.wave_vrows, C.rb - C.rb0, icol);
         C.kb = 0;
         ++C.rb;
       }
@@ -344,46 +414,69 @@ __device__ __forceinline__ void matvec_run(const Params& P, Comp& C, Fetch& F, i
       C.kb += 2;
       C.pend = true;
       if (C.kb == KB) {
-        mv_flush<NC>(A, pout, P.vrow_stride, C.rb, icol);
+        mv_flush<NC>(A, pout, P.wave_vrows, C.rb - C.rb0, icol);
         C.kb = 0;
         ++C.rb;
         C.pend = false;
       }
       k += 2;
+      koff = next_slot_off<DEPTH>(k1off);
       C.left -= 2;
-    } else if (ready >= 1) {
+      // steady state: the two slots just read take the copy task's next two items
+      if (!F.kv && F.t + 2 <= F.n && F.issued + 2 <= k + DEPTH) {
+        const uint32_t d0s = ring + F.soff;
+        const uint32_t s1 = next_slot_off<DEPTH>(F.soff);
+        const uint32_t d1s = ring + s1;
+        copy_nt(F.src, d0s);
+        copy_nt(F.src + kUnitBytes, d0s + kUnitBytes);
+        copy_nt(F.src + kItemBytes, d1s);
+        copy_nt(F.src + kItemBytes + kUnitBytes, d1s + kUnitBytes);
+        F.src += 2 * kItemBytes;
+        F.issued += 2;
+        F.t += 2;
+        F.soff = next_slot_off<DEPTH>(s1);
+        continue;
+      }
+    } else if (ready >= 1 && C.left >= 1) {
       wait_item<DEPTH>(ready - 1);
-      if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
-      const uint8_t* i0 = rp + ((uint32_t)k % DEPTH) * kItemBytes;
-      const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
+      const uint8_t* i0 = rp + koff;
+      if constexpr (NC == 1) {
+        u32x4 w[2];
+        f32x4 a[4];
+        lds_one_item(lds_addr(i0), lds_addr(h + C.kb * kUnitCols), w, a);
+        A.a[0] += dot8(w[0], to_f4(a[0]), to_f4(a[1])) + dot8(w[1], to_f4(a[2]), to_f4(a[3]));
+      } else {
+        const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float* ha = h + c * kp + C.kb * kUnitCols;
-        A.a[c] += dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
+        for (int c = 0; c < NC; ++c) {
+          const float* ha = h + c * kp + C.kb * kUnitCols;
+          A.a[c] += dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
+        }
       }
       C.kb += 2;
       C.pend = true;
       if (C.kb == KB) {
-        mv_flush<NC>(A, pout, P.vrow_stride, C.rb, icol);
+        mv_flush<NC>(A, pout, P.wave_vrows, C.rb - C.rb0, icol);
         C.kb = 0;
         ++C.rb;
         C.pend = false;
       }
       k += 1;
+      koff = next_slot_off<DEPTH>(koff);
       C.left -= 1;
     } else {
       return;
     }
     // refill the read slots from the current copy task (weights only)
     if (F.kv) return;
-    wait_lgkm();
     while (F.issued < k + DEPTH && F.t < F.n) {
-      const uint32_t dst = ring + ((uint32_t)F.issued % DEPTH) * kItemBytes;
+      const uint32_t dst = ring + F.soff;
       copy_nt(F.src, dst);
       copy_nt(F.src + kUnitBytes, dst + kUnitBytes);
       F.src += kItemBytes;
       ++F.issued;
       ++F.t;
+      F.soff = next_slot_off<DEPTH>(F.soff);
     }
     if (C.left == 0 || F.issued < k + DEPTH) return;
   }
@@ -423,6 +516,8 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
   Acc<NC> A;
   AttState S;
   uint32_t t_first = 0;
+  uint32_t koff = 0;  // ring byte offset of item k's slot
+  F.soff = 0;
 
   for (;;) {
     // refill every slot whose item has been read
@@ -435,8 +530,12 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
         if (C.type == T_ATT) {
           if (lpp == 8) att_finish<8>(P, S, part, s, lane, C.t == 0);
           else att_finish<16>(P, S, part, s, lane, C.t == 0);
-        } else if (C.pend) {
-          mv_flush<NC>(A, part + (size_t)s * P.ncap * P.vrow_stride + jrow, P.vrow_stride, C.rb, icol);
+        } else {
+          if (C.pend) mv_flush<NC>(A, part + (size_t)s * P.ncap * P.wave_vrows + jrow, P.wave_vrows, C.rb - C.rb0, icol);
+          // the row blocks this piece touched (b < a: none), for the retirer's sums
+          int* pr = piece_words(cx, C.slot, s);
+          pr[0] = C.rb0;
+          pr[1] = C.k0 == k ? C.rb0 - 1 : (C.pend ? C.rb : C.rb - 1);
         }
         if (prof) {
           uint32_t* pw = prof_words(cx, C.slot, s);
@@ -462,6 +561,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
         waits_add(wt, 2, s0);
       }
       t_first = 0;
+      C.k0 = k;
       if (prof) prof_words(cx, C.slot, s)[0] = rfl((uint32_t)wall_clock64());
       hin = slot_ptr(cx, C.slot) + kHdr;
       part = part_ptr(cx, C.slot);
@@ -499,6 +599,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
         C.left = i1 - i0;
         C.KB = kq & 0xffff;
         C.rb = (2 * i0) / C.KB;
+        C.rb0 = C.rb;
         C.kb = 2 * i0 - C.rb * C.KB;
         C.pend = false;
         kp = slot_kp(P, C.slot);
@@ -520,17 +621,18 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
     if (C.type == T_ATT) {
       wait_item<DEPTH>(F.issued - k - 1);
       if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
-      const uint8_t* it = rp + ((uint32_t)k % DEPTH) * kItemBytes;
+      const uint8_t* it = rp + koff;
       const u32x4 w0 = ld_u32x4(it), w1 = ld_u32x4(it + kUnitBytes);
       const bool valid = C.lo + (C.u0 + C.t) * ppi + lane / lpp < C.end;
       if (lpp == 8) att_item<8>(P, S, w0, w1, valid);
       else att_item<16>(P, S, w0, w1, valid);
       ++C.t;
       ++k;
+      koff = next_slot_off<DEPTH>(koff);
       --C.left;
     } else {
-      matvec_run<DEPTH, NC>(P, C, F, k, ring, rp, hin, kp, part + (size_t)s * P.ncap * P.vrow_stride + jrow, icol,
-                            A, t_first, prof);
+      matvec_run<DEPTH, NC>(P, C, F, k, koff, ring, rp, hin, kp, part + (size_t)s * P.ncap * P.wave_vrows + jrow,
+                            icol, A, t_first, prof);
     }
   }
   wait_all();
