@@ -625,13 +625,14 @@ struct PieceRows {
   int a[kStreams], b[kStreams];
 };
 __device__ __forceinline__ PieceRows piece_rows(const Ctx& cx, int slot) {
+  static_assert(kStreams == 4, "two 16-byte reads hold the four waves' ranges");
+  const int4 q0 = *reinterpret_cast<const int4*>(piece_words(cx, slot, 0));
+  const int4 q1 = *reinterpret_cast<const int4*>(piece_words(cx, slot, 2));
   PieceRows pr;
-#pragma unroll
-  for (int w = 0; w < kStreams; ++w) {
-    const int* pw = piece_words(cx, slot, w);
-    pr.a[w] = lds_ld(pw);
-    pr.b[w] = lds_ld(pw + 1);
-  }
+  pr.a[0] = __builtin_amdgcn_readfirstlane(q0.x); pr.b[0] = __builtin_amdgcn_readfirstlane(q0.y);
+  pr.a[1] = __builtin_amdgcn_readfirstlane(q0.z); pr.b[1] = __builtin_amdgcn_readfirstlane(q0.w);
+  pr.a[2] = __builtin_amdgcn_readfirstlane(q1.x); pr.b[2] = __builtin_amdgcn_readfirstlane(q1.y);
+  pr.a[3] = __builtin_amdgcn_readfirstlane(q1.z); pr.b[3] = __builtin_amdgcn_readfirstlane(q1.w);
   return pr;
 }
 // Sum of the stream waves' partials of row vrow (task-relative) in column c.

@@ -216,23 +216,22 @@ def test_watchdog_recovers_from_dropped_signal():
     ss.close()
 
 
-@pytest.mark.slow
-def test_1b_full_size_sampled():
-    """Llama-3.2-1B shape at full size, in the launch configuration the bench
-    times (default graph, mk_generate): prompt prefill, then teacher-forced
-    logits at the last prompt position and two decode steps vs the oracle, then
-    a 32-step greedy run checked token by token against the oracle's argmax of
-    the same prefix (ties within 1e-4 accepted either way)."""
-    wl = workload.config(1)
-    ss = session(1)
-    om = oracle_model(1, cache=False)
-    prompt = workload.make_prompt(wl)[0]
+def full_size_sampled(cfg: int, prefix: int, what: str):
+    """A full-size shape in the launch configuration the benchmark times
+    (default graph, megakernel): the first `prefix` prompt tokens fed one step
+    each, logits at the last of them checked against the oracle's no-cache
+    forward, then two decode steps checked against the oracle's incremental
+    decode, each with the greedy token."""
+    wl = workload.config(cfg)
+    ss = session(cfg)
+    om = oracle_model(cfg, cache=False)
+    prompt = workload.make_prompt(wl)[0][:prefix]
     P = len(prompt)
     for p in range(P - 1):
         ss.decode_step([int(prompt[p])], [p], logits=False)
     full, ks, vs = om.forward_full(prompt)
     nxt, lg = ss.decode_step([int(prompt[-1])], [P - 1])
-    check_logits(lg[0].double().cpu().numpy(), full[P - 1], "1B last prompt position")
+    check_logits(lg[0].double().cpu().numpy(), full[P - 1], f"{what} last prompt position")
     # oracle state = the forward's cache
     st = om.new_state(1, wl.max_seq)
     st.kcache[:, 0, :, :P] = ks
@@ -242,8 +241,21 @@ def test_1b_full_size_sampled():
     for k in range(2):
         ref = om.decode_step(st, [tok], [P + k])[0]
         nxt, lg = ss.decode_step([tok], [P + k])
-        check_logits(lg[0].double().cpu().numpy(), ref, f"1B decode step {k}")
+        check_logits(lg[0].double().cpu().numpy(), ref, f"{what} decode step {k}")
         tok = int(np.argmax(ref))
         assert int(nxt[0]) == tok
     ss.check()
     ss.close()
+
+
+@pytest.mark.slow
+def test_1b_full_size_sampled():
+    """Llama-3.2-1B shape, the whole 39-token prompt."""
+    full_size_sampled(1, 39, "1B")
+
+
+@pytest.mark.slow
+def test_8b_full_size_sampled():
+    """Llama-3-8B shape (hidden 4096, head dim 128, untied LM head, the
+    smallest ring depth the LDS leaves room for): the first 8 prompt tokens."""
+    full_size_sampled(2, 8, "8B")
