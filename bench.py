@@ -128,20 +128,26 @@ def main():
     from decode_persistent_megakernel_amd.session import Session
 
     wl = workload.config(args.config)
-    if wl.batch != 1 or wl.kv_prefill != "none":
-        log("note: non-default workload")
+    if wl.batch != 1:
+        raise SystemExit(f"bench.py: the {wl.name} workload (batch {wl.batch}) is not supported by this build")
     torch.cuda.set_device(0)
     t = time.time()
     w = workload.make_weights(wl)
+    kv = workload.make_prefill(wl)
     log(f"weights generated in {time.time() - t:.1f}s")
-    ss = Session(wl.shape, w, wl.batch, wl.max_seq)
-    log(f"model loaded: {ss.n_tasks} tasks, {ss.num_cus} CUs, packed weights {ss.packed_bytes / 1e9:.3f} GB")
-    prompt = workload.make_prompt(wl)[0]
+    ss = Session(wl.shape, w, wl.batch, wl.max_seq, kv=kv)
+    kv = None
+    log(f"model loaded: {ss.n_tasks} tasks, {ss.num_cus} CUs, packed weights {ss.packed_bytes / 1e9:.3f} GB, "
+        f"ring {ss.ring_slots} slots, LDS {ss.lds_bytes} B")
+    if wl.kv_prefill == "none":
+        prompt = workload.make_prompt(wl)[0]
+    else:  # the cache holds positions 0 .. kv_len-1; decoding starts after them
+        prompt = [0] * int(workload.kv_lengths(wl)[0]) + [int(workload.make_prompt(wl)[0][0])]
     P = len(prompt)
     K, W = args.steps, args.warmup
     if P - 1 + max(K, W) > wl.max_seq:
         raise SystemExit("steps exceed max_seq")
-    for p in range(P - 1):
+    for p in range(P - 1 if wl.kv_prefill == "none" else 0):
         ss.decode_step([int(prompt[p])], [p], mode=MK_MODE_OPLAUNCH, logits=False)
     torch.cuda.synchronize()
     ss.check()
@@ -200,12 +206,13 @@ def main():
         "ms_per_step": round(ms / K, 6), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "global_batch": wl.batch, "seq_len": P - 1 + K,
-                   "prompt": P, "decode_steps": K, "parallelism": "none (1 GPU)"},
+                   "prompt": P if wl.kv_prefill == "none" else 1, "kv_prefilled": P - 1 if wl.kv_prefill != "none" else 0,
+                   "decode_steps": K, "parallelism": "none (1 GPU)"},
         "achieved_gbs": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": recorded_traffic(wl.name, K, wl.batch),
-                     "kernel": "mk_persistent", "launch_ms": round(ms, 4),
+                     "kernel": f"mk_persistent_b1_d{ss.ring_slots}", "launch_ms": round(ms, 4),
                      "bytes_per_launch": bytes_launch},
         "oplaunch_baseline_us_per_token": round(us_b, 3),
         "cpu_baseline": cpu,

@@ -520,11 +520,14 @@ int mk_set_wait_counters(mk_model* m, void* d_buf, size_t bytes) {
   return MK_OK;
 }
 
-int mk_model_info(const mk_model* m, uint64_t* packed_weight_bytes, int32_t* num_cus, int32_t* n_tasks) {
+int mk_model_info(const mk_model* m, uint64_t* packed_weight_bytes, int32_t* num_cus, int32_t* n_tasks,
+                  int32_t* ring_slots, int32_t* lds_bytes) {
   if (!m) return fail(MK_EINVAL, "mk_model_info: NULL model");
   if (packed_weight_bytes) *packed_weight_bytes = m->packed_bytes;
   if (num_cus) *num_cus = m->g.opts.num_cus;
   if (n_tasks) *n_tasks = static_cast<int32_t>(m->g.tasks.size());
+  if (ring_slots) *ring_slots = m->base.ring_slots;
+  if (lds_bytes) *lds_bytes = m->lds_bytes;
   return MK_OK;
 }
 

@@ -22,6 +22,8 @@ class Session:
                  opts: Optional[GraphOpts] = None, kv=None, keep_weights: bool = False):
         import torch
         self.torch = torch
+        self.model = 0
+        self.graph = 0
         self.shape = shape
         self.max_batch, self.max_seq = max_batch, max_seq
         dev = torch.device("cuda", torch.cuda.current_device())
@@ -40,7 +42,7 @@ class Session:
             assert tuple(self.k.shape) == kvshape
         self.model = mk_load_weights(self.graph, w, self.k, self.v, shape.n_layers)
         self.weights = w if keep_weights else None
-        self.packed_bytes, self.num_cus, _ = mk_model_info(self.model)
+        self.packed_bytes, self.num_cus, _, self.ring_slots, self.lds_bytes = mk_model_info(self.model)
         self.tok = torch.zeros(max_batch, dtype=torch.int32, device=dev)
         self.pos = torch.zeros(max_batch, dtype=torch.int32, device=dev)
         self.next = torch.zeros(max_batch, dtype=torch.int32, device=dev)

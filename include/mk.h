@@ -182,10 +182,16 @@ int mk_set_profile_buffer(mk_model *m, void *d_buf, size_t bytes);
  * NULL disables. */
 int mk_set_wait_counters(mk_model *m, void *d_buf, size_t bytes);
 
-/* Device bytes the model reads per step for its weights (packed copy, padding
- * included) -- the numerator of the roofline. */
+/* Facts about a loaded model (each pointer may be NULL):
+ *   packed_weight_bytes  device bytes of the packed weight copy (padding
+ *                        included);
+ *   num_cus, n_tasks     workgroups of the persistent launch, tasks per step;
+ *   ring_slots           2 KiB ring slots per stream wave (the kernel variant
+ *                        mk_persistent_b<batch>_d<ring_slots> runs a call);
+ *   lds_bytes            dynamic LDS per workgroup.
+ * MK_EINVAL for a NULL model. */
 int mk_model_info(const mk_model *m, uint64_t *packed_weight_bytes, int32_t *num_cus,
-                  int32_t *n_tasks);
+                  int32_t *n_tasks, int32_t *ring_slots, int32_t *lds_bytes);
 
 void mk_free_model(mk_model *m);
 

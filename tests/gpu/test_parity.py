@@ -23,14 +23,14 @@ GOLDEN = os.path.join(os.path.dirname(os.path.dirname(__file__)), "golden", "tin
 MAX_ABS, REL_L2 = 3e-2, 1e-2
 
 
-def session(cfg, gains="ones", opts=None, max_batch=None, max_seq=None, shape=None, w=None):
+def session(cfg, gains="ones", opts=None, max_batch=None, max_seq=None, shape=None, w=None, kv=None):
     import decode_persistent_megakernel_amd.session as S
     wl = workload.config(cfg)
     if w is None:
         _, w = weights(cfg, gains)
     print(f"[session] cfg={cfg} gains={gains} opts={opts and tuple(getattr(opts, f[0]) for f in opts._fields_)}",
           flush=True)
-    return S.Session(shape or wl.shape, w, max_batch or wl.batch, max_seq or wl.max_seq, opts)
+    return S.Session(shape or wl.shape, w, max_batch or wl.batch, max_seq or wl.max_seq, opts, kv=kv)
 
 
 def check_logits(gpu: np.ndarray, ref: np.ndarray, what: str):
@@ -259,3 +259,38 @@ def test_8b_full_size_sampled():
     """Llama-3-8B shape (hidden 4096, head dim 128, untied LM head, the
     smallest ring depth the LDS leaves room for): the first 8 prompt tokens."""
     full_size_sampled(2, 8, "8B")
+
+
+@pytest.mark.slow
+def test_long_context_sampled():
+    """Llama-3.2-1B shape with 32768 KV positions prefilled (synthetic bf16
+    N(0,1), read as already rotated): two decode steps from position 32768,
+    logits and greedy token against the oracle over the same cache."""
+    import torch
+    wl = workload.config(3)
+    L0 = int(workload.kv_lengths(wl)[0])
+    kc, vc = workload.make_prefill(wl)
+    ss = session(3, kv=(kc, vc))
+    om = oracle_model(3, cache=False)
+    st = om.new_state(1, wl.max_seq)
+    st.kcache[:, 0] = kc[:, 0].contiguous().view(torch.int16).numpy().view(np.uint16)
+    st.vcache[:, 0] = vc[:, 0].contiguous().view(torch.int16).numpy().view(np.uint16)
+    del kc, vc
+    tok = int(workload.make_prompt(wl)[0][0])
+    for k in range(2):
+        ref = om.decode_step(st, [tok], [L0 + k])[0]
+        nxt, lg = ss.decode_step([tok], [L0 + k])
+        check_logits(lg[0].double().cpu().numpy(), ref, f"long context step {k}")
+        tok = int(np.argmax(ref))
+        assert int(nxt[0]) == tok
+    ss.check()
+    ss.close()
+
+
+def test_batch_above_four_is_refused():
+    """Batch 16 (the 8B batch workload) needs the MFMA task bodies, which are
+    not built: loading refuses it with MK_EUNSUPPORTED instead of running."""
+    import decode_persistent_megakernel_amd as mk
+    with pytest.raises(mk.MKError) as e:
+        session(0, max_batch=16)
+    assert e.value.code == -5
