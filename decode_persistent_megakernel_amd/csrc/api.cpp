@@ -232,7 +232,9 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   const int64_t Ncx = g.opts.attn_chunks;
   const int res_stride = (max_res + 3) & ~3;
   const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * res_stride;
-  const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D;
+  // attention: raw q|k|v, rotated q, new k and v, their bf16 bits, then the
+  // stream waves' partials (acc[wave][head][D], then (m, l) per wave and head)
+  const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D + int64_t(kStreams) * G * (D + 2);
   const int64_t need_arg = r256(nlm_tasks) * 2;
   const int64_t need_emb = r256(d.hidden / 2 + 1);
   const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
@@ -240,7 +242,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   const int64_t small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
   const int64_t big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
   const int64_t part_floats =
-      (std::max<int64_t>(int64_t(kStreams) * ncap * wave_vrows, int64_t(kStreams) * G * (D + 2)) + 3) & ~int64_t(3);
+      (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
   const size_t fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
                        size_t(srec_max) * sizeof(StreamRec);
   const size_t lds_max = 160 * 1024;

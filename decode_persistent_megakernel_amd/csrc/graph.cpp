@@ -81,7 +81,7 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   r.lm_tasks = cap(o.lm_tasks ? o.lm_tasks : N, d.vocab);
   r.attn_chunks = o.attn_chunks
                       ? o.attn_chunks
-                      : std::max(1, std::min(N / (B * Hkv), std::max(1, d.max_seq / 16)));
+                      : std::max(1, std::min(N / (B * Hkv), std::max(1, d.max_seq / 1024)));
   const int32_t Nc = r.attn_chunks;
 
   Graph& g = *out;

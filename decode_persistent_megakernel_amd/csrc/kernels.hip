@@ -486,6 +486,11 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
 // up to 256 floats), rotated queries [G][D], new key [D] and value [D] as
 // bf16-rounded floats, then their bf16 bits [2D].
 __device__ __forceinline__ int att_raw_floats(const Params& P) { return ((P.G + 2) * P.D + 255) & ~255; }
+// The stream waves' attention partials follow, in the same slot: acc[wave][head][D],
+// then (m, l) of [wave][head].
+__device__ __forceinline__ float* att_part_ptr(const Params& P, const Ctx& cx, int slot) {
+  return slot_ptr(cx, slot) + kHdr + att_raw_floats(P) + P.G * P.D + 2 * P.D + P.D;
+}
 
 __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
   float* hdr = slot_ptr(cx, slot);
@@ -704,7 +709,7 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
   const float* kf = q + G * D;
   const float* vf = kf + D;
   const uint32_t* kvw = reinterpret_cast<const uint32_t*>(vf + D);
-  const float* part = part_ptr(cx, slot);
+  const float* part = att_part_ptr(P, cx, slot);
   const float* pml = part + kStreams * G * D;  // (m, l) of [wave][head]
   const int lane = cx.lane, p = ih[H_P];
   // score of the new position (its key and value are the staged ones)

@@ -564,7 +564,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
       C.k0 = k;
       if (prof) prof_words(cx, C.slot, s)[0] = rfl((uint32_t)wall_clock64());
       hin = slot_ptr(cx, C.slot) + kHdr;
-      part = part_ptr(cx, C.slot);
+      part = C.type == T_ATT ? att_part_ptr(P, cx, C.slot) : part_ptr(cx, C.slot);
       if (C.type == T_ATT) {
         const int* ih = reinterpret_cast<const int*>(slot_ptr(cx, C.slot));
         const int flags = lds_ld(&ih[H_FLAGS]);

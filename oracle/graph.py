@@ -128,7 +128,7 @@ def resolve(d: Desc, o: Opts) -> Opts:
         return max(1, min(req, _ceil_div(rows, rb)))
 
     chunks = o.attn_chunks or max(1, min(n // (d.max_batch * d.n_kv_heads),
-                                         max(1, d.max_seq // 16)))
+                                         max(1, d.max_seq // 1024)))
     return Opts(
         num_cus=n,
         qkv_tasks_per_group=cap(o.qkv_tasks_per_group or _ceil_div(n, d.n_kv_heads), grp_rows),
