@@ -44,18 +44,19 @@ def algorithmic_bytes(shape, positions) -> int:
     return w + sum((p + 1) * kv_per_pos for p in positions)
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mk_persistent_llama3.2-1b-shape_b1_hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc", f)
                   for f in ("kernels.hip", "pipeline.h", "device.h")]
 
 
-def recorded_traffic(workload_name: str, steps: int, batch: int):
+def recorded_traffic(kernel: str, workload_name: str, steps: int, batch: int):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain copy of known size), if recorded for this
-    workload and step count with the kernel sources as they are now; else None."""
+    kernel variant, workload and step count with the kernel sources as they are
+    now; else None."""
     import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_b{batch}_hbm_traffic.json")
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     h = hashlib.sha256()
@@ -211,7 +212,7 @@ def main():
         "achieved_gbs": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": recorded_traffic(wl.name, K, wl.batch),
+                     "traffic": recorded_traffic(f"mk_persistent_b1_d{ss.ring_slots}", wl.name, K, wl.batch),
                      "kernel": f"mk_persistent_b1_d{ss.ring_slots}", "launch_ms": round(ms, 4),
                      "bytes_per_launch": bytes_launch},
         "oplaunch_baseline_us_per_token": round(us_b, 3),
