@@ -129,8 +129,8 @@ def main():
     from decode_persistent_megakernel_amd.session import Session
 
     wl = workload.config(args.config)
-    if wl.batch != 1:
-        raise SystemExit(f"bench.py: the {wl.name} workload (batch {wl.batch}) is not supported by this build")
+    if wl.batch != 1 and wl.kv_prefill == "none":
+        raise SystemExit(f"bench.py: the {wl.name} workload (batch {wl.batch} with a prompt) is not supported")
     torch.cuda.set_device(0)
     t = time.time()
     w = workload.make_weights(wl)
@@ -139,85 +139,92 @@ def main():
     ss = Session(wl.shape, w, wl.batch, wl.max_seq, kv=kv)
     kv = None
     log(f"model loaded: {ss.n_tasks} tasks, {ss.num_cus} CUs, packed weights {ss.packed_bytes / 1e9:.3f} GB, "
-        f"ring {ss.ring_slots} slots, LDS {ss.lds_bytes} B")
+        f"ring {ss.ring_slots} slots, LDS {ss.lds_bytes} B, {ss.batch_per_launch} sequence(s) per launch")
+    B = wl.batch
+    K, W = args.steps, args.warmup
     if wl.kv_prefill == "none":
         prompt = workload.make_prompt(wl)[0]
-    else:  # the cache holds positions 0 .. kv_len-1; decoding starts after them
-        prompt = [0] * int(workload.kv_lengths(wl)[0]) + [int(workload.make_prompt(wl)[0][0])]
-    P = len(prompt)
-    K, W = args.steps, args.warmup
-    if P - 1 + max(K, W) > wl.max_seq:
+        P = len(prompt)
+        for p in range(P - 1):
+            ss.decode_step([int(prompt[p])], [p], mode=MK_MODE_OPLAUNCH, logits=False)
+        tok0, pos0 = [int(prompt[-1])], [P - 1]
+    else:  # the cache holds positions 0 .. len_b - 1 of sequence b; decoding starts after them
+        tok0 = [int(x) for x in workload.make_prompt(wl)[:, 0]]
+        pos0 = [int(x) for x in workload.kv_lengths(wl)]
+    if max(pos0) + max(K, W) > wl.max_seq:
         raise SystemExit("steps exceed max_seq")
-    for p in range(P - 1 if wl.kv_prefill == "none" else 0):
-        ss.decode_step([int(prompt[p])], [p], mode=MK_MODE_OPLAUNCH, logits=False)
     torch.cuda.synchronize()
     ss.check()
     log("prompt prefilled")
 
     stream = torch.cuda.current_stream()
-    out = torch.zeros((max(K, 1), 1), dtype=torch.int32, device="cuda")
-    tok = int(prompt[-1])
-    for k in range(W):  # warm-up steps (positions P-1.. are written again by the timed launch)
-        nxt, _ = ss.decode_step([tok], [P - 1 + k], mode=MK_MODE_OPLAUNCH, logits=False)
-        tok = int(nxt[0])
+    out = torch.zeros((max(K, 1), B), dtype=torch.int32, device="cuda")
+    tok = list(tok0)
+    for k in range(W):  # warm-up steps (positions pos0.. are written again by the timed launch)
+        nxt, _ = ss.decode_step(tok, [p + k for p in pos0], mode=MK_MODE_OPLAUNCH, logits=False)
+        tok = [int(x) for x in nxt.cpu().tolist()]
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record(stream)
-    ss.generate([int(prompt[-1])], [P - 1], K, out=out[:K])
+    ss.generate(tok0, pos0, K, out=out[:K])
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ss.check()
     ms = e0.elapsed_time(e1)
     us_tok = ms * 1e3 / K
-    positions = [P - 1 + k for k in range(K)]
-    bytes_launch = sum(algorithmic_bytes(wl.shape, [p]) for p in positions)
+    bytes_launch = sum(algorithmic_bytes(wl.shape, [p + k for p in pos0]) for k in range(K))
     achieved = bytes_launch / (ms * 1e-3) / 1e9
-    log(f"megakernel: {K} steps in {ms:.3f} ms (wall {wall * 1e3:.1f} ms): {us_tok:.2f} us/token, "
+    log(f"megakernel: {K} steps in {ms:.3f} ms (wall {wall * 1e3:.1f} ms): {us_tok:.2f} us/step, "
         f"{achieved:.1f} GB/s algorithmic")
 
     # per-operator-launch baseline (same task bodies), a shorter run
     Kb = min(args.oplaunch_steps, K)
-    tok = int(prompt[-1])
-    toks_b = out[:Kb, 0].tolist()
+    toks_b = out[:Kb].cpu().tolist()
+    from decode_persistent_megakernel_amd import mk_decode_step
     torch.cuda.synchronize()
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for k in range(Kb):
-        ss.tok[0] = tok if k == 0 else toks_b[k - 1]
-        ss.pos[0] = P - 1 + k
-        from decode_persistent_megakernel_amd import mk_decode_step
-        mk_decode_step(ss.model, ss.tok, ss.pos, 1, None, ss.next, MK_MODE_OPLAUNCH)
+        ss.tok[:B] = torch.as_tensor(tok0 if k == 0 else toks_b[k - 1], dtype=torch.int32)
+        ss.pos[:B] = torch.as_tensor([p + k for p in pos0], dtype=torch.int32)
+        mk_decode_step(ss.model, ss.tok, ss.pos, B, None, ss.next, MK_MODE_OPLAUNCH)
     b1.record(stream)
     torch.cuda.synchronize()
     ss.check()
     us_b = b0.elapsed_time(b1) * 1e3 / Kb
-    log(f"per-operator launches: {us_b:.2f} us/token over {Kb} steps")
+    log(f"per-operator launches: {us_b:.2f} us/step over {Kb} steps")
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, w, args.cpu_seconds)
         log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads")
 
+    kernel = f"mk_persistent_b{min(B, ss.batch_per_launch)}_d{ss.ring_slots}"
+    per = "token at batch 1" if B == 1 else f"step at batch {B}"
     rec = {
-        "metric": "decode \u00b5s/token at batch 1 + achieved HBM GB/s as % of roofline",
-        "value": round(us_tok, 3), "unit": "\u00b5s/token", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": round(ms / K, 6), "higher_is_better": False, "scaling": "weak",
+        "metric": f"decode \u00b5s/{per} + achieved HBM GB/s as % of roofline",
+        "value": round(us_tok, 3), "unit": "\u00b5s/token" if B == 1 else "\u00b5s/step", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms / K, 6), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "global_batch": wl.batch, "seq_len": P - 1 + K,
-                   "prompt": P if wl.kv_prefill == "none" else 1, "kv_prefilled": P - 1 if wl.kv_prefill != "none" else 0,
-                   "decode_steps": K, "parallelism": "none (1 GPU)"},
+        "config": {"workload": wl.name, "global_batch": B, "seq_len": max(pos0) + K,
+                   "prompt": P if wl.kv_prefill == "none" else 1,
+                   "kv_prefilled": 0 if wl.kv_prefill == "none" else (pos0[0] if B == 1 else pos0),
+                   "decode_steps": K, "sequences_per_launch": min(B, ss.batch_per_launch),
+                   "parallelism": "none (1 GPU)"},
         "achieved_gbs": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": recorded_traffic(f"mk_persistent_b1_d{ss.ring_slots}", wl.name, K, wl.batch),
-                     "kernel": f"mk_persistent_b1_d{ss.ring_slots}", "launch_ms": round(ms, 4),
+                     "traffic": recorded_traffic(kernel, wl.name, K, B),
+                     "kernel": kernel, "launch_ms": round(ms, 4),
                      "bytes_per_launch": bytes_launch},
-        "oplaunch_baseline_us_per_token": round(us_b, 3),
+        "oplaunch_baseline_us_per_step": round(us_b, 3),
         "cpu_baseline": cpu,
     }
+    if B > 1:
+        rec["us_per_sequence_token"] = round(us_tok / B, 3)
     ss.close()
     print(json.dumps(rec), flush=True)
 

@@ -88,7 +88,7 @@ def lib() -> ctypes.CDLL:
         "mk_set_profile_buffer": [vp, vp, ctypes.c_size_t],
         "mk_set_wait_counters": [vp, vp, ctypes.c_size_t],
         "mk_model_info": [vp, u64p, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32),
-                          ctypes.POINTER(i32)],
+                          ctypes.POINTER(i32), ctypes.POINTER(i32)],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -207,11 +207,13 @@ def mk_set_wait_counters(model: int, buf, nbytes: int) -> None:
 
 
 def mk_model_info(model: int):
-    """(packed weight bytes, CUs, tasks per step, ring slots per stream wave, LDS bytes)."""
-    b, n, t, r, l = ctypes.c_uint64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    """(packed weight bytes, CUs, tasks per step, ring slots per stream wave, LDS bytes,
+    sequences per launch)."""
+    b, n, t, r, l, g = (ctypes.c_uint64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(),
+                        ctypes.c_int32())
     _ok(lib().mk_model_info(model, ctypes.byref(b), ctypes.byref(n), ctypes.byref(t), ctypes.byref(r),
-                            ctypes.byref(l)))
-    return b.value, n.value, t.value, r.value, l.value
+                            ctypes.byref(l), ctypes.byref(g)))
+    return b.value, n.value, t.value, r.value, l.value, g.value
 
 
 def mk_free_model(model: int) -> None:

@@ -37,10 +37,13 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+static_assert(mk::kMaxCols == mk::kGroupCols, "the graph's group size is the launch's column capacity");
+
 struct mk_model {
   mk::Graph g;
   int device = 0;
   int lds_bytes = 0;
+  int ncap = 1;  // sequences one launch stages (a call with more runs them in groups)
   uint64_t packed_bytes = 0;
   uint32_t epoch = 0;
   uint32_t max_threshold = 1;
@@ -209,8 +212,8 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
 
   // --- LDS budget -------------------------------------------------------------
   const int D = d.head_dim;
-  if (d.max_batch > kMaxCols)
-    return fail(MK_EUNSUPPORTED, "mk_load_weights: max_batch above 4 is not supported by the VALU task bodies");
+  if (d.max_batch > kMaxBatch)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: max_batch above " + std::to_string(kMaxBatch));
   if (G > kMaxG) return fail(MK_EUNSUPPORTED, "mk_load_weights: more than 4 query heads per kv head");
   if (D != 64 && D != 128) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim must be 64 or 128");
   if (d.hidden > 4096) return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden above 4096");
@@ -224,37 +227,44 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   // Staged copies move whole 1 KiB pieces, so every region is rounded up to
   // 256 floats where a copy lands.
   auto r256 = [](int64_t n) { return (n + 255) / 256 * 256; };
-  const int ncap = std::min<int>(d.max_batch, kMaxCols);
+  // The sequences one launch stages (ncap): as many as leave LDS room for
+  // rings of at least kMinDepth items beside the staging slots; a call with
+  // more sequences runs them in groups of ncap (sequences are independent).
+  int ncap = std::min<int>(d.max_batch, kMaxCols);
   const int kp = static_cast<int>(r256(std::max(d.hidden, d.n_q_heads * D)));
   const int kp_big = static_cast<int>(r256(d.ffn));
   int nlm_tasks = 0;
   for (const Task& t : g.tasks) nlm_tasks += t.type == T_LM;
   const int64_t Ncx = g.opts.attn_chunks;
   const int res_stride = (max_res + 3) & ~3;
-  const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * res_stride;
-  // attention: raw q|k|v, rotated q, new k and v, their bf16 bits, then the
-  // stream waves' partials (acc[wave][head][D], then (m, l) per wave and head)
-  const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D + int64_t(kStreams) * G * (D + 2);
-  const int64_t need_arg = r256(nlm_tasks) * 2;
-  const int64_t need_emb = r256(d.hidden / 2 + 1);
-  const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
-  const int64_t need_comb = r256(int64_t(G) * Ncx * 2) + r256(int64_t(G) * Ncx * D);
-  const int64_t small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
-  const int64_t big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
-  const int64_t part_floats =
-      (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
-  const size_t fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
-                       size_t(srec_max) * sizeof(StreamRec);
-  const size_t lds_max = 160 * 1024;
-  // The rest holds the stream waves' rings of 2 KiB items; each slot is one
-  // item in flight, and a few suffice to keep HBM busy (8 KiB in flight per
-  // wave already streams near the HBM peak).
   const int64_t item_bytes = 2 * kUnitBytes;
-  int64_t ring = std::min<int64_t>(kMaxDepth, (int64_t(lds_max) - int64_t(fixed)) / (kStreams * item_bytes));
-  ring = ring >= 11 ? 11 : ring >= 8 ? 8 : ring >= 6 ? 6 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
-  if (ring < kMinDepth)
-    return fail(MK_EUNSUPPORTED, "mk_load_weights: staging needs " + std::to_string(fixed) +
+  const size_t lds_max = 160 * 1024;
+  int64_t small_floats = 0, big_floats = 0, part_floats = 0, ring = 0;
+  size_t fixed = 0;
+  for (; ncap >= 1; --ncap) {
+    const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * res_stride;
+    // attention: raw q|k|v, rotated q, new k and v, their bf16 bits, then the
+    // stream waves' partials (acc[wave][head][D], then (m, l) per wave and head)
+    const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D + int64_t(kStreams) * G * (D + 2);
+    const int64_t need_arg = r256(nlm_tasks) * 2;
+    const int64_t need_emb = r256(d.hidden / 2 + 1);
+    const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
+    const int64_t need_comb = r256(int64_t(G) * Ncx * 2) + r256(int64_t(G) * Ncx * D);
+    small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
+    big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
+    part_floats = (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
+    fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
+            size_t(srec_max) * sizeof(StreamRec);
+    // The rest holds the stream waves' rings of 2 KiB items; each slot is one
+    // item in flight.
+    ring = fixed < lds_max ? std::min<int64_t>(kMaxDepth, (int64_t(lds_max) - int64_t(fixed)) / (kStreams * item_bytes)) : 0;
+    ring = ring >= 11 ? 11 : ring >= 8 ? 8 : ring >= 6 ? 6 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
+    if (ring >= kMinDepth) break;
+  }
+  if (ncap < 1)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: staging one sequence needs " + std::to_string(fixed) +
                                      " bytes of LDS, leaving no room for the weight rings");
+  m->ncap = ncap;
   const size_t lds = fixed + size_t(kStreams) * size_t(ring) * size_t(item_bytes);
   m->lds_bytes = static_cast<int>(lds);
   HIP_TRY(set_lds_limit(m->lds_bytes), "hipFuncSetAttribute(max dynamic LDS)");
@@ -424,25 +434,41 @@ static int prepare_epoch(mk_model* m, int32_t n_steps, hipStream_t s) {
   return MK_OK;
 }
 
+// The per-call fields for the group of sequences [b0, b0 + nb) of a call with
+// `batch` sequences: its tokens, positions, outputs and KV cache rows.
+static mk::Params group_params(const mk_model* m, const int32_t* tok, const int32_t* pos, int32_t batch, int32_t b0,
+                               int32_t nb, int32_t n_steps, int32_t* out_tokens, float* logits) {
+  mk::Params P = m->base;
+  const size_t seq_kv = size_t(P.Hkv) * size_t(P.S) * size_t(P.D);  // one sequence's rows of a layer
+  P.tokens_in = tok + b0;
+  P.pos_in = pos + b0;
+  P.out_tokens = out_tokens + b0;
+  P.out_stride = batch;
+  P.logits_out = logits ? logits + size_t(b0) * size_t(P.V) : nullptr;
+  P.kcache = m->base.kcache + size_t(b0) * seq_kv;
+  P.vcache = m->base.vcache + size_t(b0) * seq_kv;
+  P.batch = nb;
+  P.n_steps = n_steps;
+  P.timeout_ticks = m->timeout_ticks;
+  return P;
+}
+
+// One persistent launch per group of at most ncap sequences, in order on the
+// stream (sequences never interact, so the groups may run one after another).
 static int run_megakernel(mk_model* m, const int32_t* tok, const int32_t* pos, int32_t batch, int32_t n_steps,
                           int32_t* out_tokens, float* logits, hipStream_t s) {
-  int rc = prepare_epoch(m, n_steps, s);
-  if (rc) return rc;
-  mk::Params P = m->base;
-  P.tokens_in = tok;
-  P.pos_in = pos;
-  P.out_tokens = out_tokens;
-  P.logits_out = logits;
-  P.batch = batch;
-  P.n_steps = n_steps;
-  P.epoch0 = m->epoch;
-  P.use_events = 1;
-  P.timeout_ticks = m->timeout_ticks;
-  P.drop_task = m->drop_task;
-  P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * mk::kProfWords * 8) ? m->profile : nullptr;
-  P.waits = m->waits;
-  HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
-  m->epoch += static_cast<uint32_t>(n_steps);
+  for (int32_t b0 = 0; b0 < batch; b0 += m->ncap) {
+    int rc = prepare_epoch(m, n_steps, s);
+    if (rc) return rc;
+    mk::Params P = group_params(m, tok, pos, batch, b0, std::min(m->ncap, batch - b0), n_steps, out_tokens, logits);
+    P.epoch0 = m->epoch;
+    P.use_events = 1;
+    P.drop_task = m->drop_task;
+    P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * mk::kProfWords * 8) ? m->profile : nullptr;
+    P.waits = m->waits;
+    HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
+    m->epoch += static_cast<uint32_t>(n_steps);
+  }
   return MK_OK;
 }
 
@@ -453,19 +479,14 @@ int mk_decode_step(mk_model* m, const int32_t* d_tokens, const int32_t* d_pos, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == MK_MODE_MEGAKERNEL) return run_megakernel(m, d_tokens, d_pos, batch, 1, d_next, d_logits, s);
   if (mode != MK_MODE_OPLAUNCH) return fail(MK_EINVAL, "mk_decode_step: unknown mode");
-  mk::Params P = m->base;
-  P.tokens_in = d_tokens;
-  P.pos_in = d_pos;
-  P.out_tokens = d_next;
-  P.logits_out = d_logits;
-  P.batch = batch;
-  P.n_steps = 1;
-  P.epoch0 = 0;
-  P.use_events = 0;
-  P.timeout_ticks = m->timeout_ticks;
-  P.drop_task = -1;
-  for (const auto& op : m->g.ops)
-    HIP_TRY(mk::launch_op(P, op.first, op.second - op.first, m->lds_bytes, s), "hipLaunchKernel(mk_oplaunch)");
+  for (int32_t b0 = 0; b0 < batch; b0 += m->ncap) {
+    mk::Params P = group_params(m, d_tokens, d_pos, batch, b0, std::min(m->ncap, batch - b0), 1, d_next, d_logits);
+    P.epoch0 = 0;
+    P.use_events = 0;
+    P.drop_task = -1;
+    for (const auto& op : m->g.ops)
+      HIP_TRY(mk::launch_op(P, op.first, op.second - op.first, m->lds_bytes, s), "hipLaunchKernel(mk_oplaunch)");
+  }
   return MK_OK;
 }
 
@@ -523,8 +544,9 @@ int mk_set_wait_counters(mk_model* m, void* d_buf, size_t bytes) {
 }
 
 int mk_model_info(const mk_model* m, uint64_t* packed_weight_bytes, int32_t* num_cus, int32_t* n_tasks,
-                  int32_t* ring_slots, int32_t* lds_bytes) {
+                  int32_t* ring_slots, int32_t* lds_bytes, int32_t* batch_per_launch) {
   if (!m) return fail(MK_EINVAL, "mk_model_info: NULL model");
+  if (batch_per_launch) *batch_per_launch = m->ncap;
   if (packed_weight_bytes) *packed_weight_bytes = m->packed_bytes;
   if (num_cus) *num_cus = m->g.opts.num_cus;
   if (n_tasks) *n_tasks = static_cast<int32_t>(m->g.tasks.size());

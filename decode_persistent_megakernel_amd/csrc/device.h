@@ -28,6 +28,7 @@ constexpr int kThreads = 64 * (kCtlWaves + kStreams);
 constexpr int kMaxDepth = 11;  // ring slots (2 KiB items) per stream wave: 4, 6, 8 or 11
 constexpr int kMinDepth = 4;   // fewer cannot hide the copy latency
 constexpr int kMaxCols = 4;    // sequences a matvec task handles
+constexpr int kMaxBatch = 256; // sequences a model holds (larger calls run in groups of at most kMaxCols)
 constexpr int kMaxG = 4;       // query heads per kv head
 constexpr int kStripes = 8;    // event counter stripes (one per XCD)
 constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte line
@@ -85,7 +86,7 @@ struct Params {
   int32_t kp_big;       // staged floats per column in the big slot (FFN rounded up to 256)
   int32_t wave_vrows;   // partial-sum rows per (stream wave, column): the row blocks its piece touches
   int32_t res_stride;   // staged residual rows per column (projection tasks)
-  int32_t ncap;         // staged columns = min(max_batch, kMaxCols)
+  int32_t ncap;         // staged columns: the most sequences one launch handles (<= kMaxCols)
   int32_t small_floats; // LDS staging slot size (two small slots)
   int32_t big_floats;   // LDS staging slot size for down-projection and merge tasks
   int32_t part_floats;  // LDS partial-sum area per slot
@@ -112,7 +113,8 @@ struct Params {
   // call
   const int32_t* tokens_in;   // [batch]
   const int32_t* pos_in;      // [batch]
-  int32_t* out_tokens;        // [n_steps][batch]
+  int32_t* out_tokens;        // [n_steps][out_stride]
+  int32_t out_stride;         // sequences between consecutive steps' rows of out_tokens
   float* logits_out;          // [batch][V] or null (written at the last step)
   int32_t batch;
   int32_t n_steps;

@@ -65,7 +65,7 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
     return fail("mk_graph_opts: negative option");
 
   const int32_t N = o.num_cus ? o.num_cus : 256;
-  const int32_t rb = o.row_block ? o.row_block : (d.max_batch == 1 ? 4 : 16);
+  const int32_t rb = o.row_block ? o.row_block : 4;
   const int32_t Hkv = d.n_kv_heads, G = d.n_q_heads / d.n_kv_heads, B = d.max_batch;
   const int32_t grp_rows = (G + 2) * d.head_dim;
   auto cap = [&](int32_t req, int32_t rows) {
@@ -81,7 +81,7 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   r.lm_tasks = cap(o.lm_tasks ? o.lm_tasks : N, d.vocab);
   r.attn_chunks = o.attn_chunks
                       ? o.attn_chunks
-                      : std::max(1, std::min(N / (B * Hkv), std::max(1, d.max_seq / 1024)));
+                      : std::max(1, std::min(N / (std::min(B, kGroupCols) * Hkv), std::max(1, d.max_seq / 1024)));
   const int32_t Nc = r.attn_chunks;
 
   Graph& g = *out;

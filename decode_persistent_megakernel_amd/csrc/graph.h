@@ -13,6 +13,10 @@
 
 namespace mk {
 
+// most sequences one launch decodes; the default attention chunking is sized
+// for a group of this many
+constexpr int32_t kGroupCols = 4;
+
 enum TaskType : int32_t {
   T_EMB = 0, T_QKV = 1, T_ATT = 2, T_COMB = 3, T_O = 4, T_GU = 5, T_D = 6, T_LM = 7, T_ARGMAX = 8,
   T_COUNT = 9

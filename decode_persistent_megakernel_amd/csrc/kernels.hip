@@ -874,7 +874,7 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
       wave_argmax(best, bi);
       if (lane == 0) {
         if (bi < 0 || bi >= P.V) bi = 0;  // every logit was NaN
-        P.out_tokens[(size_t)step * P.batch + T.b] = bi;
+        P.out_tokens[(size_t)step * P.out_stride + T.b] = bi;
         st_coh(P.tok_cur + T.b, bi);
       }
       break;

@@ -42,7 +42,8 @@ class Session:
             assert tuple(self.k.shape) == kvshape
         self.model = mk_load_weights(self.graph, w, self.k, self.v, shape.n_layers)
         self.weights = w if keep_weights else None
-        self.packed_bytes, self.num_cus, _, self.ring_slots, self.lds_bytes = mk_model_info(self.model)
+        (self.packed_bytes, self.num_cus, _, self.ring_slots, self.lds_bytes,
+         self.batch_per_launch) = mk_model_info(self.model)
         self.tok = torch.zeros(max_batch, dtype=torch.int32, device=dev)
         self.pos = torch.zeros(max_batch, dtype=torch.int32, device=dev)
         self.next = torch.zeros(max_batch, dtype=torch.int32, device=dev)

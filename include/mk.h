@@ -112,6 +112,9 @@ void mk_free_graph(mk_graph *g);
  * KV cache may not. Work is enqueued on `stream` and completed before return.
  * *out receives a model the caller frees with mk_free_model (after its work
  * has finished). The graph may be freed afterwards.
+ * One launch stages at most batch_per_launch sequences (mk_model_info): the
+ * largest count up to 4 whose staging slots leave LDS room for weight rings of
+ * at least 4 items per stream wave. max_batch may exceed it (up to 256).
  * Errors: MK_EINVAL (NULL pointer), MK_EUNSUPPORTED (fewer resident compute
  * units than num_cus, shape outside this build), MK_ENOMEM, MK_EHIP. */
 int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_model **out);
@@ -121,7 +124,10 @@ int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_mod
  * greedy next token to d_next[b] and (if d_logits != NULL) the fp32 logits to
  * d_logits [batch, V] row-major. All four arrays are device pointers (int32 /
  * fp32). mode MK_MODE_MEGAKERNEL = one persistent launch; MK_MODE_OPLAUNCH = one
- * launch per operator with the same task bodies. Asynchronous on `stream`;
+ * launch per operator with the same task bodies. A batch above the model's
+ * batch_per_launch runs as consecutive launches over groups of that many
+ * sequences (sequences never interact), each group's outputs at its own rows.
+ * Asynchronous on `stream`;
  * argument errors return synchronously. Device-side errors (token >= V,
  * position >= max_seq, watchdog) are recorded in the model's status word and
  * returned by mk_check or by the next call. */
@@ -133,8 +139,10 @@ int mk_decode_step(mk_model *m, const int32_t *d_tokens, const int32_t *d_pos, i
  * device). Step k feeds, for every sequence b, d_tokens0[b] (k = 0) or the
  * token chosen at step k-1, at position d_pos0[b] + k. Chosen tokens go to
  * d_out_tokens [n_steps, batch] (int32, device); if d_last_logits != NULL the
- * fp32 logits of the final step go there [batch, V]. Asynchronous on `stream`;
- * errors as for mk_decode_step. */
+ * fp32 logits of the final step go there [batch, V]. A batch above
+ * batch_per_launch runs group by group, as for mk_decode_step (each group's
+ * n_steps in one launch). Asynchronous on `stream`; errors as for
+ * mk_decode_step. */
 int mk_generate(mk_model *m, const int32_t *d_tokens0, const int32_t *d_pos0, int32_t batch,
                 int32_t n_steps, int32_t *d_out_tokens, float *d_last_logits, void *stream);
 
@@ -188,10 +196,13 @@ int mk_set_wait_counters(mk_model *m, void *d_buf, size_t bytes);
  *   num_cus, n_tasks     workgroups of the persistent launch, tasks per step;
  *   ring_slots           2 KiB ring slots per stream wave (the kernel variant
  *                        mk_persistent_b<batch>_d<ring_slots> runs a call);
- *   lds_bytes            dynamic LDS per workgroup.
+ *   lds_bytes            dynamic LDS per workgroup;
+ *   batch_per_launch     the most sequences one launch handles (larger calls
+ *                        run in groups of this size).
  * MK_EINVAL for a NULL model. */
 int mk_model_info(const mk_model *m, uint64_t *packed_weight_bytes, int32_t *num_cus,
-                  int32_t *n_tasks, int32_t *ring_slots, int32_t *lds_bytes);
+                  int32_t *n_tasks, int32_t *ring_slots, int32_t *lds_bytes,
+                  int32_t *batch_per_launch);
 
 void mk_free_model(mk_model *m);
 

@@ -44,6 +44,8 @@ from .decoder import Model, State, rmsnorm, rope, silu
 # task types
 EMB, QKV, ATT, COMB, OPROJ, GU, DOWN, LM, ARGMAX = range(9)
 TYPE_NAMES = ["EMB", "QKV", "ATT", "COMB", "O", "GU", "D", "LM", "ARGMAX"]
+# most sequences one launch decodes (the graph spec's group size)
+GROUP_COLS = 4
 
 MAGIC = b"MKGRAPH1"
 VERSION = 1
@@ -120,14 +122,16 @@ def _ceil_div(a: int, b: int) -> int:
 def resolve(d: Desc, o: Opts) -> Opts:
     """Fill every zero option with its default (a pure function of the shape)."""
     n = o.num_cus or 256
-    rb = o.row_block or (4 if d.max_batch == 1 else 16)
+    rb = o.row_block or 4
     G = d.n_q_heads // d.n_kv_heads
     grp_rows = (G + 2) * d.head_dim
 
     def cap(req: int, rows: int) -> int:
         return max(1, min(req, _ceil_div(rows, rb)))
 
-    chunks = o.attn_chunks or max(1, min(n // (d.max_batch * d.n_kv_heads),
+    # sequences decode in groups of at most GROUP_COLS per launch: chunks are
+    # sized so that one group's attention tasks cover the compute units
+    chunks = o.attn_chunks or max(1, min(n // (min(d.max_batch, GROUP_COLS) * d.n_kv_heads),
                                          max(1, d.max_seq // 1024)))
     return Opts(
         num_cus=n,

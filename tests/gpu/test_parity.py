@@ -287,10 +287,85 @@ def test_long_context_sampled():
     ss.close()
 
 
-def test_batch_above_four_is_refused():
-    """Batch 16 (the 8B batch workload) needs the MFMA task bodies, which are
-    not built: loading refuses it with MK_EUNSUPPORTED instead of running."""
-    import decode_persistent_megakernel_amd as mk
-    with pytest.raises(mk.MKError) as e:
-        session(0, max_batch=16)
-    assert e.value.code == -5
+def test_tiny_batch16_in_groups():
+    """max_batch 16 on the tiny shape: a launch stages at most four sequences,
+    so batch 16 and batch 13 calls run in groups. Ragged positions; logits of
+    every sequence against the oracle; megakernel and per-operator launches
+    bit-identical (logits and caches); mk_generate over the groups equal to
+    step-by-step decoding."""
+    wl = workload.config(0)
+    a = session(0, "random", max_batch=16, max_seq=40)
+    b = session(0, "random", max_batch=16, max_seq=40)
+    assert 1 <= a.batch_per_launch < 16
+    om = oracle_model(0, "random")
+    st = om.new_state(16, 40)
+    toks = workload.make_prompt(wl)[0]
+    for k in range(5):
+        nb = 13 if k == 3 else 16
+        tk = [int(toks[(k + 3 * s) % len(toks)]) for s in range(nb)]
+        ps = [k + (s % 5) for s in range(nb)]
+        na, la = a.decode_step(tk, ps, mode=0)
+        nb_, lb = b.decode_step(tk, ps, mode=1)
+        assert torch.equal(la, lb) and torch.equal(na, nb_), k
+        ref = om.decode_step(st, tk, ps)
+        g = la.double().cpu().numpy()
+        for s in range(nb):
+            check_logits(g[s], ref[s], f"step {k} seq {s}")
+            assert int(na[s]) == int(np.argmax(g[s]))
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+    # continue all 16 sequences: one mk_generate call against stepwise steps
+    t0 = [int(toks[s % len(toks)]) for s in range(16)]
+    p0 = [5 + (s % 5) for s in range(16)]
+    out = a.generate(t0, p0, 4)
+    tk = list(t0)
+    for k in range(4):
+        nxt, _ = b.decode_step(tk, [p + k for p in p0], mode=1)
+        tk = [int(x) for x in nxt.cpu().tolist()]
+        assert tk == out[k].cpu().tolist(), k
+    a.check()
+    b.check()
+    a.close()
+    b.close()
+
+
+@pytest.mark.slow
+def test_8b_batch16_sampled():
+    """The batch workload at full size: Llama-3-8B shape, 16 sequences with
+    prefilled caches of seeded lengths in 512..8192, run in groups of the
+    launch's capacity. Two decode steps for all 16; the shortest and the
+    longest sequence checked against the oracle over the same cache (logits
+    and greedy token); mk_generate over the groups equal to the two steps."""
+    import torch
+    wl = workload.config(4)
+    lens = [int(x) for x in workload.kv_lengths(wl)]
+    kc, vc = workload.make_prefill(wl)
+    ss = session(4, kv=(kc, vc))
+    print(f"[batch16] lens {lens} sequences per launch {ss.batch_per_launch} ring {ss.ring_slots}", flush=True)
+    om = oracle_model(4, cache=False)
+    picks = [int(np.argmin(lens)), int(np.argmax(lens))]
+    states = {}
+    for b in picks:
+        st = om.new_state(1, wl.max_seq)
+        st.kcache[:, 0] = kc[:, b].contiguous().view(torch.int16).numpy().view(np.uint16)
+        st.vcache[:, 0] = vc[:, b].contiguous().view(torch.int16).numpy().view(np.uint16)
+        states[b] = st
+    del kc, vc
+    tok0 = [int(t) for t in workload.make_prompt(wl)[:, 0]]
+    tk = list(tok0)
+    steps = []
+    for k in range(2):
+        nxt, lg = ss.decode_step(tk, [n + k for n in lens])
+        g = lg.double().cpu().numpy()
+        nxt = [int(x) for x in nxt.cpu().tolist()]
+        for b in picks:
+            ref = om.decode_step(states[b], [tk[b]], [lens[b] + k])[0]
+            check_logits(g[b], ref, f"batch16 seq {b} (len {lens[b]}) step {k}")
+            assert nxt[b] == int(np.argmax(ref))
+        steps.append(nxt)
+        tk = nxt
+    ss.check()
+    # the same two steps in one mk_generate call (positions rewritten with the same values)
+    out = ss.generate(tok0, lens, 2)
+    assert out.cpu().tolist() == steps
+    ss.check()
+    ss.close()
