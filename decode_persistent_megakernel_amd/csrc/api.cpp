@@ -43,7 +43,8 @@ struct mk_model {
   mk::Graph g;
   int device = 0;
   int lds_bytes = 0;
-  int ncap = 1;  // sequences one launch stages (a call with more runs them in groups)
+  int ncap = 1;       // sequences one launch stages (a call with more runs them in groups)
+  int max_batch = 1;  // sequences the KV caches hold
   uint64_t packed_bytes = 0;
   uint32_t epoch = 0;
   uint32_t max_threshold = 1;
@@ -109,11 +110,11 @@ int mk_graph_info(const mk_graph* g, int32_t* n_tasks, int32_t* n_events, mk_gra
 
 void mk_free_graph(mk_graph* g) { delete g; }
 
-int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_model** out) {
+// Load `gsrc` (whose per-sequence tasks cover gsrc.desc.max_batch sequences)
+// for KV caches that hold cache_batch sequences.
+static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weights* w, void* stream, mk_model** out) {
   using namespace mk;
-  if (!gr || !w || !out || !w->layers || !w->embed || !w->g_final || !w->k_cache || !w->v_cache)
-    return fail(MK_EINVAL, "mk_load_weights: NULL argument");
-  const mk_model_desc& d = gr->g.desc;
+  const mk_model_desc& d = gsrc.desc;
   if (!d.tied_embeddings && !w->lm_head) return fail(MK_EINVAL, "mk_load_weights: lm_head is NULL but not tied");
   for (int l = 0; l < d.n_layers; ++l) {
     const mk_layer_weights& L = w->layers[l];
@@ -129,7 +130,8 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
     mk_model*& m;
     ~Guard() { delete m; }
   } guard{m};
-  m->g = gr->g;
+  m->g = gsrc;
+  m->max_batch = cache_batch;
   const Graph& g = m->g;
   HIP_TRY(hipGetDevice(&m->device), "hipGetDevice");
   hipDeviceProp_t prop;
@@ -387,7 +389,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   P.counters = d_cnt;
   P.n_tasks = static_cast<int32_t>(g.tasks.size());
   P.L = d.n_layers; P.H = d.hidden; P.Hq = d.n_q_heads; P.Hkv = d.n_kv_heads; P.D = d.head_dim; P.F = d.ffn;
-  P.V = d.vocab; P.G = G; P.B = d.max_batch; P.S = d.max_seq; P.Nc = g.opts.attn_chunks; P.n_lm = nlm;
+  P.V = d.vocab; P.G = G; P.B = cache_batch; P.S = d.max_seq; P.Nc = g.opts.attn_chunks; P.n_lm = nlm;
   P.eps = d.rms_eps;
   P.small_floats = static_cast<int32_t>(small_floats);
   P.big_floats = static_cast<int32_t>(big_floats);
@@ -412,11 +414,33 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   return MK_OK;
 }
 
+int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_model** out) {
+  if (!gr || !w || !out || !w->layers || !w->embed || !w->g_final || !w->k_cache || !w->v_cache)
+    return fail(MK_EINVAL, "mk_load_weights: NULL argument");
+  const mk_model_desc& d = gr->g.desc;
+  int rc = load_model(gr->g, d.max_batch, w, stream, out);
+  if (rc != MK_OK || (*out)->ncap >= d.max_batch) return rc;
+  // One launch decodes a group of ncap sequences: run the graph of a
+  // ncap-sequence model (same options) on every group, so that a launch holds
+  // no tasks of sequences outside its group.
+  const int32_t ncap = (*out)->ncap;
+  mk_free_model(*out);
+  *out = nullptr;
+  mk_model_desc d1 = d;
+  d1.max_batch = ncap;
+  mk_graph_opts o1 = gr->g.opts;
+  mk::Graph g1;
+  std::string err;
+  rc = mk::build_graph(d1, &o1, &g1, &err);
+  if (rc != MK_OK) return fail(rc, "mk_load_weights: group graph: " + err);
+  return load_model(g1, d.max_batch, w, stream, out);
+}
+
 static int check_call(mk_model* m, const int32_t* tok, const int32_t* pos, int32_t batch, const void* outp) {
   if (!m) return fail(MK_EINVAL, "NULL model");
   if (!tok || !pos || !outp) return fail(MK_EINVAL, "NULL token, position or output pointer");
-  if (batch < 1 || batch > m->g.desc.max_batch)
-    return fail(MK_EINVAL, "batch must be in 1..max_batch (" + std::to_string(m->g.desc.max_batch) + ")");
+  if (batch < 1 || batch > m->max_batch)
+    return fail(MK_EINVAL, "batch must be in 1..max_batch (" + std::to_string(m->max_batch) + ")");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != m->device)
     return fail(MK_EINVAL, "the current HIP device is not the model's device");
