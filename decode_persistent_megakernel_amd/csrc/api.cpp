@@ -418,22 +418,30 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   if (!gr || !w || !out || !w->layers || !w->embed || !w->g_final || !w->k_cache || !w->v_cache)
     return fail(MK_EINVAL, "mk_load_weights: NULL argument");
   const mk_model_desc& d = gr->g.desc;
-  int rc = load_model(gr->g, d.max_batch, w, stream, out);
-  if (rc != MK_OK || (*out)->ncap >= d.max_batch) return rc;
-  // One launch decodes a group of ncap sequences: run the graph of a
-  // ncap-sequence model (same options) on every group, so that a launch holds
-  // no tasks of sequences outside its group.
-  const int32_t ncap = (*out)->ncap;
-  mk_free_model(*out);
-  *out = nullptr;
-  mk_model_desc d1 = d;
-  d1.max_batch = ncap;
-  mk_graph_opts o1 = gr->g.opts;
-  mk::Graph g1;
-  std::string err;
-  rc = mk::build_graph(d1, &o1, &g1, &err);
-  if (rc != MK_OK) return fail(rc, "mk_load_weights: group graph: " + err);
-  return load_model(g1, d.max_batch, w, stream, out);
+  // One launch decodes a group of at most kGroupCols sequences (fewer when the
+  // LDS stages fewer). A model whose batch exceeds its group runs, on every
+  // group, the graph of a desc with the group's size and the same options, so
+  // that a launch holds no tasks of sequences outside its group.
+  int32_t group = std::min<int32_t>(d.max_batch, mk::kGroupCols);
+  mk_graph_opts opts = gr->g.opts;
+  for (;;) {
+    mk::Graph g1;
+    const mk::Graph* src = &gr->g;
+    if (group < d.max_batch) {
+      mk_model_desc d1 = d;
+      d1.max_batch = group;
+      std::string err;
+      const int brc = mk::build_graph(d1, &opts, &g1, &err);
+      if (brc != MK_OK) return fail(brc, "mk_load_weights: group graph: " + err);
+      src = &g1;
+    }
+    const int rc = load_model(*src, d.max_batch, w, stream, out);
+    if (rc != MK_OK || (*out)->ncap == group) return rc;
+    // the LDS stages fewer sequences than the graph holds: rebuild for that many
+    group = (*out)->ncap;
+    mk_free_model(*out);
+    *out = nullptr;
+  }
 }
 
 static int check_call(mk_model* m, const int32_t* tok, const int32_t* pos, int32_t batch, const void* outp) {

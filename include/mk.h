@@ -114,9 +114,10 @@ void mk_free_graph(mk_graph *g);
  * has finished). The graph may be freed afterwards.
  * One launch stages at most batch_per_launch sequences (mk_model_info): the
  * largest count up to 4 whose staging slots leave LDS room for weight rings of
- * at least 4 items per stream wave. max_batch may exceed it (up to 256); such
- * a model runs, on each group of sequences, the graph these options give for
- * a batch_per_launch-sequence desc (mk_model_info's n_tasks counts it).
+ * at least 4 items per stream wave. max_batch may exceed it (up to 256); a
+ * model whose max_batch exceeds batch_per_launch runs, on each group of
+ * sequences, the graph these options give for a batch_per_launch-sequence desc
+ * (mk_model_info's n_tasks counts that graph's tasks).
  * Errors: MK_EINVAL (NULL pointer), MK_EUNSUPPORTED (fewer resident compute
  * units than num_cus, shape outside this build), MK_ENOMEM, MK_EHIP. */
 int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_model **out);
