@@ -192,7 +192,9 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     const size_t first = srec.size();
     for (size_t qp = 0; qp < q.size(); ++qp) {
       const DevTask& x = dt[q[qp]];
-      const int slot = (x.type == T_D || x.type == T_COMB) ? 2 : (nsmall++ & 1);
+      // staging slot as the kernel assigns it: 3 down-projection (overlays the
+      // others), 2 merge, else the small slots alternately
+      const int slot = x.type == T_D ? 3 : x.type == T_COMB ? 2 : (nsmall++ & 1);
       const bool stream = x.type == T_QKV || x.type == T_ATT || x.type == T_O || x.type == T_GU ||
                           x.type == T_D || x.type == T_LM;
       if (!stream) continue;
@@ -224,8 +226,10 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     return fail(MK_EUNSUPPORTED, "mk_load_weights: attn_chunks * (max_seq + 1) must stay below 2^32");
   if (d.hidden % 4 || (d.n_q_heads * d.head_dim) % 4 || d.ffn % 4)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden, q width and ffn must be multiples of 4");
-  // LDS: control words, two small staging slots, one big slot (down-projection
-  // inputs and attention merges), three partial-sum areas, then the rings.
+  // LDS: control words, two small staging slots, the merge slot (attention
+  // merges), three partial-sum areas, then the rings. A down-projection input
+  // overlays the two small slots and the merge slot (the kernel stages it only
+  // once every earlier task has retired).
   // Staged copies move whole 1 KiB pieces, so every region is rounded up to
   // 256 floats where a copy lands.
   auto r256 = [](int64_t n) { return (n + 255) / 256 * 256; };
@@ -253,7 +257,9 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
     const int64_t need_comb = r256(int64_t(G) * Ncx * 2) + r256(int64_t(G) * Ncx * D);
     small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
-    big_floats = (32 + std::max(need_mv_big, need_comb) + 3) & ~int64_t(3);
+    // the merge slot follows the two small ones; the down-projection input
+    // overlays all three, so the merge slot holds what it needs beyond them
+    big_floats = (std::max(32 + need_comb, 32 + need_mv_big - 2 * small_floats) + 3) & ~int64_t(3);
     part_floats = (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
     fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
             size_t(srec_max) * sizeof(StreamRec);

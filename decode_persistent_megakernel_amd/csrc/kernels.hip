@@ -281,18 +281,28 @@ __device__ __forceinline__ int chunk_bound(int c, int64_t len, int Nc) {
   return (int)((uint32_t)c * (uint32_t)len / (uint32_t)Nc);
 }
 
-__device__ __forceinline__ bool is_big(int type) { return type == T_D || type == T_COMB; }
-// Staging slot of the next task: 2 for down-projection and merge tasks, else
-// the two small slots alternate over the whole walk of the queue (across
-// steps). The stream waves' records carry the assignment of the first step
-// and whether it flips from one step to the next.
+// Staging slots: two small ones (0, 1), the merge slot (2) and the
+// down-projection slot (3), which overlays all three: [small 0][small 1][merge]
+// in LDS, with the down-projection input starting at small 0. A task of slot 3
+// is staged once every earlier task has retired, and every later task waits
+// for it (its dependency event implies both); the other slots are disjoint.
+// Slot 3 shares slot 2's control words, partial sums and profile words (merge
+// tasks use none of them).
+enum { kSlotMerge = 2, kSlotDown = 3 };
+__device__ __forceinline__ int ctl_slot(int slot) { return slot == kSlotDown ? kSlotMerge : slot; }
+// Staging slot of the next task: the small slots alternate over the whole walk
+// of the queue (across steps). The stream waves' records carry the assignment
+// of the first step and whether it flips from one step to the next.
 __device__ __forceinline__ int next_slot(int& nsmall, int type) {
-  if (is_big(type)) return 2;
+  if (type == T_D) return kSlotDown;
+  if (type == T_COMB) return kSlotMerge;
   return (nsmall++) & 1;
 }
-__device__ __forceinline__ int slot_kp(const Params& P, int slot) { return slot == 2 ? P.kp_big : P.kp; }
-__device__ __forceinline__ float* slot_ptr(const Ctx& cx, int slot) { return cx.slots + slot * cx.small_floats; }
-__device__ __forceinline__ float* part_ptr(const Ctx& cx, int slot) { return cx.parts + slot * cx.part_floats; }
+__device__ __forceinline__ int slot_kp(const Params& P, int slot) { return slot == kSlotDown ? P.kp_big : P.kp; }
+__device__ __forceinline__ float* slot_ptr(const Ctx& cx, int slot) {
+  return slot == kSlotDown ? cx.slots : cx.slots + slot * cx.small_floats;
+}
+__device__ __forceinline__ float* part_ptr(const Ctx& cx, int slot) { return cx.parts + ctl_slot(slot) * cx.part_floats; }
 
 __device__ __forceinline__ void raise_abort(const Params& P, const Ctx& cx, int32_t status_bits) {
   if (cx.lane == 0) {
@@ -354,11 +364,11 @@ __device__ __forceinline__ void waits_put(const Params& P, const Ctx& cx, const 
 }
 
 __device__ __forceinline__ uint32_t* prof_words(const Ctx& cx, int slot, int s) {
-  return reinterpret_cast<uint32_t*>(cx.ctl) + kProfCtl + (slot * kStreams + s) * 4;
+  return reinterpret_cast<uint32_t*>(cx.ctl) + kProfCtl + (ctl_slot(slot) * kStreams + s) * 4;
 }
 
 __device__ __forceinline__ int* piece_words(const Ctx& cx, int slot, int s) {
-  return cx.ctl + kPieceCtl + (slot * kStreams + s) * 2;
+  return cx.ctl + kPieceCtl + (ctl_slot(slot) * kStreams + s) * 2;
 }
 
 __device__ __forceinline__ bool has_stream(int type) {
@@ -584,7 +594,7 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
 
 __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
-  int last0 = -1, last1 = -1, last2 = -1;  // last task staged into each slot
+  int last0 = -1, last1 = -1, last2 = -1, last3 = -1;  // last task staged into each slot
   Waits wt;  // slot free, dependency event, staging, tasks
   waits_init(P, cx, wt);
   for (int step = 0; step < P.n_steps; ++step) {
@@ -593,11 +603,12 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
       const int id = task_at(P, cx, qi);
       const DevTask T = ld_task(P, id);
       const int slot = next_slot(nsmall, T.type);
-      const int prev = slot == 0 ? last0 : slot == 1 ? last1 : last2;
+      // the task whose retirement frees the slot (slot 3 overlays the others)
+      const int prev = slot == kSlotDown ? i - 1 : max(slot == 0 ? last0 : slot == 1 ? last1 : last2, last3);
       uint64_t s0 = waits_now(wt);
       if (prev >= 0 && !spin_ctl(P, cx, C_RETIRED, prev + 1)) return;
       waits_add(wt, 0, s0);
-      if (slot == 0) last0 = i; else if (slot == 1) last1 = i; else last2 = i;
+      if (slot == 0) last0 = i; else if (slot == 1) last1 = i; else if (slot == 2) last2 = i; else last3 = i;
       StagePre pre;
       if (T.type == T_QKV || T.type == T_O || T.type == T_GU || T.type == T_D || T.type == T_LM)
         stage_matvec_pre(P, cx, T, slot, pre);
@@ -896,7 +907,7 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
       if (!spin_ctl(P, cx, C_STAGED, i + 1)) return;
       waits_add(wt, 0, s0);
       const uint64_t t_staged = wall_clock64();
-      if (has_stream(T.type) && !spin_ctl(P, cx, C_DONE + slot, kStreams)) return;
+      if (has_stream(T.type) && !spin_ctl(P, cx, C_DONE + ctl_slot(slot), kStreams)) return;
       const uint64_t t_computed = wall_clock64();
       waits_count(wt, 1, (uint32_t)(t_computed - t_staged));
       retire_task(P, cx, T, slot, step);
@@ -919,7 +930,7 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
               rec[8 + w] = pw[1];
             }
         }
-        __hip_atomic_store(&cx.ctl[C_DONE + slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&cx.ctl[C_DONE + ctl_slot(slot)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       lds_st(&cx.ctl[C_RETIRED], i + 1);
     }
@@ -968,7 +979,8 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
     cx.nrec = has_stream(T.type) ? 1 : 0;
     if (threadIdx.x == 0 && cx.nrec) {
       StreamRec r;
-      r.tsbg = (uint32_t)T.type | (uint32_t)(is_big(T.type) ? 2 : 0) << 4 | (uint32_t)T.b << 6 | (uint32_t)T.g << 16;
+      int nsmall = 0;
+      r.tsbg = (uint32_t)T.type | (uint32_t)next_slot(nsmall, T.type) << 4 | (uint32_t)T.b << 6 | (uint32_t)T.g << 16;
       r.lc = (uint32_t)T.layer | (uint32_t)T.chunk << 16;
       r.n_units = T.n_units;
       r.kq = (uint32_t)T.kb;

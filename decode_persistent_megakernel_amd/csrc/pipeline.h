@@ -542,7 +542,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
           pw[1] = t_first;
           pw[2] = rfl((uint32_t)wall_clock64());
         }
-        lds_add_lane0(&cx.ctl[C_DONE + C.slot], 1);
+        lds_add_lane0(&cx.ctl[C_DONE + ctl_slot(C.slot)], 1);
         C.type = -1;
       }
       if (++C.r >= cx.nrec) {
