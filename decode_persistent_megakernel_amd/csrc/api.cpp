@@ -226,10 +226,10 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     return fail(MK_EUNSUPPORTED, "mk_load_weights: attn_chunks * (max_seq + 1) must stay below 2^32");
   if (d.hidden % 4 || (d.n_q_heads * d.head_dim) % 4 || d.ffn % 4)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden, q width and ffn must be multiples of 4");
-  // LDS: control words, two small staging slots, the merge slot (attention
-  // merges), three partial-sum areas, then the rings. A down-projection input
-  // overlays the two small slots and the merge slot (the kernel stages it only
-  // once every earlier task has retired).
+  // LDS: control words, the stream waves' rings, two small staging slots, the
+  // merge slot (attention merges), three partial-sum areas, then the stream
+  // records. A down-projection input overlays the two small slots and the
+  // merge slot (the kernel stages it only once every earlier task has retired).
   // Staged copies move whole 1 KiB pieces, so every region is rounded up to
   // 256 floats where a copy lands.
   auto r256 = [](int64_t n) { return (n + 255) / 256 * 256; };

@@ -949,12 +949,12 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   extern __shared__ __align__(16) char smem[];
   Ctx cx;
   cx.ctl = reinterpret_cast<int*>(smem);
-  float* base = reinterpret_cast<float*>(smem + kCtlBytes);
+  cx.ring = reinterpret_cast<uint8_t*>(smem + kCtlBytes);
+  float* base = reinterpret_cast<float*>(cx.ring + (size_t)kStreams * P.ring_slots * 2 * kUnitBytes);
   cx.slots = base;
   cx.small_floats = P.small_floats;
   cx.parts = base + 2 * P.small_floats + P.big_floats;
   cx.part_floats = P.part_floats;
-  cx.ring = reinterpret_cast<uint8_t*>(cx.parts + 3 * P.part_floats);
   cx.cu = cu;
   cx.single = single;
   if (single >= 0) {
@@ -965,7 +965,7 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
     cx.q1 = ld_uniform(P.queue_ptr, cu + 1);
   }
   cx.lane = threadIdx.x & 63;
-  cx.recs = reinterpret_cast<StreamRec*>(cx.ring + (size_t)kStreams * P.ring_slots * 2 * kUnitBytes);
+  cx.recs = reinterpret_cast<StreamRec*>(cx.parts + 3 * P.part_floats);
   for (int j = threadIdx.x; j < kCtlBytes / 4; j += blockDim.x) cx.ctl[j] = 0;
   if (single < 0) {
     const int r0 = ld_uniform(P.srec_ptr, cu), r1 = ld_uniform(P.srec_ptr, cu + 1);
