@@ -338,8 +338,9 @@ struct Waits {
 __device__ __forceinline__ uint32_t* waits_area(const Ctx& cx) {
   return reinterpret_cast<uint32_t*>(cx.ctl) + kCtlWords + (threadIdx.x >> 6) * kWaitWords;
 }
+template <bool PROF>
 __device__ __forceinline__ void waits_init(const Params& P, const Ctx& cx, Waits& w) {
-  w.on = P.waits != nullptr;
+  w.on = PROF && P.waits != nullptr;
   w.c = waits_area(cx);
   if (w.on) w.c[4] = rfl32((uint32_t)wall_clock64());
 }
@@ -592,11 +593,12 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
   }
 }
 
+template <bool PROF>
 __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
   int last0 = -1, last1 = -1, last2 = -1, last3 = -1;  // last task staged into each slot
   Waits wt;  // slot free, dependency event, staging, tasks
-  waits_init(P, cx, wt);
+  waits_init<PROF>(P, cx, wt);
   for (int step = 0; step < P.n_steps; ++step) {
     const uint32_t epoch = P.epoch0 + (uint32_t)step;
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
@@ -619,7 +621,7 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
         if (!wait_event(P, cx, T.dep, thr * mult)) return;
       }
       waits_add(wt, 1, s0);
-      if (P.profile && cx.lane == 0) P.profile[((size_t)step * P.n_tasks + id) * kProfWords] = wall_clock64();
+      if (PROF && P.profile && cx.lane == 0) P.profile[((size_t)step * P.n_tasks + id) * kProfWords] = wall_clock64();
       if (qi == cx.q0) lds_st(&cx.ctl[C_STEPOK], step + 1);
       s0 = waits_now(wt);
       stage_task(P, cx, T, slot, step, pre);
@@ -894,10 +896,11 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
   }
 }
 
+template <bool PROF>
 __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
   Waits wt;  // staged, computed, epilogue, tasks
-  waits_init(P, cx, wt);
+  waits_init<PROF>(P, cx, wt);
   for (int step = 0; step < P.n_steps; ++step) {
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
       const int id = task_at(P, cx, qi);
@@ -918,7 +921,7 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
         if (P.use_events && id != P.drop_task)
           __hip_atomic_fetch_add(&P.counters[(size_t)T.trig * kEventWords + (cx.cu & (kStripes - 1)) * 32], 1u,
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (P.profile) {
+        if (PROF && P.profile) {
           uint64_t* rec = P.profile + ((size_t)step * P.n_tasks + id) * kProfWords;
           rec[1] = t_staged;
           rec[2] = t_computed;
@@ -944,7 +947,7 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
 // kernels
 // ---------------------------------------------------------------------------
 
-template <int NC, int DEPTH>
+template <int NC, int DEPTH, bool PROF>
 __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   extern __shared__ __align__(16) char smem[];
   Ctx cx;
@@ -993,19 +996,26 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   __syncthreads();
   // wave index as a wave-uniform value: every role's control flow is scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave == 0) run_stager(P, cx);
-  else if (wave == 1) run_retirer(P, cx);
-  else run_stream<DEPTH, NC>(P, cx, wave - kCtlWaves);
+  if (wave == 0) run_stager<PROF>(P, cx);
+  else if (wave == 1) run_retirer<PROF>(P, cx);
+  else run_stream<DEPTH, NC, PROF>(P, cx, wave - kCtlWaves);
 }
 
 // One kernel per (staged columns, ring depth): each holds the code of its own
-// variant only, which keeps the instruction working set of a workgroup small.
+// variant only, which keeps the instruction working set of a workgroup small
+// (it shares a 64 KiB instruction cache with a neighbouring compute unit). The
+// per-task timestamps and wait counters live in separate persistent variants
+// (mk_persistent_prof_*), launched only when a profile or wait-counter buffer
+// is set.
 #define MK_KERNELS(NC, DEPTH)                                                                           \
   extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent_b##NC##_d##DEPTH(Params P) {     \
-    run<NC, DEPTH>(P, blockIdx.x, -1);                                                                 \
+    run<NC, DEPTH, false>(P, blockIdx.x, -1);                                                          \
+  }                                                                                                    \
+  extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent_prof_b##NC##_d##DEPTH(Params P) { \
+    run<NC, DEPTH, true>(P, blockIdx.x, -1);                                                           \
   }                                                                                                    \
   extern "C" __global__ void __launch_bounds__(kThreads) mk_oplaunch_b##NC##_d##DEPTH(Params P, int first) { \
-    run<NC, DEPTH>(P, blockIdx.x, first + blockIdx.x);                                                 \
+    run<NC, DEPTH, false>(P, blockIdx.x, first + blockIdx.x);                                          \
   }
 MK_KERNELS(1, 11)
 MK_KERNELS(2, 11)
@@ -1035,6 +1045,11 @@ static const PersistentFn kPersistent[kDepths][kMaxCols] = {
     {mk_persistent_b1_d8, mk_persistent_b2_d8, mk_persistent_b3_d8, mk_persistent_b4_d8},
     {mk_persistent_b1_d6, mk_persistent_b2_d6, mk_persistent_b3_d6, mk_persistent_b4_d6},
     {mk_persistent_b1_d4, mk_persistent_b2_d4, mk_persistent_b3_d4, mk_persistent_b4_d4}};
+static const PersistentFn kPersistentProf[kDepths][kMaxCols] = {
+    {mk_persistent_prof_b1_d11, mk_persistent_prof_b2_d11, mk_persistent_prof_b3_d11, mk_persistent_prof_b4_d11},
+    {mk_persistent_prof_b1_d8, mk_persistent_prof_b2_d8, mk_persistent_prof_b3_d8, mk_persistent_prof_b4_d8},
+    {mk_persistent_prof_b1_d6, mk_persistent_prof_b2_d6, mk_persistent_prof_b3_d6, mk_persistent_prof_b4_d6},
+    {mk_persistent_prof_b1_d4, mk_persistent_prof_b2_d4, mk_persistent_prof_b3_d4, mk_persistent_prof_b4_d4}};
 static const OpFn kOplaunch[kDepths][kMaxCols] = {
     {mk_oplaunch_b1_d11, mk_oplaunch_b2_d11, mk_oplaunch_b3_d11, mk_oplaunch_b4_d11},
     {mk_oplaunch_b1_d8, mk_oplaunch_b2_d8, mk_oplaunch_b3_d8, mk_oplaunch_b4_d8},
@@ -1102,6 +1117,9 @@ hipError_t set_lds_limit(int bytes) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistent[d][c]),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistentProf[d][c]),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kOplaunch[d][c]),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (e != hipSuccess) return e;
@@ -1111,13 +1129,13 @@ hipError_t set_lds_limit(int bytes) {
 
 hipError_t persistent_occupancy(int lds, int depth, int* blocks_per_cu) {
   int worst = 1 << 30;
-  for (int c = 0; c < kMaxCols; ++c) {
-    int n = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &n, reinterpret_cast<const void*>(kPersistent[depth_index(depth)][c]), kThreads, lds);
-    if (e != hipSuccess) return e;
-    worst = n < worst ? n : worst;
-  }
+  for (int c = 0; c < kMaxCols; ++c)
+    for (const PersistentFn f : {kPersistent[depth_index(depth)][c], kPersistentProf[depth_index(depth)][c]}) {
+      int n = 0;
+      hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(f), kThreads, lds);
+      if (e != hipSuccess) return e;
+      worst = n < worst ? n : worst;
+    }
   *blocks_per_cu = worst;
   return hipSuccess;
 }
@@ -1127,8 +1145,9 @@ hipError_t launch_persistent(const Params& P, int grid, int lds, hipStream_t s) 
   if (P.batch < 1 || P.batch > kMaxCols) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kPersistent[depth_index(P.ring_slots)][P.batch - 1]),
-                                    dim3(grid), dim3(kThreads), args, lds, s);
+  const PersistentFn f = (P.profile || P.waits) ? kPersistentProf[depth_index(P.ring_slots)][P.batch - 1]
+                                                 : kPersistent[depth_index(P.ring_slots)][P.batch - 1];
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(f), dim3(grid), dim3(kThreads), args, lds, s);
 }
 
 hipError_t launch_op(const Params& P, int first, int count, int lds, hipStream_t s) {

@@ -277,8 +277,8 @@ __device__ __forceinline__ void mv_flush(Acc<NC>& A, float* pout, int cs, int rb
 
 // Attention state of one wave over its piece: G query heads, this lane's 8
 // dims of the query and of the output accumulator, and the running maximum and
-// denominator shared by the whole wave (one maximum for all lanes, so the
-// lanes' outputs only need adding at the end).
+// denominator of this lane's position group (the lanes that share a
+// position). The groups are merged once, at the end of the piece.
 struct AttState {
   float q[kMaxG][8], acc[kMaxG][8], m[kMaxG], l[kMaxG];
 };
@@ -305,10 +305,11 @@ __device__ __forceinline__ float in_group(float v) {
   return v;
 }
 
-// One item (position block) of attention: scores of the G heads, the block's
-// maximum, the rescale of the running state and the weighted values. Scores
-// are in base-2 units (the queries carry scale * log2(e)), so the
-// exponentials are the hardware's exp2.
+// One item (position block) of attention: for each of the G heads, the score
+// of this lane's position, and the online-softmax update of its group's
+// running maximum, denominator and weighted values. Scores are in base-2 units
+// (the queries carry scale * log2(e)), so the exponentials are the hardware's
+// exp2.
 template <int LPP>
 __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32x4 wk, const u32x4 wv, bool valid) {
   float kf[8], vf[8];
@@ -321,12 +322,10 @@ __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(S.q[h][e], kf[e], d);
       const float sc = valid ? in_group<LPP>(d) : -INFINITY;
-      const float mn = fmaxf(S.m[h], across_groups<true, LPP>(sc));
+      const float mn = fmaxf(S.m[h], sc);
       const float al = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(S.m[h] - mn);
       const float pe = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
-      // pe is equal on the lanes of a group, so the sum over groups of any
-      // one lane's pe is the block's denominator share, in every lane
-      S.l[h] = fmaf(S.l[h], al, across_groups<false, LPP>(pe));
+      S.l[h] = fmaf(S.l[h], al, pe);
 #pragma unroll
       for (int e = 0; e < 8; ++e) S.acc[h][e] = fmaf(pe, vf[e], S.acc[h][e] * al);
       S.m[h] = mn;
@@ -334,19 +333,25 @@ __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32
   }
 }
 
-// End of a wave's attention piece: add the lanes' outputs over the position
-// groups and store this wave's partial: acc[D] of each head (at [wave][head]),
-// then (m, l) of each head (at [wave][head] after all the accumulators), m in
-// natural-log units. A piece without items stores m = -inf, l = 0 and zeros.
+// End of a wave's attention piece: merge the position groups (with M the
+// largest group maximum, each group's denominator and values scaled by
+// 2^(m_g - M) and added over the groups) and store this wave's partial: acc[D]
+// of each head (at [wave][head]), then (m, l) of each head (at [wave][head]
+// after all the accumulators), m in natural-log units. A piece without items
+// stores m = -inf, l = 0 and zeros.
 template <int LPP>
 __device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* part, int s, int lane, bool empty) {
   const int D = P.D, G = P.G, de = (lane % LPP) * 8;
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     if (h < G) {
+      float M = -INFINITY, l = 0.f;
       if (!empty) {
+        M = across_groups<true, LPP>(S.m[h]);
+        const float f = S.m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m[h] - M);
+        l = across_groups<false, LPP>(S.l[h] * f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) S.acc[h][e] = across_groups<false, LPP>(S.acc[h][e]);
+        for (int e = 0; e < 8; ++e) S.acc[h][e] = across_groups<false, LPP>(S.acc[h][e] * f);
       }
       // every lane holds the sums of its dims (and the wave's m, l): lanes with
       // equal dims store equal values to the same words
@@ -354,8 +359,8 @@ __device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* 
       *reinterpret_cast<float4*>(dst + de) = make_float4(S.acc[h][0], S.acc[h][1], S.acc[h][2], S.acc[h][3]);
       *reinterpret_cast<float4*>(dst + de + 4) = make_float4(S.acc[h][4], S.acc[h][5], S.acc[h][6], S.acc[h][7]);
       float* ml = part + (size_t)kStreams * G * D + (s * G + h) * 2;
-      ml[0] = S.m[h] * kLn2;
-      ml[1] = S.l[h];
+      ml[0] = M * kLn2;
+      ml[1] = l;
     }
   }
 }
@@ -486,15 +491,15 @@ __device__ __forceinline__ void matvec_run(const Params& P, Comp& C, Fetch& F, i
 // stream wave
 // ---------------------------------------------------------------------------
 
-template <int DEPTH, int NC>
+template <int DEPTH, int NC, bool PROF>
 __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s) {
   const int lane = cx.lane, jrow = lane >> 4, icol = lane & 15;
   const uint32_t ring = lds_addr(cx.ring) + (uint32_t)s * DEPTH * kItemBytes;
   const uint8_t* rp = cx.ring + (size_t)s * DEPTH * kItemBytes + lane * 16;  // this lane's bytes of slot 0
-  const bool prof = P.profile != nullptr;
+  const bool prof = PROF && P.profile != nullptr;
   const int lpp = P.D / 8, ppi = 64 / lpp;
   Waits wt;  // j0: KV step not open; j2: task not staged; j3: items
-  waits_init(P, cx, wt);
+  waits_init<PROF>(P, cx, wt);
 
   Fetch F;
   F.r = -1;

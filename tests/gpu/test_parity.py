@@ -177,6 +177,42 @@ def test_tiny_generate_matches_stepwise():
     b.close()
 
 
+def test_instrumented_variant_matches():
+    """With a profile buffer and wait counters set, the persistent launch runs
+    the instrumented kernel variant: tokens and logits equal the plain
+    variant's, every task of every step has ordered timestamps, and the wait
+    counters are filled."""
+    import decode_persistent_megakernel_amd as mk
+    wl = workload.config(0)
+    a = session(0, "random")
+    b = session(0, "random")
+    prompt = workload.make_prompt(wl)[0]
+    for p in range(len(prompt) - 1):
+        a.decode_step([int(prompt[p])], [p], logits=False)
+        b.decode_step([int(prompt[p])], [p], logits=False)
+    P, K = len(prompt), 6
+    _, _, n_tasks, _, _, _ = mk.mk_model_info(b.model)
+    prof = torch.zeros(K * n_tasks * 12, dtype=torch.int64, device="cuda")
+    waits = torch.zeros(b.num_cus * 6 * 16, dtype=torch.int64, device="cuda")
+    mk.mk_set_profile_buffer(b.model, prof, prof.numel() * 8)
+    mk.mk_set_wait_counters(b.model, waits, waits.numel() * 8)
+    oa = a.generate([int(prompt[-1])], [P - 1], K, last_logits=True)
+    ob = b.generate([int(prompt[-1])], [P - 1], K, last_logits=True)
+    a.check()
+    b.check()
+    assert torch.equal(oa, ob)
+    assert torch.equal(a.logits[0], b.logits[0])
+    r = prof.view(K, n_tasks, 12).cpu().numpy().astype(np.int64)
+    # event seen <= staged <= computed <= signalled, all set
+    assert (r[:, :, 0] > 0).all() and (r[:, :, 3] > 0).all()
+    assert (r[:, :, 1] >= r[:, :, 0]).all() and (r[:, :, 2] >= r[:, :, 1]).all() and (r[:, :, 3] >= r[:, :, 2]).all()
+    assert int(waits.sum()) > 0
+    mk.mk_set_profile_buffer(b.model, None, 0)
+    mk.mk_set_wait_counters(b.model, None, 0)
+    a.close()
+    b.close()
+
+
 def test_device_errors_reported():
     import decode_persistent_megakernel_amd as mk
     wl = workload.config(0)
