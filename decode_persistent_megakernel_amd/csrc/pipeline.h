@@ -285,24 +285,27 @@ struct AttState {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Reduce over the position groups of a wave (lanes equal modulo LPP): max or sum.
-template <bool MAX, int LPP>
-__device__ __forceinline__ float across_groups(float v) {
+// Reduce over the position groups of a wave (lanes equal modulo lpp, which is
+// 8 or 16; l16: lpp is 16): max or sum. One code path for both head widths
+// keeps the kernel small.
+template <bool MAX>
+__device__ __forceinline__ float across_groups(float v, bool l16) {
   float lo, hi;
-  if constexpr (LPP <= 8) { xpair<8>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
-  if constexpr (LPP <= 16) { xpair<16>(v, lo, hi); v = MAX ? fmaxf(lo, hi) : lo + hi; }
+  xpair<8>(v, lo, hi);
+  v = l16 ? v : (MAX ? fmaxf(lo, hi) : lo + hi);
+  xpair<16>(v, lo, hi);
+  v = MAX ? fmaxf(lo, hi) : lo + hi;
   xpair<32>(v, lo, hi);
   return MAX ? fmaxf(lo, hi) : lo + hi;
 }
 
-// Sum over the LPP lanes of a position group.
-template <int LPP>
-__device__ __forceinline__ float in_group(float v) {
+// Sum over the lpp lanes of a position group.
+__device__ __forceinline__ float in_group(float v, bool l16) {
   v += dpp<kDppSwap1>(v);
   v += dpp<kDppSwap2>(v);
   v += dpp<kDppHalfMirror>(v);
-  if constexpr (LPP == 16) v += dpp<kDppMirror>(v);
-  return v;
+  const float w = v + dpp<kDppMirror>(v);
+  return l16 ? w : v;
 }
 
 // One item (position block) of attention: for each of the G heads, the score
@@ -310,8 +313,8 @@ __device__ __forceinline__ float in_group(float v) {
 // running maximum, denominator and weighted values. Scores are in base-2 units
 // (the queries carry scale * log2(e)), so the exponentials are the hardware's
 // exp2.
-template <int LPP>
-__device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32x4 wk, const u32x4 wv, bool valid) {
+__device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32x4 wk, const u32x4 wv, bool valid,
+                                         bool l16) {
   float kf[8], vf[8];
   unpack8(wk, kf);
   unpack8(wv, vf);
@@ -321,7 +324,7 @@ __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(S.q[h][e], kf[e], d);
-      const float sc = valid ? in_group<LPP>(d) : -INFINITY;
+      const float sc = valid ? in_group(d, l16) : -INFINITY;
       const float mn = fmaxf(S.m[h], sc);
       const float al = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(S.m[h] - mn);
       const float pe = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
@@ -339,19 +342,19 @@ __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32
 // of each head (at [wave][head]), then (m, l) of each head (at [wave][head]
 // after all the accumulators), m in natural-log units. A piece without items
 // stores m = -inf, l = 0 and zeros.
-template <int LPP>
 __device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* part, int s, int lane, bool empty) {
-  const int D = P.D, G = P.G, de = (lane % LPP) * 8;
+  const bool l16 = P.D == 128;
+  const int D = P.D, G = P.G, de = (lane % (l16 ? 16 : 8)) * 8;
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     if (h < G) {
       float M = -INFINITY, l = 0.f;
       if (!empty) {
-        M = across_groups<true, LPP>(S.m[h]);
+        M = across_groups<true>(S.m[h], l16);
         const float f = S.m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m[h] - M);
-        l = across_groups<false, LPP>(S.l[h] * f);
+        l = across_groups<false>(S.l[h] * f, l16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) S.acc[h][e] = across_groups<false, LPP>(S.acc[h][e] * f);
+        for (int e = 0; e < 8; ++e) S.acc[h][e] = across_groups<false>(S.acc[h][e] * f, l16);
       }
       // every lane holds the sums of its dims (and the wave's m, l): lanes with
       // equal dims store equal values to the same words
@@ -533,8 +536,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
       // ---- the compute cursor's task change: finish the task, start the next
       if (C.type >= 0) {
         if (C.type == T_ATT) {
-          if (lpp == 8) att_finish<8>(P, S, part, s, lane, C.t == 0);
-          else att_finish<16>(P, S, part, s, lane, C.t == 0);
+          att_finish(P, S, part, s, lane, C.t == 0);
         } else {
           if (C.pend) mv_flush<NC>(A, part + (size_t)s * P.ncap * P.wave_vrows + jrow, P.wave_vrows, C.rb - C.rb0, icol);
           // the row blocks this piece touched (b < a: none), for the retirer's sums
@@ -629,8 +631,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
       const uint8_t* it = rp + koff;
       const u32x4 w0 = ld_u32x4(it), w1 = ld_u32x4(it + kUnitBytes);
       const bool valid = C.lo + (C.u0 + C.t) * ppi + lane / lpp < C.end;
-      if (lpp == 8) att_item<8>(P, S, w0, w1, valid);
-      else att_item<16>(P, S, w0, w1, valid);
+      att_item(P, S, w0, w1, valid, lpp == 16);
       ++C.t;
       ++k;
       koff = next_slot_off<DEPTH>(koff);
