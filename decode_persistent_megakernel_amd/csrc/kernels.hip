@@ -688,22 +688,23 @@ __device__ __forceinline__ void retire_matvec(const Params& P, const Ctx& cx, co
     }
     return;
   }
-  for (int idx = lane; idx < ncols * R; idx += 64) {
-    const int c = idx / R, r = idx - c * R;
-    switch (T.type) {
-      case T_QKV:
-        st_coh(P.qkv + ((size_t)c * P.Hkv + T.g) * (P.G + 2) * P.D + T.row0 + r, part_sum(P, pr, part, c, r) * hdr[c]);
-        break;
-      case T_GU: {
+  for (int c = 0; c < ncols; ++c) {
+    const float nf = hdr[c];  // RMS-norm factor of column c (QKV, GU)
+    if (T.type == T_QKV) {
+      float* dst = P.qkv + ((size_t)c * P.Hkv + T.g) * (P.G + 2) * P.D + T.row0;
+      for (int r = lane; r < R; r += 64) st_coh(dst + r, part_sum(P, pr, part, c, r) * nf);
+    } else if (T.type == T_GU) {
+      float* dst = P.mlp + (size_t)c * P.F + T.row0;
+      for (int r = lane; r < R; r += 64) {
         const int vr = 8 * (r >> 2) + (r & 3);
-        const float gt = part_sum(P, pr, part, c, vr) * hdr[c];
-        const float up = part_sum(P, pr, part, c, vr + 4) * hdr[c];
-        st_coh(P.mlp + (size_t)c * P.F + T.row0 + r, gt / (1.0f + expf(-gt)) * up);
-        break;
+        const float gt = part_sum(P, pr, part, c, vr) * nf;
+        const float up = part_sum(P, pr, part, c, vr + 4) * nf;
+        st_coh(dst + r, gt / (1.0f + expf(-gt)) * up);
       }
-      default:  // O, D: residual add
-        st_coh(P.x + (size_t)c * P.H + T.row0 + r, res[(size_t)c * P.res_stride + r] + part_sum(P, pr, part, c, r));
-        break;
+    } else {  // O, D: residual add
+      float* dst = P.x + (size_t)c * P.H + T.row0;
+      const float* rs = res + (size_t)c * P.res_stride;
+      for (int r = lane; r < R; r += 64) st_coh(dst + r, rs[r] + part_sum(P, pr, part, c, r));
     }
   }
 }
