@@ -436,6 +436,8 @@ __device__ __forceinline__ void stage_matvec_pre(const Params& P, const Ctx& cx,
   }
 }
 
+// NC: sequences staged, the call's batch (each kernel variant runs one batch size)
+template <int NC>
 __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, const DevTask& T, int slot,
                                              const StagePre& pre) {
   float* hdr = slot_ptr(cx, slot);
@@ -443,7 +445,7 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
   float* in = hdr + kHdr;
   float* res = in + (size_t)P.ncap * kp;
   const int lane = cx.lane;
-  const int ncols = P.batch;
+  constexpr int ncols = NC;
   const int K = T.kdim;
   if (is_normed(T.type)) {
     for (int c = 0; c < ncols; ++c) {
@@ -555,6 +557,7 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
 // offset of the second staged array of merge / argmax tasks
 __device__ __forceinline__ int second_off(int n) { return (n + 255) & ~255; }
 
+template <int NC>
 __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step,
                                            const StagePre& pre) {
   float* hdr = slot_ptr(cx, slot);
@@ -589,11 +592,11 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
                  P.n_lm);
       break;
     }
-    default: stage_matvec(P, cx, T, slot, pre); break;
+    default: stage_matvec<NC>(P, cx, T, slot, pre); break;
   }
 }
 
-template <bool PROF>
+template <int NC, bool PROF>
 __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
   int last0 = -1, last1 = -1, last2 = -1, last3 = -1;  // last task staged into each slot
@@ -624,7 +627,7 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
       if (PROF && P.profile && cx.lane == 0) P.profile[((size_t)step * P.n_tasks + id) * kProfWords] = wall_clock64();
       if (qi == cx.q0) lds_st(&cx.ctl[C_STEPOK], step + 1);
       s0 = waits_now(wt);
-      stage_task(P, cx, T, slot, step, pre);
+      stage_task<NC>(P, cx, T, slot, step, pre);
       waits_add(wt, 2, s0);
       waits_count(wt, 3, 1);
       lds_st(&cx.ctl[C_STAGED], i + 1);
@@ -664,11 +667,13 @@ __device__ __forceinline__ float part_sum(const Params& P, const PieceRows& pr, 
   return s;
 }
 
+template <int NC>
 __device__ __forceinline__ void retire_matvec(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
   const float* hdr = slot_ptr(cx, slot);
   const float* res = hdr + kHdr + (size_t)P.ncap * slot_kp(P, slot);
   const float* part = part_ptr(cx, slot);
-  const int lane = cx.lane, ncols = P.batch, R = T.row1 - T.row0;
+  const int ncols = P.batch;
+  const int lane = cx.lane, R = T.row1 - T.row0;
   const PieceRows pr = piece_rows(cx, slot);
   if (T.type == T_LM) {
     const bool last = step == P.n_steps - 1;
@@ -793,6 +798,7 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
   }
 }
 
+template <int NC>
 __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
   const float* hdr = slot_ptr(cx, slot);
   const float* data = hdr + kHdr;
@@ -893,11 +899,11 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
       }
       break;
     }
-    default: retire_matvec(P, cx, T, slot, step); break;
+    default: retire_matvec<NC>(P, cx, T, slot, step); break;
   }
 }
 
-template <bool PROF>
+template <int NC, bool PROF>
 __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
   int i = 0, nsmall = 0;
   Waits wt;  // staged, computed, epilogue, tasks
@@ -914,7 +920,7 @@ __device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
       if (has_stream(T.type) && !spin_ctl(P, cx, C_DONE + ctl_slot(slot), kStreams)) return;
       const uint64_t t_computed = wall_clock64();
       waits_count(wt, 1, (uint32_t)(t_computed - t_staged));
-      retire_task(P, cx, T, slot, step);
+      retire_task<NC>(P, cx, T, slot, step);
       wait_all();  // every store of the epilogue has completed
       waits_add(wt, 2, t_computed);
       waits_count(wt, 3, 1);
@@ -997,8 +1003,8 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   __syncthreads();
   // wave index as a wave-uniform value: every role's control flow is scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave == 0) run_stager<PROF>(P, cx);
-  else if (wave == 1) run_retirer<PROF>(P, cx);
+  if (wave == 0) run_stager<NC, PROF>(P, cx);
+  else if (wave == 1) run_retirer<NC, PROF>(P, cx);
   else run_stream<DEPTH, NC, PROF>(P, cx, wave - kCtlWaves);
 }
 
