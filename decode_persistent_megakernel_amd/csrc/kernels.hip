@@ -165,6 +165,20 @@ __device__ __forceinline__ void wave_argmax(float& best, int& bi) {
   argmax_step<32>(best, bi);
 }
 
+// The kernel arguments read through a pointer the compiler cannot prove equal
+// to any earlier one. Each role takes a fresh view at the top of its per-task
+// loop, so the fields are loaded again there (scalar loads from the argument
+// segment, which stays unchanged for the whole launch) instead of being held
+// in scalar registers across the whole kernel, where they spilled to vector
+// lanes. Every kernel of this file takes its Params as the first argument,
+// which the HSA kernel ABI places at offset 0 of the argument segment.
+__device__ __forceinline__ const Params& fresh_params() {
+  using KP = const __attribute__((address_space(4))) Params*;
+  KP p = (KP)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const Params*)p;
+}
+
 template <class T>
 __device__ __forceinline__ T ld_coh(const T* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -597,7 +611,8 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
 }
 
 template <int NC, bool PROF>
-__device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
+__device__ __forceinline__ void run_stager(const Params& P0, const Ctx& cx) {
+  const Params& P = P0;
   int i = 0, nsmall = 0;
   int last0 = -1, last1 = -1, last2 = -1, last3 = -1;  // last task staged into each slot
   Waits wt;  // slot free, dependency event, staging, tasks
@@ -605,6 +620,7 @@ __device__ __forceinline__ void run_stager(const Params& P, const Ctx& cx) {
   for (int step = 0; step < P.n_steps; ++step) {
     const uint32_t epoch = P.epoch0 + (uint32_t)step;
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
+      const Params& P = fresh_params();
       const int id = task_at(P, cx, qi);
       const DevTask T = ld_task(P, id);
       const int slot = next_slot(nsmall, T.type);
@@ -904,12 +920,14 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
 }
 
 template <int NC, bool PROF>
-__device__ __forceinline__ void run_retirer(const Params& P, const Ctx& cx) {
+__device__ __forceinline__ void run_retirer(const Params& P0, const Ctx& cx) {
+  const Params& P = P0;
   int i = 0, nsmall = 0;
   Waits wt;  // staged, computed, epilogue, tasks
   waits_init<PROF>(P, cx, wt);
   for (int step = 0; step < P.n_steps; ++step) {
     for (int qi = cx.q0; qi < cx.q1; ++qi, ++i) {
+      const Params& P = fresh_params();
       const int id = task_at(P, cx, qi);
       const DevTask T = ld_task(P, id);
       const int slot = next_slot(nsmall, T.type);

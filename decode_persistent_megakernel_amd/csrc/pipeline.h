@@ -495,7 +495,8 @@ __device__ __forceinline__ void matvec_run(const Params& P, Comp& C, Fetch& F, i
 // ---------------------------------------------------------------------------
 
 template <int DEPTH, int NC, bool PROF>
-__device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s) {
+__device__ __forceinline__ void run_stream(const Params& P0, const Ctx& cx, int s) {
+  const Params& P = P0;
   const int lane = cx.lane, jrow = lane >> 4, icol = lane & 15;
   const uint32_t ring = lds_addr(cx.ring) + (uint32_t)s * DEPTH * kItemBytes;
   const uint8_t* rp = cx.ring + (size_t)s * DEPTH * kItemBytes + lane * 16;  // this lane's bytes of slot 0
@@ -528,6 +529,7 @@ __device__ __forceinline__ void run_stream(const Params& P, const Ctx& cx, int s
   F.soff = 0;
 
   for (;;) {
+    const Params& P = fresh_params();
     // refill every slot whose item has been read
     wait_lgkm();
     fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
