@@ -397,16 +397,21 @@ __device__ __forceinline__ bool has_stream(int type) {
 // Wait until the striped counter of `ev` reaches `need` (coherent polling).
 __device__ __forceinline__ bool wait_event(const Params& P, const Ctx& cx, int ev, uint32_t need) {
   const uint64_t t0 = wall_clock64();
+  // lanes 0..7 read the stripes and lane 8 the abort flag: one load, so each
+  // poll costs a single memory round trip
+  const uint32_t* src = cx.lane < kStripes ? &P.counters[(size_t)ev * kEventWords + cx.lane * 32]
+                                           : reinterpret_cast<const uint32_t*>(P.abort_flag);
   for (;;) {
     uint32_t v = 0;
-    if (cx.lane < kStripes) v = ld_coh(&P.counters[(size_t)ev * kEventWords + cx.lane * 32]);
+    if (cx.lane <= kStripes) v = ld_coh(src);
+    const uint32_t aborted = __builtin_amdgcn_readlane(v, kStripes);
     // sum of the 8 stripes in lanes 0..7 (integer adds, any order)
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppSwap1, 0xF, 0xF, false);
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppSwap2, 0xF, 0xF, false);
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, false);
     v = __builtin_amdgcn_readfirstlane(v);
     if ((int32_t)(v - need) >= 0) break;
-    if (__builtin_amdgcn_readfirstlane(ld_coh(P.abort_flag)) || lds_ld(&cx.ctl[C_ABORT])) {
+    if (aborted || lds_ld(&cx.ctl[C_ABORT])) {
       if (cx.lane == 0) __hip_atomic_store(&cx.ctl[C_ABORT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       return false;
     }
