@@ -524,7 +524,18 @@ __device__ __forceinline__ float* att_part_ptr(const Params& P, const Ctx& cx, i
   return slot_ptr(cx, slot) + kHdr + att_raw_floats(P) + P.G * P.D + 2 * P.D + P.D;
 }
 
-__device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
+// Before the event wait: the RoPE (cos, sin) pair jj = lane of the position
+// the task appends, which does not depend on the event (held in pre.g[0]).
+__device__ __forceinline__ void stage_att_pre(const Params& P, const Ctx& cx, const DevTask& T, int step,
+                                              StagePre& pre) {
+  const int p = T.b < P.batch ? ld_uniform(P.pos_in, T.b) + step : -1;
+  float2 cs = make_float2(0.f, 0.f);
+  if (p >= 0 && p < P.S && cx.lane < P.D / 2) cs = P.rope_cs[(size_t)p * (P.D / 2) + cx.lane];
+  pre.g[0] = make_uint2(__float_as_uint(cs.x), __float_as_uint(cs.y));
+}
+
+__device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step,
+                                          const StagePre& pre) {
   float* hdr = slot_ptr(cx, slot);
   int* ih = reinterpret_cast<int*>(hdr);
   float* raw = hdr + kHdr;
@@ -550,10 +561,13 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
   }
   if (!valid) return;
   stage_copy(cx, P.qkv + ((size_t)T.b * P.Hkv + T.g) * GR, raw, GR);
-  for (int idx = lane; idx < (G + 1) * Dh; idx += 64) {
+  // whole-wave iterations: the (cos, sin) pair comes from lane jj of pre
+  for (int base = 0; base < (G + 1) * Dh; base += 64) {
+    const int idx = base + lane;
     const int h = idx / Dh, jj = idx - h * Dh;
+    const float2 cs = make_float2(__uint_as_float(__shfl(pre.g[0].x, jj, 64)), __uint_as_float(__shfl(pre.g[0].y, jj, 64)));
+    if (idx >= (G + 1) * Dh) continue;
     const float a = raw[h * D + jj], b = raw[h * D + jj + Dh];
-    const float2 cs = P.rope_cs[(size_t)p * Dh + jj];
     const float r0 = a * cs.x - b * cs.y, r1 = b * cs.x + a * cs.y;
     if (h < G) {
       q[h * D + jj] = r0;
@@ -596,7 +610,7 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
       wait_all();
       break;
     }
-    case T_ATT: stage_att(P, cx, T, slot, step); break;
+    case T_ATT: stage_att(P, cx, T, slot, step, pre); break;
     case T_COMB: {
       if (T.b >= P.batch) break;
       const size_t head0 = (size_t)T.b * P.Hq + (size_t)T.g * P.G;
@@ -638,6 +652,8 @@ __device__ __forceinline__ void run_stager(const Params& P0, const Ctx& cx) {
       StagePre pre;
       if (T.type == T_QKV || T.type == T_O || T.type == T_GU || T.type == T_D || T.type == T_LM)
         stage_matvec_pre(P, cx, T, slot, pre);
+      else if (T.type == T_ATT)
+        stage_att_pre(P, cx, T, step, pre);
       s0 = waits_now(wt);
       if (P.use_events) {
         const uint32_t mult = T.type == T_EMB ? epoch : epoch + 1;
