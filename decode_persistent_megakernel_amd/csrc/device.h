@@ -30,7 +30,7 @@ constexpr int kMinDepth = 4;   // fewer cannot hide the copy latency
 constexpr int kMaxCols = 4;    // sequences a matvec task handles
 constexpr int kMaxBatch = 256; // sequences a model holds (larger calls run in groups of at most kMaxCols)
 constexpr int kMaxG = 4;       // query heads per kv head
-constexpr int kStripes = 8;    // event counter stripes (one per XCD)
+constexpr int kStripes = 64;   // event counter stripes: one per lane of the polling wave
 constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte line
 constexpr int kCtlBytes = 1024;             // control words + ring metadata (see kernels)
 constexpr int kWaves = kThreads / 64;

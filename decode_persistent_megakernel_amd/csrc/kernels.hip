@@ -397,18 +397,25 @@ __device__ __forceinline__ bool has_stream(int type) {
 // Wait until the striped counter of `ev` reaches `need` (coherent polling).
 __device__ __forceinline__ bool wait_event(const Params& P, const Ctx& cx, int ev, uint32_t need) {
   const uint64_t t0 = wall_clock64();
-  // lanes 0..7 read the stripes and lane 8 the abort flag: one load, so each
-  // poll costs a single memory round trip
-  const uint32_t* src = cx.lane < kStripes ? &P.counters[(size_t)ev * kEventWords + cx.lane * 32]
-                                           : reinterpret_cast<const uint32_t*>(P.abort_flag);
+  // each lane reads one stripe; the abort word is read in the same round trip
+  static_assert(kStripes == 64, "one stripe per lane");
+  const uint32_t* src = &P.counters[(size_t)ev * kEventWords + cx.lane * 32];
   for (;;) {
-    uint32_t v = 0;
-    if (cx.lane <= kStripes) v = ld_coh(src);
-    const uint32_t aborted = __builtin_amdgcn_readlane(v, kStripes);
-    // sum of the 8 stripes in lanes 0..7 (integer adds, any order)
+    uint32_t v = ld_coh(src);
+    const uint32_t aborted = __builtin_amdgcn_readfirstlane(ld_coh(P.abort_flag));
+    // sum over the wave (integer adds, any order)
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppSwap1, 0xF, 0xF, false);
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppSwap2, 0xF, 0xF, false);
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xF, 0xF, false);
+    {
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      v = r[0] + r[1];
+    }
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      v = r[0] + r[1];
+    }
     v = __builtin_amdgcn_readfirstlane(v);
     if ((int32_t)(v - need) >= 0) break;
     if (aborted || lds_ld(&cx.ctl[C_ABORT])) {
