@@ -22,8 +22,9 @@
 // Cross-compute-unit data moves with device-coherent (sc1) loads and stores;
 // a producer waits for its stores to complete before it counts the event, and
 // a consumer reads the inputs only after it has seen the count, so no cache
-// writeback or invalidate is needed. Event counters are split into 8 stripes
-// (one per XCD) to spread the atomic traffic.
+// writeback or invalidate is needed. Event counters are split into 64 stripes
+// (four producer CUs of one XCD per stripe) to spread the atomic traffic; a
+// poll reads all of them with one load per lane.
 //
 // mk_oplaunch runs the same roles on a one-task queue per workgroup with no
 // event waits: one launch per operator (the conventional many-kernel engine
