@@ -171,8 +171,9 @@ __device__ __forceinline__ void wave_argmax(float& best, int& bi) {
 // loop, so the fields are loaded again there (scalar loads from the argument
 // segment, which stays unchanged for the whole launch) instead of being held
 // in scalar registers across the whole kernel, where they spilled to vector
-// lanes. Every kernel of this file takes its Params as the first argument,
-// which the HSA kernel ABI places at offset 0 of the argument segment.
+// lanes. Only the kernels that run the roles (mk_persistent*, mk_oplaunch*)
+// call this; each takes its Params as the first argument, which the HSA kernel
+// ABI places at offset 0 of the argument segment.
 __device__ __forceinline__ const Params& fresh_params() {
   using KP = const __attribute__((address_space(4))) Params*;
   KP p = (KP)__builtin_amdgcn_kernarg_segment_ptr();
