@@ -4,11 +4,18 @@ persistent decode megakernel on one MI355X.
 Workload (default): the Llama-3.2-1B-shaped decoder at batch 1, seeded random
 bf16 weights, a 39-token prompt consumed untimed, then K greedy decode steps
 inside ONE persistent launch (mk_generate), timed with HIP events on the
-launch stream. The prompt and the W warm-up steps run on the per-operator
-path, so the timed launch is the run's only mk_persistent dispatch (a
-profiler's average for that kernel is the timed launch). Also timed, for
-context: the same steps with one launch per operator (the baseline built from
-the same task bodies), and the CPU oracle on a bounded sample.
+launch stream. W untimed warm-up steps run first as one persistent launch of
+their own from the same start (it writes the same cache positions with the
+same values the timed launch writes again), so the timed launch is a warm
+kernel. Also timed, for context: the same steps with one launch per operator
+(the baseline built from the same task bodies), and the CPU oracle on a
+bounded sample.
+
+Correctness of the timed launch: the per-operator leg replays its first steps
+feeding the timed launch's own tokens, and every next token it computes must
+equal the token the timed launch chose at that step (the two paths are
+bit-identical by construction); any difference exits with status 3 before the
+JSON line is printed.
 
 Prints one JSON line (rank 0). `--gpus N` with N > 1 exits: this build runs on
 one GPU.
@@ -51,8 +58,9 @@ KERNEL_SOURCES = [os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc",
 def recorded_traffic(kernel: str, workload_name: str, steps: int, batch: int):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain copy of known size), if recorded for this
-    kernel variant, workload and step count with the kernel sources as they are
-    now; else None."""
+    kernel variant, workload, batch and step count with the kernel sources as
+    they are now; else None. The record holds one entry per measured step
+    count."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_b{batch}_hbm_traffic.json")
     try:
@@ -63,9 +71,11 @@ def recorded_traffic(kernel: str, workload_name: str, steps: int, batch: int):
     for f in KERNEL_SOURCES:
         h.update(open(f, "rb").read())
     if (rec.get("kernel_source_sha256") != h.hexdigest() or rec.get("workload") != workload_name
-            or rec.get("steps") != steps or rec.get("batch") != batch):
+            or rec.get("batch") != batch):
         return None
-    return int(rec["traffic_bytes_per_launch"])
+    per_steps = rec.get("traffic_bytes_per_launch_by_steps", {})
+    v = per_steps.get(str(steps))
+    return int(v) if v is not None else None
 
 
 def cpu_baseline(wl, weights, seconds: float = 15.0):
@@ -100,7 +110,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (1: Llama-3.2-1B shape)")
     ap.add_argument("--oplaunch-steps", type=int, default=32, help="steps timed for the per-operator baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -159,43 +169,61 @@ def main():
 
     stream = torch.cuda.current_stream()
     out = torch.zeros((max(K, 1), B), dtype=torch.int32, device="cuda")
-    tok = list(tok0)
-    for k in range(W):  # warm-up steps (positions pos0.. are written again by the timed launch)
-        nxt, _ = ss.decode_step(tok, [p + k for p in pos0], mode=MK_MODE_OPLAUNCH, logits=False)
-        tok = [int(x) for x in nxt.cpu().tolist()]
-    torch.cuda.synchronize()
+    from decode_persistent_megakernel_amd import mk_decode_step, mk_generate
+    ss.set_inputs(tok0, pos0)  # device token / position buffers, filled before any timing
+    if W > 0:  # warm-up: one untimed persistent launch from the same start
+        wout = torch.zeros((W, B), dtype=torch.int32, device="cuda")
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        mk_generate(ss.model, ss.tok, ss.pos, B, W, wout)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        ss.check()
+        log(f"warm-up launch: {W} steps in {w0.elapsed_time(w1):.3f} ms")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record(stream)
-    ss.generate(tok0, pos0, K, out=out[:K])
+    mk_generate(ss.model, ss.tok, ss.pos, B, K, out[:K])
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ss.check()
     ms = e0.elapsed_time(e1)
+    if W > 0 and K == W:
+        assert torch.equal(wout, out[:K]), "the warm-up and timed launches chose different tokens"
     us_tok = ms * 1e3 / K
     bytes_launch = sum(algorithmic_bytes(wl.shape, [p + k for p in pos0]) for k in range(K))
     achieved = bytes_launch / (ms * 1e-3) / 1e9
     log(f"megakernel: {K} steps in {ms:.3f} ms (wall {wall * 1e3:.1f} ms): {us_tok:.2f} us/step, "
         f"{achieved:.1f} GB/s algorithmic")
 
-    # per-operator-launch baseline (same task bodies), a shorter run
+    # per-operator-launch baseline (same task bodies), a shorter run that
+    # replays the timed launch's steps: step k feeds the token the timed launch
+    # fed, and its next token must equal the one the timed launch chose
     Kb = min(args.oplaunch_steps, K)
     toks_b = out[:Kb].cpu().tolist()
-    from decode_persistent_megakernel_amd import mk_decode_step
+    tok_in = torch.as_tensor([tok0] + toks_b[:Kb - 1], dtype=torch.int32, device="cuda")
+    pos_in = torch.as_tensor([[p + k for p in pos0] for k in range(Kb)], dtype=torch.int32, device="cuda")
+    chk = torch.full((Kb, B), -1, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for k in range(Kb):
-        ss.tok[:B] = torch.as_tensor(tok0 if k == 0 else toks_b[k - 1], dtype=torch.int32)
-        ss.pos[:B] = torch.as_tensor([p + k for p in pos0], dtype=torch.int32)
-        mk_decode_step(ss.model, ss.tok, ss.pos, B, None, ss.next, MK_MODE_OPLAUNCH)
+        mk_decode_step(ss.model, tok_in[k], pos_in[k], B, None, chk[k], MK_MODE_OPLAUNCH)
     b1.record(stream)
     torch.cuda.synchronize()
     ss.check()
     us_b = b0.elapsed_time(b1) * 1e3 / Kb
     log(f"per-operator launches: {us_b:.2f} us/step over {Kb} steps")
+    bad = (chk != out[:Kb]).nonzero().cpu().tolist()
+    if bad:
+        k, b_ = bad[0]
+        log(f"MISMATCH: the timed launch chose token {toks_b[k][b_]} at step {k} (sequence {b_}), the per-operator "
+            f"replay {int(chk[k, b_])}; {len(bad)} differing entries")
+        ss.close()
+        sys.exit(3)
+    log(f"timed launch checked: {Kb} steps x {B} sequence(s) equal the per-operator replay")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -221,6 +249,7 @@ def main():
                      "kernel": kernel, "launch_ms": round(ms, 4),
                      "bytes_per_launch": bytes_launch},
         "oplaunch_baseline_us_per_step": round(us_b, 3),
+        "timed_launch_checked_steps": Kb,
         "cpu_baseline": cpu,
     }
     if B > 1:

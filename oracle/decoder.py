@@ -146,9 +146,15 @@ class Model:
 
     # -- one decode step -----------------------------------------------------
     def decode_step(self, st: State, tokens: Sequence[int], pos: Sequence[int],
-                    want_hidden: bool = False):
+                    want_hidden: bool = False, kv_given: bool = False):
         """Feed ``tokens[b]`` at position ``pos[b]``; write K/V there; return
-        float64 logits ``[B, V]`` (and the final hidden states if asked)."""
+        float64 logits ``[B, V]`` (and the final hidden states if asked).
+
+        ``kv_given=True`` leaves the cache entries at ``pos[b]`` as the state
+        holds them (written by another implementation of the same step) and
+        attends over those instead of this step's own rounding of K/V; the
+        arithmetic is otherwise unchanged. Tests use it to compare logits over
+        one identical cache."""
         s = self.s
         B = len(tokens)
         G, D = s.group, s.head_dim
@@ -159,21 +165,22 @@ class Model:
             ga = bf16.decode(self.w[f"l{l}.g_attn"])
             gm = bf16.decode(self.w[f"l{l}.g_mlp"])
             attn = np.zeros((B, s.n_q_heads * D))
+            h = rmsnorm(x, ga, s.rms_eps)                           # [B, H]
+            qs = (h @ wq.T).reshape(B, s.n_q_heads, D)
+            ks = (h @ wk.T).reshape(B, s.n_kv_heads, D)
+            vs = (h @ wv.T).reshape(B, s.n_kv_heads, D)
             for b in range(B):
                 p = int(pos[b])
-                h = rmsnorm(x[b], ga, s.rms_eps)
-                q = (wq @ h).reshape(s.n_q_heads, D)
-                k = (wk @ h).reshape(s.n_kv_heads, D)
-                v = (wv @ h).reshape(s.n_kv_heads, D)
-                q = rope(q, p, s.rope_theta)
-                k = rope(k, p, s.rope_theta)
-                st.kcache[l, b, :, p] = self._store(k)
-                st.vcache[l, b, :, p] = self._store(v)
-                for hq in range(s.n_q_heads):
-                    g = hq // G
+                q = rope(qs[b], p, s.rope_theta)
+                k = rope(ks[b], p, s.rope_theta)
+                if not kv_given:
+                    st.kcache[l, b, :, p] = self._store(k)
+                    st.vcache[l, b, :, p] = self._store(vs[b])
+                for g in range(s.n_kv_heads):
                     kk = self._load(st.kcache[l, b, g, : p + 1])
                     vv = self._load(st.vcache[l, b, g, : p + 1])
-                    attn[b, hq * D:(hq + 1) * D] = attend(q[hq], kk, vv)
+                    for hq in range(g * G, (g + 1) * G):
+                        attn[b, hq * D:(hq + 1) * D] = attend(q[hq], kk, vv)
             x = x + attn @ wo.T
             wg, wu, wd = self.W(f"l{l}.wg"), self.W(f"l{l}.wu"), self.W(f"l{l}.wd")
             h2 = rmsnorm(x, gm, s.rms_eps)

@@ -25,3 +25,21 @@ def gpu_available() -> bool:
 def tiny_shape():
     import workload
     return workload.config(0).shape
+
+
+def pytest_runtest_logstart(nodeid, location):
+    """Start of every test, also as a line in gpurun_out/pytest_progress.log
+    when that folder exists (long GPU tests are otherwise silent under -q)."""
+    _progress(f"start {nodeid}")
+
+
+def pytest_runtest_logfinish(nodeid, location):
+    _progress(f"end {nodeid}")
+
+
+def _progress(line: str):
+    import time
+    d = os.path.join(ROOT, "gpurun_out")
+    if os.path.isdir(d):
+        with open(os.path.join(d, "pytest_progress.log"), "a") as f:
+            f.write(f"{time.strftime('%H:%M:%S')} {line}\n")

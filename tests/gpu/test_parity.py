@@ -14,13 +14,19 @@ import pytest
 
 import workload
 from oracle import bf16
-from tests.helpers import oracle_model, weights
+from tests.helpers import oracle_model, progress, weights
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 GOLDEN = os.path.join(os.path.dirname(os.path.dirname(__file__)), "golden", "tiny_greedy.json")
 MAX_ABS, REL_L2 = 3e-2, 1e-2
+# Logits when the oracle attends over the very cache entries the kernel wrote
+# (copied from the device): what is left is fp32 against fp64 accumulation.
+SHARED_REL_L2 = 1e-4
+# Fraction of layer-0 KV-cache entries allowed to differ by one rounding
+# (kv_close); 1.5e-4 was observed on the 1B shape's prompt.
+KV_LAYER0_FRAC = 1e-3
 
 
 def session(cfg, gains="ones", opts=None, max_batch=None, max_seq=None, shape=None, w=None, kv=None):
@@ -28,32 +34,52 @@ def session(cfg, gains="ones", opts=None, max_batch=None, max_seq=None, shape=No
     wl = workload.config(cfg)
     if w is None:
         _, w = weights(cfg, gains)
-    print(f"[session] cfg={cfg} gains={gains} opts={opts and tuple(getattr(opts, f[0]) for f in opts._fields_)}",
-          flush=True)
+    progress(f"[session] cfg={cfg} gains={gains} opts={opts and tuple(getattr(opts, f[0]) for f in opts._fields_)}")
     return S.Session(shape or wl.shape, w, max_batch or wl.batch, max_seq or wl.max_seq, opts, kv=kv)
 
 
 def check_logits(gpu: np.ndarray, ref: np.ndarray, what: str):
     err = np.abs(gpu - ref)
     rel = np.linalg.norm(gpu - ref) / np.linalg.norm(ref)
-    print(f"[{what}] max-abs {err.max():.3e} rel-L2 {rel:.3e}", flush=True)
+    progress(f"[{what}] max-abs {err.max():.3e} rel-L2 {rel:.3e}")
     assert err.max() <= MAX_ABS and rel <= REL_L2, (what, err.max(), rel)
     return err.max(), rel
 
 
-def kv_close(got_u16, ref_u16, max_frac=1e-2):
-    """bf16 caches equal up to one bf16 step (relative) plus 1e-3 of the
-    tensor's rms (absolute), with differences in at most max_frac of entries."""
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 values at |x| (7 stored mantissa bits): 2^(e-7) for
+    |x| in [2^e, 2^(e+1)); the smallest normal's spacing below it."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def kv_close(got_u16, ref_u16, what="kv", layer0_frac=KV_LAYER0_FRAC):
+    """bf16 caches [L][...] written by the kernel against the oracle's.
+
+    Layer 0's inputs are identical on both sides (the embedding row), so its
+    entries may differ only by one rounding: |got - ref| at most one bf16 ulp
+    of the larger magnitude plus 1e-3 of the tensor's rms (RoPE's rotation can
+    leave a small remainder of cancellation whose fp32 and fp64 values round
+    differently), in fewer than layer0_frac of the entries. Later layers see
+    inputs that already differ by the earlier layers' rounding (each side
+    attends over its own cache), so their entries are held to the logits' bar
+    instead: per layer, rel-L2 <= REL_L2. Fractions and errors are printed."""
     g = bf16.decode(np.asarray(got_u16, dtype=np.uint16))
     r = bf16.decode(np.asarray(ref_u16, dtype=np.uint16))
-    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
-    tol = np.maximum(np.abs(g), np.abs(r)) * 2.0 ** -8 + 1e-3 * rms
-    d = np.abs(g - r)
-    ok = bool(np.all(d <= tol)) and float((d > 0).mean() if d.size else 0.0) < max_frac
-    if not ok:
+    g0, r0 = g[0], r[0]
+    rms = float(np.sqrt(np.mean(r0 * r0))) if r0.size else 0.0
+    tol = bf16_ulp(np.maximum(np.abs(g0), np.abs(r0))) + 1e-3 * rms
+    d = np.abs(g0 - r0)
+    f0 = float((d > 0).mean()) if d.size else 0.0
+    ok0 = bool(np.all(d <= tol)) and f0 < layer0_frac
+    rel = [float(np.linalg.norm(g[l] - r[l]) / max(np.linalg.norm(r[l]), 1e-30)) for l in range(1, g.shape[0])]
+    worst = max(rel) if rel else 0.0
+    progress(f"[{what}] layer 0: differing entries {f0:.2e} (limit {layer0_frac:.0e}); "
+             f"later layers: largest rel-L2 {worst:.2e} (limit {REL_L2:.0e}); {d.size} entries per layer")
+    if not ok0:
         i = np.unravel_index(int(np.argmax(d - tol)), d.shape)
-        print(f"kv mismatch at {i}: got {g[i]!r} ref {r[i]!r} tol {tol[i]!r}; differing {(d > 0).mean():.2e}")
-    return ok
+        print(f"kv mismatch in layer 0 at {i}: got {g0[i]!r} ref {r0[i]!r} tol {tol[i]!r}")
+    return ok0 and worst <= REL_L2
 
 
 def prefill_and_compare(ss, om, prompt, mode=0, cmp_every=True):
@@ -71,11 +97,14 @@ def prefill_and_compare(ss, om, prompt, mode=0, cmp_every=True):
     return st, worst
 
 
-@pytest.mark.parametrize("gains", ["ones", "random"])
-def test_tiny_teacher_forced_logits(gains):
-    wl = workload.config(0)
-    ss = session(0, gains)
-    om = oracle_model(0, gains)
+@pytest.mark.parametrize("cfg,gains", [(0, "ones"), (0, "random"), (5, "random")])
+def test_tiny_teacher_forced_logits(cfg, gains):
+    """Config 0 (head dim 64, two query heads per kv head, untied) and config 5
+    (head dim 128, four query heads per kv head, untied): the head widths and
+    group sizes of the full-size shapes, at a size the oracle runs in seconds."""
+    wl = workload.config(cfg)
+    ss = session(cfg, gains)
+    om = oracle_model(cfg, gains)
     prompt = workload.make_prompt(wl)[0]
     st, worst = prefill_and_compare(ss, om, prompt)
     assert worst < 1e-4          # fp32 accumulation; far inside the bar
@@ -84,10 +113,10 @@ def test_tiny_teacher_forced_logits(gains):
     # straddle a rounding boundary, plus the fp32 absolute error where the
     # entry is a small result of cancellation (RoPE's rotation); rare.
     P = len(prompt)
-    for dev_cache, ref_cache in ((ss.k, st.kcache), (ss.v, st.vcache)):
+    for name, dev_cache, ref_cache in (("k", ss.k, st.kcache), ("v", ss.v, st.vcache)):
         kg = dev_cache[:, 0, :, :P].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         ko = ref_cache[:, 0, :, :P]
-        assert kv_close(kg, ko)
+        assert kv_close(kg, ko, what=f"cfg {cfg} {name} cache")
     ss.check()
     ss.close()
 
@@ -252,12 +281,31 @@ def test_watchdog_recovers_from_dropped_signal():
     ss.close()
 
 
+def dev_cache_u16(t, layers_b, n):
+    """Positions 0..n-1 of a device bf16 cache [L][B][Hkv][S][D] for sequence b
+    as uint16 bit patterns [L][Hkv][n][D] (no arithmetic)."""
+    return t[:, layers_b, :, :n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def shared_cache_state(om, ss, b, n, max_seq):
+    """An oracle state whose cache positions 0..n-1 are the device's own bf16
+    entries of sequence b."""
+    st = om.new_state(1, max_seq)
+    st.kcache[:, 0, :, :n] = dev_cache_u16(ss.k, b, n)
+    st.vcache[:, 0, :, :n] = dev_cache_u16(ss.v, b, n)
+    return st
+
+
 def full_size_sampled(cfg: int, prefix: int, what: str):
     """A full-size shape in the launch configuration the benchmark times
     (default graph, megakernel): the first `prefix` prompt tokens fed one step
     each, logits at the last of them checked against the oracle's no-cache
-    forward, then two decode steps checked against the oracle's incremental
-    decode, each with the greedy token."""
+    forward, then two decode steps checked against the oracle twice: with the
+    oracle's own cache (the bar), and with the oracle attending over the
+    device's own cache entries (copied after the step, the ones it wrote
+    included), where only fp32 against fp64 accumulation is left
+    (SHARED_REL_L2). The device cache is
+    also compared entry by entry with the oracle's."""
     wl = workload.config(cfg)
     ss = session(cfg)
     om = oracle_model(cfg, cache=False)
@@ -268,8 +316,10 @@ def full_size_sampled(cfg: int, prefix: int, what: str):
     full, ks, vs = om.forward_full(prompt)
     nxt, lg = ss.decode_step([int(prompt[-1])], [P - 1])
     check_logits(lg[0].double().cpu().numpy(), full[P - 1], f"{what} last prompt position")
+    assert kv_close(dev_cache_u16(ss.k, 0, P), ks, what=f"{what} k cache")
+    assert kv_close(dev_cache_u16(ss.v, 0, P), vs, what=f"{what} v cache")
     # oracle state = the forward's cache
-    st = om.new_state(1, wl.max_seq)
+    st = om.new_state(1, P + 2)
     st.kcache[:, 0, :, :P] = ks
     st.vcache[:, 0, :, :P] = vs
     tok = int(np.argmax(full[P - 1]))
@@ -277,7 +327,13 @@ def full_size_sampled(cfg: int, prefix: int, what: str):
     for k in range(2):
         ref = om.decode_step(st, [tok], [P + k])[0]
         nxt, lg = ss.decode_step([tok], [P + k])
-        check_logits(lg[0].double().cpu().numpy(), ref, f"{what} decode step {k}")
+        g = lg[0].double().cpu().numpy()
+        check_logits(g, ref, f"{what} decode step {k}")
+        # the device's cache, the entries this step wrote included
+        shared = shared_cache_state(om, ss, 0, P + k + 1, P + k + 1)
+        ref_s = om.decode_step(shared, [tok], [P + k], kv_given=True)[0]
+        _, rel = check_logits(g, ref_s, f"{what} decode step {k}, shared cache")
+        assert rel <= SHARED_REL_L2, (what, k, rel)
         tok = int(np.argmax(ref))
         assert int(nxt[0]) == tok
     ss.check()
@@ -295,6 +351,71 @@ def test_8b_full_size_sampled():
     """Llama-3-8B shape (hidden 4096, head dim 128, untied LM head, the
     smallest ring depth the LDS leaves room for): the first 8 prompt tokens."""
     full_size_sampled(2, 8, "8B")
+
+
+@pytest.mark.slow
+def test_1b_generate_one_launch_vs_oracle():
+    """The benchmark's configuration end to end: the Llama-3.2-1B shape, the
+    39-token prompt, then 16 greedy steps inside ONE persistent launch
+    (mk_generate). Token ids bit-exact against the oracle's greedy decoding
+    (the oracle's smallest top-2 margin over these steps is printed: a flip
+    needs an error that large), the launch's last-step logits within the bar,
+    and the cache it wrote close to the oracle's."""
+    from oracle.decoder import greedy
+    wl = workload.config(1)
+    n = 16
+    ss = session(1)
+    om = oracle_model(1, cache=False)
+    prompt = workload.make_prompt(wl)[0]
+    P = len(prompt)
+    for p in range(P - 1):
+        ss.decode_step([int(prompt[p])], [p], logits=False)
+    out = ss.generate([int(prompt[-1])], [P - 1], n, last_logits=True)
+    got = out[:, 0].cpu().tolist()
+    last = ss.logits[0].double().cpu().numpy()
+    # oracle: the prompt's cache from the no-cache forward, then n greedy steps
+    _, ks, vs = om.forward_full(prompt[:-1])
+    st = om.new_state(1, P + n)
+    st.kcache[:, 0, :, :P - 1] = ks
+    st.vcache[:, 0, :, :P - 1] = vs
+    progress("[1B generate] device launch done; oracle greedy running")
+    toks, margins, logits = greedy(om, st, [int(prompt[-1])], [P - 1], n, keep_logits=True)
+    print(f"[1B generate] gpu {got}\n[1B generate] ref {toks[:, 0].tolist()}\n"
+          f"[1B generate] smallest oracle top-2 margin {margins.min():.4f}", flush=True)
+    assert got == toks[:, 0].tolist()
+    check_logits(last, logits[-1][0], "1B one launch, last step")
+    n_pos = P - 1 + n
+    assert kv_close(dev_cache_u16(ss.k, 0, n_pos), st.kcache[:, 0, :, :n_pos], what="1B generate k cache")
+    assert kv_close(dev_cache_u16(ss.v, 0, n_pos), st.vcache[:, 0, :, :n_pos], what="1B generate v cache")
+    ss.check()
+    ss.close()
+
+
+@pytest.mark.slow
+def test_1b_generate_long_launch_equals_stepwise():
+    """The cross-step machinery of one long persistent launch at the benchmark's
+    shape (copy-ahead across steps, staging-slot flips, epoch thresholds): 64
+    greedy steps in one mk_generate equal 64 per-operator steps fed the same
+    tokens, token for token, with bit-identical last-step logits."""
+    from decode_persistent_megakernel_amd import MK_MODE_OPLAUNCH
+    wl = workload.config(1)
+    n = 64
+    ss = session(1)
+    prompt = workload.make_prompt(wl)[0]
+    P = len(prompt)
+    for p in range(P - 1):
+        ss.decode_step([int(prompt[p])], [p], logits=False)
+    out = ss.generate([int(prompt[-1])], [P - 1], n, last_logits=True)
+    lg_mk = ss.logits[0].clone()
+    toks = out[:, 0].cpu().tolist()
+    tok = int(prompt[-1])
+    for k in range(n):
+        nxt, lg = ss.decode_step([tok], [P - 1 + k], mode=MK_MODE_OPLAUNCH, logits=(k == n - 1))
+        assert int(nxt[0]) == toks[k], k
+        tok = toks[k]
+    assert torch.equal(lg[0], lg_mk)
+    ss.check()
+    ss.close()
 
 
 @pytest.mark.slow
@@ -367,36 +488,45 @@ def test_tiny_batch16_in_groups():
 @pytest.mark.slow
 def test_8b_batch16_sampled():
     """The batch workload at full size: Llama-3-8B shape, 16 sequences with
-    prefilled caches of seeded lengths in 512..8192, run in groups of the
-    launch's capacity. Two decode steps for all 16; the shortest and the
-    longest sequence checked against the oracle over the same cache (logits
-    and greedy token); mk_generate over the groups equal to the two steps."""
+    prefilled caches of seeded lengths in 512..8192. Two decode steps for all
+    16 sequences, every sequence checked against one batched oracle step:
+    step 0 over the same prefilled cache (the bar), step 1 with the oracle
+    attending over the device's own cache entries, the ones the step wrote
+    included (SHARED_REL_L2), greedy tokens at both; mk_generate over the same two steps equal to them."""
     import torch
     wl = workload.config(4)
     lens = [int(x) for x in workload.kv_lengths(wl)]
     kc, vc = workload.make_prefill(wl)
+    progress("[batch16] prefilled caches generated")
     ss = session(4, kv=(kc, vc))
-    print(f"[batch16] lens {lens} sequences per launch {ss.batch_per_launch} ring {ss.ring_slots}", flush=True)
+    progress(f"[batch16] lens {lens} sequences per launch {ss.batch_per_launch} ring {ss.ring_slots}")
     om = oracle_model(4, cache=False)
-    picks = [int(np.argmin(lens)), int(np.argmax(lens))]
-    states = {}
-    for b in picks:
-        st = om.new_state(1, wl.max_seq)
-        st.kcache[:, 0] = kc[:, b].contiguous().view(torch.int16).numpy().view(np.uint16)
-        st.vcache[:, 0] = vc[:, b].contiguous().view(torch.int16).numpy().view(np.uint16)
-        states[b] = st
+    B = wl.batch
+    S1 = max(lens) + 2
+    st = om.new_state(B, S1)
+    st.kcache[:] = kc[:, :, :, :S1].contiguous().view(torch.int16).numpy().view(np.uint16)
+    st.vcache[:] = vc[:, :, :, :S1].contiguous().view(torch.int16).numpy().view(np.uint16)
     del kc, vc
     tok0 = [int(t) for t in workload.make_prompt(wl)[:, 0]]
     tk = list(tok0)
     steps = []
     for k in range(2):
-        nxt, lg = ss.decode_step(tk, [n + k for n in lens])
+        pos = [n + k for n in lens]
+        nxt, lg = ss.decode_step(tk, pos)
         g = lg.double().cpu().numpy()
         nxt = [int(x) for x in nxt.cpu().tolist()]
-        for b in picks:
-            ref = om.decode_step(states[b], [tk[b]], [lens[b] + k])[0]
-            check_logits(g[b], ref, f"batch16 seq {b} (len {lens[b]}) step {k}")
-            assert nxt[b] == int(np.argmax(ref))
+        if k == 1:  # the device's own entries at every position the step reads (this step's included)
+            for b in range(B):
+                n = lens[b] + 2
+                st.kcache[:, b, :, :n] = dev_cache_u16(ss.k, b, n)
+                st.vcache[:, b, :, :n] = dev_cache_u16(ss.v, b, n)
+        progress(f"[batch16] device step {k} done; oracle step {k} (16 sequences) running")
+        ref = om.decode_step(st, tk, pos, kv_given=(k == 1))
+        for b in range(B):
+            _, rel = check_logits(g[b], ref[b], f"batch16 seq {b} (len {lens[b]}) step {k}")
+            if k == 1:
+                assert rel <= SHARED_REL_L2, (b, rel)
+            assert nxt[b] == int(np.argmax(ref[b])), b
         steps.append(nxt)
         tk = nxt
     ss.check()

@@ -145,3 +145,28 @@ def test_greedy_protocol_and_kv_written():
     assert toks.shape == (4, 1) and np.all(margins > 0)
     assert np.all(st.kcache[:, 0, :, : P - 1 + 4].any(axis=-1))   # every position written
     assert not st.kcache[:, 0, :, P - 1 + 4:].any()
+
+
+def test_kv_given_reads_the_entries_it_is_given():
+    """kv_given=True attends over the cache entries the state already holds at
+    the fed position: with the entries the normal step writes there, the
+    logits are identical; with other entries, they differ (so the option does
+    not silently rewrite them)."""
+    wl = workload.config(0)
+    m = oracle_model(0, "random")
+    prompt = workload.make_prompt(wl)[0]
+    st = m.new_state(1, wl.max_seq)
+    for p in range(4):
+        m.decode_step(st, [int(prompt[p])], [p])
+    import copy
+    st2 = copy.deepcopy(st)
+    ref = m.decode_step(st, [int(prompt[4])], [4])          # writes position 4
+    st2.kcache[:, :, :, 4] = st.kcache[:, :, :, 4]
+    st2.vcache[:, :, :, 4] = st.vcache[:, :, :, 4]
+    got = m.decode_step(st2, [int(prompt[4])], [4], kv_given=True)
+    assert np.array_equal(got, ref)
+    st3 = copy.deepcopy(st)
+    st3.vcache[:, :, :, 4] = bf16.encode(bf16.decode(st3.vcache[:, :, :, 4]) * 2.0)
+    other = m.decode_step(st3, [int(prompt[4])], [4], kv_given=True)
+    assert not np.allclose(other, ref)
+    assert np.array_equal(st3.kcache, st.kcache)            # nothing written

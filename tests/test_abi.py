@@ -37,7 +37,7 @@ def c_bytes(desc, opts=None):
         mk.mk_free_graph(g)
 
 
-@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("cfg", range(len(workload.CONFIGS)))
 def test_graph_bytes_equal_oracle_default(cfg):
     wl = workload.config(cfg)
     b = c_bytes(mk.desc_from_shape(wl.shape, wl.batch, wl.max_seq))

@@ -71,6 +71,7 @@ class Workload:
 _TINY = ModelShape(2, 256, 4, 2, 64, 688, 1024, False, 1e4)
 _1B = ModelShape(16, 2048, 32, 8, 64, 8192, 128256, True, 5e5)
 _8B = ModelShape(32, 4096, 32, 8, 128, 14336, 128256, False, 5e5)
+_TINY_D128 = ModelShape(2, 512, 8, 2, 128, 1024, 2048, False, 1e4)
 
 CONFIGS: List[Workload] = [
     Workload(0, "tiny-2L-h256", _TINY, 1, 64, 8, 16, "none"),
@@ -79,6 +80,9 @@ CONFIGS: List[Workload] = [
     Workload(3, "1b-shape-kv32768", _1B, 1, 32768 + 128, 0, 128, "fixed", kv_len=32768),
     Workload(4, "8b-shape-batch16", _8B, 16, 8192 + 128, 0, 128, "uniform",
              kv_lo=512, kv_hi=8192),
+    # test-only: the tiny config's size with the 8B shape's head width (128),
+    # four query heads per kv head and an untied LM head
+    Workload(5, "tiny-2L-h512-d128", _TINY_D128, 1, 64, 8, 16, "none"),
 ]
 
 
