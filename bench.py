@@ -149,7 +149,7 @@ def main():
     ss = Session(wl.shape, w, wl.batch, wl.max_seq, kv=kv)
     kv = None
     log(f"model loaded: {ss.n_tasks} tasks, {ss.num_cus} CUs, packed weights {ss.packed_bytes / 1e9:.3f} GB, "
-        f"ring {ss.ring_slots} slots, LDS {ss.lds_bytes} B, {ss.batch_per_launch} sequence(s) per launch")
+        f"register ring {ss.ring_slots} items per stream wave, LDS {ss.lds_bytes} B, {ss.batch_per_launch} sequence(s) per launch")
     B = wl.batch
     K, W = args.steps, args.warmup
     if wl.kv_prefill == "none":
@@ -230,7 +230,7 @@ def main():
         cpu = cpu_baseline(wl, w, args.cpu_seconds)
         log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads")
 
-    kernel = f"mk_persistent_b{min(B, ss.batch_per_launch)}_d{ss.ring_slots}"
+    kernel = f"mk_persistent_b{min(B, ss.batch_per_launch)}"
     per = "token at batch 1" if B == 1 else f"step at batch {B}"
     rec = {
         "metric": f"decode \u00b5s/{per} + achieved HBM GB/s as % of roofline",

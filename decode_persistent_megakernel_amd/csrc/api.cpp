@@ -226,16 +226,16 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     return fail(MK_EUNSUPPORTED, "mk_load_weights: attn_chunks * (max_seq + 1) must stay below 2^32");
   if (d.hidden % 4 || (d.n_q_heads * d.head_dim) % 4 || d.ffn % 4)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden, q width and ffn must be multiples of 4");
-  // LDS: control words, the stream waves' rings, two small staging slots, the
-  // merge slot (attention merges), three partial-sum areas, then the stream
-  // records. A down-projection input overlays the two small slots and the
-  // merge slot (the kernel stages it only once every earlier task has retired).
-  // Staged copies move whole 1 KiB pieces, so every region is rounded up to
-  // 256 floats where a copy lands.
+  // LDS: control words, two small staging slots, the merge slot (attention
+  // merges), three partial-sum areas, then the stream records. A
+  // down-projection input overlays the two small slots and the merge slot (the
+  // kernel stages it only once every earlier task has retired). Staged copies
+  // move whole 1 KiB pieces, so every region is rounded up to 256 floats where
+  // a copy lands. (The stream waves' weight rings live in registers.)
   auto r256 = [](int64_t n) { return (n + 255) / 256 * 256; };
-  // The sequences one launch stages (ncap): as many as leave LDS room for
-  // rings of at least kMinDepth items beside the staging slots; a call with
-  // more sequences runs them in groups of ncap (sequences are independent).
+  // The sequences one launch stages (ncap): as many as fit the LDS; a call
+  // with more sequences runs them in groups of ncap (sequences are
+  // independent).
   int ncap = std::min<int>(d.max_batch, kMaxCols);
   const int kp = static_cast<int>(r256(std::max(d.hidden, d.n_q_heads * D)));
   const int kp_big = static_cast<int>(r256(d.ffn));
@@ -243,15 +243,16 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   for (const Task& t : g.tasks) nlm_tasks += t.type == T_LM;
   const int64_t Ncx = g.opts.attn_chunks;
   const int res_stride = (max_res + 3) & ~3;
-  const int64_t item_bytes = 2 * kUnitBytes;
   const size_t lds_max = 160 * 1024;
-  int64_t small_floats = 0, big_floats = 0, part_floats = 0, ring = 0;
+  int64_t small_floats = 0, big_floats = 0, part_floats = 0;
   size_t fixed = 0;
   for (; ncap >= 1; --ncap) {
     const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * res_stride;
-    // attention: raw q|k|v, rotated q, new k and v, their bf16 bits, then the
-    // stream waves' partials (acc[wave][head][D], then (m, l) per wave and head)
-    const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D + int64_t(kStreams) * G * (D + 2);
+    // attention: raw q|k|v, rotated q, new k and v, their bf16 bits, k and v of
+    // position p - 1, the scaled rotated q, then the stream waves' partials (acc[wave][head][D],
+    // then (m, l) per wave and head)
+    const int64_t need_att = r256(int64_t(G + 2) * D) + int64_t(G) * D + 2 * D + D + 2 * D + int64_t(G) * D +
+                             int64_t(kStreams) * G * (D + 2);
     const int64_t need_arg = r256(nlm_tasks) * 2;
     const int64_t need_emb = r256(d.hidden / 2 + 1);
     const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
@@ -263,21 +264,17 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     part_floats = (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
     fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
             size_t(srec_max) * sizeof(StreamRec);
-    // The rest holds the stream waves' rings of 2 KiB items; each slot is one
-    // item in flight.
-    ring = fixed < lds_max ? std::min<int64_t>(kMaxDepth, (int64_t(lds_max) - int64_t(fixed)) / (kStreams * item_bytes)) : 0;
-    ring = ring >= 11 ? 11 : ring >= 8 ? 8 : ring >= 6 ? 6 : ring >= 4 ? 4 : 0;  // the depths the kernel is built for
-    if (ring >= kMinDepth) break;
+    if (fixed <= lds_max) break;
   }
   if (ncap < 1)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: staging one sequence needs " + std::to_string(fixed) +
-                                     " bytes of LDS, leaving no room for the weight rings");
+                                     " bytes of LDS, more than the 160 KiB a workgroup has");
   m->ncap = ncap;
-  const size_t lds = fixed + size_t(kStreams) * size_t(ring) * size_t(item_bytes);
+  const size_t lds = fixed;
   m->lds_bytes = static_cast<int>(lds);
   HIP_TRY(set_lds_limit(m->lds_bytes), "hipFuncSetAttribute(max dynamic LDS)");
   int per_cu = 0;
-  HIP_TRY(persistent_occupancy(m->lds_bytes, static_cast<int>(ring), &per_cu), "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  HIP_TRY(persistent_occupancy(m->lds_bytes, &per_cu), "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   if (int64_t(per_cu) * prop.multiProcessorCount < g.opts.num_cus)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: num_cus=" + std::to_string(g.opts.num_cus) +
                                      " workgroups cannot be co-resident (" + std::to_string(prop.multiProcessorCount) +
@@ -320,12 +317,14 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   HIP_TRY(hipMemcpy(d_thr, thr.data(), thr.size() * 4, hipMemcpyHostToDevice), "copy thresholds");
   HIP_TRY(hipMemset(d_cnt, 0, thr.size() * 4 * kEventWords), "clear counters");
 
-  uint8_t* d_wpack;
+  uint8_t *d_wpack, *d_zeros;
   uint16_t *d_embed, *d_gains;
   float2* d_rope;
   if ((rc = m->alloc(&d_wpack, m->packed_bytes, "packed weights")) || (rc = m->alloc(&d_embed, V * H + 512, "embedding")) ||
-      (rc = m->alloc(&d_gains, (2 * L + 1) * H, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")))
+      (rc = m->alloc(&d_gains, (2 * L + 1) * H, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")) ||
+      (rc = m->alloc(&d_zeros, size_t(kZeroBlocks) * 2 * kUnitBytes, "zero blocks")))
     return rc;
+  HIP_TRY(hipMemset(d_zeros, 0, size_t(kZeroBlocks) * 2 * kUnitBytes), "clear zero blocks");
   HIP_TRY(hipMemcpyAsync(d_embed, w->embed, V * H * 2, hipMemcpyDeviceToDevice, s), "copy embedding");
   for (int l = 0; l < L; ++l) {
     HIP_TRY(hipMemcpyAsync(d_gains + (2 * l) * H, w->layers[l].g_attn, H * 2, hipMemcpyDeviceToDevice, s), "copy gain");
@@ -399,7 +398,6 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   P.eps = d.rms_eps;
   P.small_floats = static_cast<int32_t>(small_floats);
   P.big_floats = static_cast<int32_t>(big_floats);
-  P.ring_slots = static_cast<int32_t>(ring);
   P.kp_big = kp_big;
   P.part_floats = static_cast<int32_t>(part_floats);
   P.attn_scale = static_cast<float>(1.0 / std::sqrt(double(d.head_dim)));
@@ -408,6 +406,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   P.res_stride = res_stride;
   P.ncap = ncap;
   P.wpack = d_wpack;
+  P.zeros = d_zeros;
   P.embed = d_embed;
   P.gains = d_gains;
   P.kcache = static_cast<uint16_t*>(w->k_cache);
@@ -588,7 +587,7 @@ int mk_model_info(const mk_model* m, uint64_t* packed_weight_bytes, int32_t* num
   if (packed_weight_bytes) *packed_weight_bytes = m->packed_bytes;
   if (num_cus) *num_cus = m->g.opts.num_cus;
   if (n_tasks) *n_tasks = static_cast<int32_t>(m->g.tasks.size());
-  if (ring_slots) *ring_slots = m->base.ring_slots;
+  if (ring_slots) *ring_slots = mk::kRing;
   if (lds_bytes) *lds_bytes = m->lds_bytes;
   return MK_OK;
 }

@@ -20,19 +20,22 @@ constexpr int kUnitRows = 4;
 
 // Workgroup layout: wave 0 stages task inputs (and polls events), wave 1
 // retires tasks (epilogue, stores, signals); then kStreams stream waves, each
-// copying its piece of every streamed task into its own LDS ring and
+// loading its piece of every streamed task into a ring of registers and
 // computing on it.
 constexpr int kCtlWaves = 2;
 constexpr int kStreams = 4;
 constexpr int kThreads = 64 * (kCtlWaves + kStreams);
-constexpr int kMaxDepth = 11;  // ring slots (2 KiB items) per stream wave: 4, 6, 8 or 11
-constexpr int kMinDepth = 4;   // fewer cannot hide the copy latency
+#ifndef MK_RING
+#define MK_RING 8
+#endif
+constexpr int kRing = MK_RING;  // 2 KiB items each stream wave keeps in flight (in registers)
+constexpr int kZeroBlocks = 256;  // 2 KiB zero blocks, one per compute unit (index taken modulo)
 constexpr int kMaxCols = 4;    // sequences a matvec task handles
 constexpr int kMaxBatch = 256; // sequences a model holds (larger calls run in groups of at most kMaxCols)
 constexpr int kMaxG = 4;       // query heads per kv head
 constexpr int kStripes = 64;   // event counter stripes: one per lane of the polling wave
 constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte line
-constexpr int kCtlBytes = 1024;             // control words + ring metadata (see kernels)
+constexpr int kCtlBytes = 1024;             // control words (see kernels)
 constexpr int kWaves = kThreads / 64;
 constexpr int kWaitWords = 16;              // per-wave wait counters (mk_set_wait_counters)
 constexpr int kProfWords = 12;              // uint64 words per task in the profile buffer
@@ -90,9 +93,9 @@ struct Params {
   int32_t small_floats; // LDS staging slot size (two small slots)
   int32_t big_floats;   // LDS staging slot size for down-projection and merge tasks
   int32_t part_floats;  // LDS partial-sum area per slot
-  int32_t ring_slots;   // ring slots per stream wave = items it keeps in flight
   // model data
   const uint8_t* wpack;
+  const uint8_t* zeros;       // [kZeroBlocks][2 KiB] of zeros: the loads that fill a stream block up
   const uint16_t* embed;      // [V][H] bf16 (library copy)
   const uint16_t* gains;      // [L][2][H] then [H] final, bf16
   uint16_t* kcache;           // [L][B][Hkv][S][D] bf16 (caller-owned)

@@ -12,12 +12,12 @@
 //  * wave 1, the retirer: once a task's compute is done it runs the epilogue
 //    (partial-sum reduction, residual add, SiLU*up, attention merge, argmax),
 //    stores the results and adds one to the task's triggering event;
-//  * kStreams stream waves: each copies its share of every task's weight (or
-//    KV cache) units straight into its own LDS ring and computes on them,
-//    copying ahead across task boundaries so weights keep arriving while the
-//    workgroup waits on an event (Hazy megakernel summary: paged shared memory
-//    lets the next instruction's weights load early; MPK blog translation:
-//    loads of the next layer overlap the current one).
+//  * kStreams stream waves: each loads its share of every task's weight (or
+//    KV cache) units into a ring of registers and computes on them, loading
+//    ahead across task boundaries so weights keep arriving while the
+//    workgroup waits on an event (Hazy megakernel summary: the next
+//    instruction's weights load early; MPK blog translation: loads of the
+//    next layer overlap the current one).
 //
 // Cross-compute-unit data moves with device-coherent (sc1) loads and stores;
 // a producer waits for its stores to complete before it counts the event, and
@@ -257,7 +257,6 @@ struct Ctx {
   float* slots;    // small0 | small1 | big
   float* parts;    // three partial-sum areas
   int small_floats, part_floats;
-  uint8_t* ring;   // [kStreams][ring_slots][2 KiB]
   StreamRec* recs; // this queue's stream records (LDS)
   int nrec;
   int cu;          // stripe / profile id
@@ -268,8 +267,8 @@ struct Ctx {
 
 // Graph tables and call inputs are read-only while a kernel runs. Reading them
 // through the constant address space with a wave-uniform index makes them
-// scalar loads (lgkmcnt): a vector load would share vmcnt with the loader's
-// in-flight weight copies, and waiting for it would drain those copies.
+// scalar loads (lgkmcnt): a vector load would share vmcnt with a stream
+// wave's in-flight weight loads, and waiting for it would drain them.
 typedef __attribute__((address_space(4))) const int32_t cint32;
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const i32x4 ci32x4;
@@ -525,12 +524,17 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
 
 // Attention slot layout after the header: raw q|k|v of the kv group (rounded
 // up to 256 floats), rotated queries [G][D], new key [D] and value [D] as
-// bf16-rounded floats, then their bf16 bits [2D].
+// bf16-rounded floats, their bf16 bits [2D], the key [D] and value [D] of
+// position p - 1 read back from the cache, then the rotated queries again,
+// scaled by log2(e)/sqrt(D) for the stream waves' base-2 scores [G][D].
 __device__ __forceinline__ int att_raw_floats(const Params& P) { return ((P.G + 2) * P.D + 255) & ~255; }
+__device__ __forceinline__ float* att_qs_ptr(const Params& P, const Ctx& cx, int slot) {
+  return slot_ptr(cx, slot) + kHdr + att_raw_floats(P) + P.G * P.D + 2 * P.D + P.D + 2 * P.D;
+}
 // The stream waves' attention partials follow, in the same slot: acc[wave][head][D],
 // then (m, l) of [wave][head].
 __device__ __forceinline__ float* att_part_ptr(const Params& P, const Ctx& cx, int slot) {
-  return slot_ptr(cx, slot) + kHdr + att_raw_floats(P) + P.G * P.D + 2 * P.D + P.D;
+  return att_qs_ptr(P, cx, slot) + P.G * P.D;
 }
 
 // Before the event wait: the RoPE (cos, sin) pair jj = lane of the position
@@ -553,6 +557,8 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
   float* kf = q + G * D;
   float* vf = kf + D;
   uint16_t* kvb = reinterpret_cast<uint16_t*>(vf + D);
+  float* qs = att_qs_ptr(P, cx, slot);
+  const float qscale = P.attn_scale * 1.4426950408889634f;  // scores in base-2 units
   const int lane = cx.lane;
   const bool active = T.b < P.batch;
   int p = active ? ld_uniform(P.pos_in, T.b) + step : 0;
@@ -562,13 +568,31 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
   const int64_t len = (int64_t)p + 1;
   const int lo = chunk_bound(T.chunk, len, P.Nc), hi = chunk_bound(T.chunk + 1, len, P.Nc);
   const bool owner = valid && T.chunk == P.Nc - 1;
+  // position p - 1 (appended by the previous step) is not streamed: this
+  // task's dependency implies its append is complete, and the chunk that holds
+  // it reads it here
+  const bool prev = valid && p >= 1 && lo <= p - 1 && p - 1 < hi;
   if (lane == 0) {
     ih[H_P] = p;
     ih[H_LO] = lo;
-    ih[H_END] = valid ? min(hi, p) : lo;
-    ih[H_FLAGS] = (valid ? 1 : 0) | (owner ? 2 : 0) | (active ? 4 : 0);
+    ih[H_END] = valid ? max(lo, min(hi, p - 1)) : lo;
+    ih[H_FLAGS] = (valid ? 1 : 0) | (owner ? 2 : 0) | (active ? 4 : 0) | (prev ? 8 : 0);
   }
   if (!valid) return;
+  if (prev) {
+    float* kf1 = vf + D + D;  // after the bf16 bits of the new key and value
+    float* vf1 = kf1 + D;
+    const size_t row = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.S + (p - 1)) * D;
+    const uint32_t* kc = reinterpret_cast<const uint32_t*>(P.kcache + row);
+    const uint32_t* vc = reinterpret_cast<const uint32_t*>(P.vcache + row);
+    for (int w = lane; w < D / 2; w += 64) {
+      const uint32_t kw = ld_coh(kc + w), vw = ld_coh(vc + w);
+      kf1[2 * w] = bf2f(kw & 0xffffu);
+      kf1[2 * w + 1] = bf2f(kw >> 16);
+      vf1[2 * w] = bf2f(vw & 0xffffu);
+      vf1[2 * w + 1] = bf2f(vw >> 16);
+    }
+  }
   stage_copy(cx, P.qkv + ((size_t)T.b * P.Hkv + T.g) * GR, raw, GR);
   // whole-wave iterations: the (cos, sin) pair comes from lane jj of pre
   for (int base = 0; base < (G + 1) * Dh; base += 64) {
@@ -581,6 +605,8 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
     if (h < G) {
       q[h * D + jj] = r0;
       q[h * D + jj + Dh] = r1;
+      qs[h * D + jj] = r0 * qscale;
+      qs[h * D + jj + Dh] = r1 * qscale;
     } else {
       const uint32_t b0 = f2bf(r0), b1 = f2bf(r1);
       kf[jj] = bf2f(b0);
@@ -768,36 +794,48 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
   const int* ih = reinterpret_cast<const int*>(hdr);
   const int flags = ih[H_FLAGS];
   if (!(flags & 4)) return;  // sequence not in this call's batch
-  const bool owner = flags & 2;
+  const bool owner = flags & 2, prev = flags & 8;
   const int G = P.G, D = P.D, D4 = D / 4;
   const float* q = hdr + kHdr + att_raw_floats(P);
   const float* kf = q + G * D;
   const float* vf = kf + D;
   const uint32_t* kvw = reinterpret_cast<const uint32_t*>(vf + D);
+  const float* kf1 = vf + 2 * D;  // position p - 1
+  const float* vf1 = kf1 + D;
   const float* part = att_part_ptr(P, cx, slot);
   const float* pml = part + kStreams * G * D;  // (m, l) of [wave][head]
   const int lane = cx.lane, p = ih[H_P];
-  // score of the new position (its key and value are the staged ones)
-  float sp[kMaxG];
+  // scores of the new position and of p - 1 (their keys and values are the
+  // staged ones)
+  float sp[kMaxG], sq[kMaxG];
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     sp[h] = -INFINITY;
+    sq[h] = -INFINITY;
     if (h < G && owner) {
       float a = 0.f;
       for (int d = lane; d < D; d += 64) a = fmaf(q[h * D + d], kf[d], a);
       sp[h] = wave_sum(a) * P.attn_scale;
     }
+    if (h < G && prev) {
+      float a = 0.f;
+      for (int d = lane; d < D; d += 64) a = fmaf(q[h * D + d], kf1[d], a);
+      sq[h] = wave_sum(a) * P.attn_scale;
+    }
   }
-  // merge of the stream waves' partials and the new position: each lane owns
-  // four dims of one head
+  // merge of the stream waves' partials and the staged positions: each lane
+  // owns four dims of one head
   const size_t chunk0 = ((size_t)T.b * P.Hq + (size_t)T.g * G) * P.Nc + T.chunk;  // head 0 of the group
   const rsrc_t racc = make_rsrc(P.part_acc, 0xffffffffu);
   for (int qd = lane; qd < G * D4; qd += 64) {
     const int h = qd / D4, d = (qd - h * D4) * 4;
-    float s_new = sp[0];
+    float s_new = sp[0], s_prev = sq[0];
 #pragma unroll
     for (int hh = 1; hh < kMaxG; ++hh)
-      if (h == hh) s_new = sp[hh];
+      if (h == hh) {
+        s_new = sp[hh];
+        s_prev = sq[hh];
+      }
     float mw[kStreams], lw[kStreams];
     float4 aw[kStreams];
 #pragma unroll
@@ -806,7 +844,7 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
       lw[w] = pml[(w * G + h) * 2 + 1];
       aw[w] = *reinterpret_cast<const float4*>(part + (size_t)(w * G + h) * D + d);
     }
-    float M = s_new;
+    float M = fmaxf(s_new, s_prev);
 #pragma unroll
     for (int w = 0; w < kStreams; ++w) M = fmaxf(M, mw[w]);
     float l = 0.f;
@@ -817,6 +855,12 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
       l = fmaf(lw[w], e, l);
       a.x = fmaf(aw[w].x, e, a.x); a.y = fmaf(aw[w].y, e, a.y);
       a.z = fmaf(aw[w].z, e, a.z); a.w = fmaf(aw[w].w, e, a.w);
+    }
+    if (prev) {
+      const float e = expf(s_prev - M);
+      l += e;
+      a.x = fmaf(e, vf1[d], a.x); a.y = fmaf(e, vf1[d + 1], a.y);
+      a.z = fmaf(e, vf1[d + 2], a.z); a.w = fmaf(e, vf1[d + 3], a.w);
     }
     if (owner) {
       const float e = expf(s_new - M);
@@ -1002,13 +1046,12 @@ __device__ __forceinline__ void run_retirer(const Params& P0, const Ctx& cx) {
 // kernels
 // ---------------------------------------------------------------------------
 
-template <int NC, int DEPTH, bool PROF>
+template <int NC, bool PROF>
 __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   extern __shared__ __align__(16) char smem[];
   Ctx cx;
   cx.ctl = reinterpret_cast<int*>(smem);
-  cx.ring = reinterpret_cast<uint8_t*>(smem + kCtlBytes);
-  float* base = reinterpret_cast<float*>(cx.ring + (size_t)kStreams * P.ring_slots * 2 * kUnitBytes);
+  float* base = reinterpret_cast<float*>(smem + kCtlBytes);
   cx.slots = base;
   cx.small_floats = P.small_floats;
   cx.parts = base + 2 * P.small_floats + P.big_floats;
@@ -1053,63 +1096,39 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) run_stager<NC, PROF>(P, cx);
   else if (wave == 1) run_retirer<NC, PROF>(P, cx);
-  else run_stream<DEPTH, NC, PROF>(P, cx, wave - kCtlWaves);
+  else run_stream<kRing, NC, PROF>(P, cx, wave - kCtlWaves);
 }
 
-// One kernel per (staged columns, ring depth): each holds the code of its own
-// variant only, which keeps the instruction working set of a workgroup small
-// (it shares a 64 KiB instruction cache with a neighbouring compute unit). The
-// per-task timestamps and wait counters live in separate persistent variants
+// One kernel per staged column count: each holds the code of its own variant
+// only, which keeps the instruction working set of a workgroup small (it shares
+// a 64 KiB instruction cache with a neighbouring compute unit). The per-task
+// timestamps and wait counters live in separate persistent variants
 // (mk_persistent_prof_*), launched only when a profile or wait-counter buffer
 // is set.
-#define MK_KERNELS(NC, DEPTH)                                                                           \
-  extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent_b##NC##_d##DEPTH(Params P) {     \
-    run<NC, DEPTH, false>(P, blockIdx.x, -1);                                                          \
+#define MK_KERNELS(NC)                                                                                   \
+  extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent_b##NC(Params P) {               \
+    run<NC, false>(P, blockIdx.x, -1);                                                                 \
   }                                                                                                    \
-  extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent_prof_b##NC##_d##DEPTH(Params P) { \
-    run<NC, DEPTH, true>(P, blockIdx.x, -1);                                                           \
+  extern "C" __global__ void __launch_bounds__(kThreads) mk_persistent_prof_b##NC(Params P) {          \
+    run<NC, true>(P, blockIdx.x, -1);                                                                  \
   }                                                                                                    \
-  extern "C" __global__ void __launch_bounds__(kThreads) mk_oplaunch_b##NC##_d##DEPTH(Params P, int first) { \
-    run<NC, DEPTH, false>(P, blockIdx.x, first + blockIdx.x);                                          \
+  extern "C" __global__ void __launch_bounds__(kThreads) mk_oplaunch_b##NC(Params P, int first) {      \
+    run<NC, false>(P, blockIdx.x, first + blockIdx.x);                                                 \
   }
-MK_KERNELS(1, 11)
-MK_KERNELS(2, 11)
-MK_KERNELS(3, 11)
-MK_KERNELS(4, 11)
-MK_KERNELS(1, 8)
-MK_KERNELS(2, 8)
-MK_KERNELS(3, 8)
-MK_KERNELS(4, 8)
-MK_KERNELS(1, 6)
-MK_KERNELS(2, 6)
-MK_KERNELS(3, 6)
-MK_KERNELS(4, 6)
-MK_KERNELS(1, 4)
-MK_KERNELS(2, 4)
-MK_KERNELS(3, 4)
-MK_KERNELS(4, 4)
+MK_KERNELS(1)
+MK_KERNELS(2)
+MK_KERNELS(3)
+MK_KERNELS(4)
 #undef MK_KERNELS
 
 typedef void (*PersistentFn)(Params);
 typedef void (*OpFn)(Params, int);
-// [ring depth 11, 8, 6, 4][columns - 1]
-constexpr int kDepths = 4;
-__device__ __host__ constexpr int depth_index(int depth) { return depth >= 11 ? 0 : depth >= 8 ? 1 : depth >= 6 ? 2 : 3; }
-static const PersistentFn kPersistent[kDepths][kMaxCols] = {
-    {mk_persistent_b1_d11, mk_persistent_b2_d11, mk_persistent_b3_d11, mk_persistent_b4_d11},
-    {mk_persistent_b1_d8, mk_persistent_b2_d8, mk_persistent_b3_d8, mk_persistent_b4_d8},
-    {mk_persistent_b1_d6, mk_persistent_b2_d6, mk_persistent_b3_d6, mk_persistent_b4_d6},
-    {mk_persistent_b1_d4, mk_persistent_b2_d4, mk_persistent_b3_d4, mk_persistent_b4_d4}};
-static const PersistentFn kPersistentProf[kDepths][kMaxCols] = {
-    {mk_persistent_prof_b1_d11, mk_persistent_prof_b2_d11, mk_persistent_prof_b3_d11, mk_persistent_prof_b4_d11},
-    {mk_persistent_prof_b1_d8, mk_persistent_prof_b2_d8, mk_persistent_prof_b3_d8, mk_persistent_prof_b4_d8},
-    {mk_persistent_prof_b1_d6, mk_persistent_prof_b2_d6, mk_persistent_prof_b3_d6, mk_persistent_prof_b4_d6},
-    {mk_persistent_prof_b1_d4, mk_persistent_prof_b2_d4, mk_persistent_prof_b3_d4, mk_persistent_prof_b4_d4}};
-static const OpFn kOplaunch[kDepths][kMaxCols] = {
-    {mk_oplaunch_b1_d11, mk_oplaunch_b2_d11, mk_oplaunch_b3_d11, mk_oplaunch_b4_d11},
-    {mk_oplaunch_b1_d8, mk_oplaunch_b2_d8, mk_oplaunch_b3_d8, mk_oplaunch_b4_d8},
-    {mk_oplaunch_b1_d6, mk_oplaunch_b2_d6, mk_oplaunch_b3_d6, mk_oplaunch_b4_d6},
-    {mk_oplaunch_b1_d4, mk_oplaunch_b2_d4, mk_oplaunch_b3_d4, mk_oplaunch_b4_d4}};
+// [columns - 1]
+static const PersistentFn kPersistent[kMaxCols] = {mk_persistent_b1, mk_persistent_b2, mk_persistent_b3,
+                                                   mk_persistent_b4};
+static const PersistentFn kPersistentProf[kMaxCols] = {mk_persistent_prof_b1, mk_persistent_prof_b2,
+                                                       mk_persistent_prof_b3, mk_persistent_prof_b4};
+static const OpFn kOplaunch[kMaxCols] = {mk_oplaunch_b1, mk_oplaunch_b2, mk_oplaunch_b3, mk_oplaunch_b4};
 
 // ---------------------------------------------------------------------------
 // weight packing
@@ -1167,25 +1186,24 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack(const PackJob* jobs, c
 // ---------------------------------------------------------------------------
 
 hipError_t set_lds_limit(int bytes) {
-  for (int d = 0; d < kDepths; ++d)
-    for (int c = 0; c < kMaxCols; ++c) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistent[d][c]),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistentProf[d][c]),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kOplaunch[d][c]),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-      if (e != hipSuccess) return e;
-    }
+  for (int c = 0; c < kMaxCols; ++c) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistent[c]),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistentProf[c]),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kOplaunch[c]), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              bytes);
+    if (e != hipSuccess) return e;
+  }
   return hipSuccess;
 }
 
-hipError_t persistent_occupancy(int lds, int depth, int* blocks_per_cu) {
+hipError_t persistent_occupancy(int lds, int* blocks_per_cu) {
   int worst = 1 << 30;
   for (int c = 0; c < kMaxCols; ++c)
-    for (const PersistentFn f : {kPersistent[depth_index(depth)][c], kPersistentProf[depth_index(depth)][c]}) {
+    for (const PersistentFn f : {kPersistent[c], kPersistentProf[c]}) {
       int n = 0;
       hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(f), kThreads, lds);
       if (e != hipSuccess) return e;
@@ -1195,19 +1213,18 @@ hipError_t persistent_occupancy(int lds, int depth, int* blocks_per_cu) {
   return hipSuccess;
 }
 
-// The variant for the call: staged columns = the call's batch, the model's ring depth.
+// The variant for the call: staged columns = the call's batch.
 hipError_t launch_persistent(const Params& P, int grid, int lds, hipStream_t s) {
   if (P.batch < 1 || P.batch > kMaxCols) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p};
-  const PersistentFn f = (P.profile || P.waits) ? kPersistentProf[depth_index(P.ring_slots)][P.batch - 1]
-                                                 : kPersistent[depth_index(P.ring_slots)][P.batch - 1];
+  const PersistentFn f = (P.profile || P.waits) ? kPersistentProf[P.batch - 1] : kPersistent[P.batch - 1];
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(f), dim3(grid), dim3(kThreads), args, lds, s);
 }
 
 hipError_t launch_op(const Params& P, int first, int count, int lds, hipStream_t s) {
   if (P.batch < 1 || P.batch > kMaxCols) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kOplaunch[depth_index(P.ring_slots)][P.batch - 1], dim3(count), dim3(kThreads), lds, s, P, first);
+  hipLaunchKernelGGL(kOplaunch[P.batch - 1], dim3(count), dim3(kThreads), lds, s, P, first);
   return hipGetLastError();
 }
 

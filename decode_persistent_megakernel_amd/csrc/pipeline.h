@@ -7,70 +7,35 @@
 // block (column blocks 2j and 2j+1; the packing makes the number of column
 // blocks even), or the K block and the V block of one group of positions.
 //
-// A stream wave feeds itself: it copies its items from HBM straight into a
-// private LDS ring of DEPTH slots (LDS DMA), DEPTH items ahead of the one it
-// computes, running ahead across task boundaries so weights keep arriving
-// while the workgroup waits on an event. Copies complete in issue order, so
-// "item k has landed" is a wait for the vector-memory counter to drop to twice
-// the number of younger items; the wave issues no other vector-memory
-// operation while it streams. The copies are inline assembly: the compiler
-// then leaves the wave's own LDS reads alone (it would otherwise wait for
-// every copy in flight before each of them, not knowing which LDS bytes a copy
-// writes).
+// A stream wave loads its weight items straight into registers. A ring of
+// RING items (two 16-byte loads per lane each) stays in flight, and the loads
+// run ahead across task and event boundaries, so weights keep arriving while
+// the workgroup waits on an event. The ring is one fully unrolled pass over
+// its RING register slots: at slot s the wave computes on the item the slot
+// holds, then refills the slot with the item RING places further on. Every
+// pass issues exactly two loads per slot, in slot order, so the compiler's
+// wait before each use is the exact count: the loads of the RING - 1 younger
+// items stay in flight. (Measured on one MI355X: about 7 TB/s over 256
+// compute units with four such waves each, against 5.7 TB/s for four waves
+// copying into LDS rings.)
 //
-// The wave is one loop over items with two cursors over the same task list:
-// the copy cursor (ahead) and the compute cursor. Each cursor's task change is
-// a single, rarely taken path and the per-item work is straight-line code, so
-// the role stays small in the instruction cache and light on registers.
+// Matvec pieces are walked in blocks of RING items; the last block of a piece
+// is filled up with loads of a zero block. Task changes therefore fall between
+// passes: one copy of the task-change code, outside the unrolled pass. The
+// block loaded in one pass is computed in the next.
 //
-// Attention items of a step read KV entries appended in earlier steps, so
-// they are copied only after the stager has passed the step's first
-// dependency (C_STEPOK); weight items never wait for anything but a free slot.
+// Attention pieces are not in the ring: when the compute cursor reaches an
+// attention task, the wave runs it in the task-change path with a ring of its
+// own (kAttRing items) over the chunk's KV entries, while the weight ring's
+// loads stay in flight. The task has been staged, so its step is open; the
+// streamed positions are below p - 1 (the stager supplies p - 1 and p), and
+// those were appended two or more steps back: every task of a step waits,
+// through its events, for the whole step before.
 
-// ---------------------------------------------------------------------------
-// copies
-// ---------------------------------------------------------------------------
-
-// 1 KiB per wave: lane l copies 16 bytes from its own address src into LDS
-// byte address lds + 16*l (lds is wave-uniform; it goes in M0, which this
-// wave's code uses for nothing else). nt: streamed once; sc1: device-coherent.
-__device__ __forceinline__ void copy_nt(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
-__device__ __forceinline__ void copy_sc1(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" : : "v"(src),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ u32x4 ld_u32x4(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt vmcnt(N): vmcnt bits [3:0] and [15:14], expcnt/lgkmcnt at max
-  constexpr int imm = (N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
-  __builtin_amdgcn_s_waitcnt(imm);
-}
-
-// Wait until the item with `younger` items issued after it has landed: at most
-// 2*younger copies may still be in flight. Counts below the steady state
-// round down (a longer wait, never a shorter one).
-template <int DEPTH>
-__device__ __forceinline__ void wait_item(int younger) {
-  cbar();
-  if (younger >= DEPTH - 1) wait_vmcnt<2 * (DEPTH - 1)>();
-  else if (younger >= DEPTH - 2) wait_vmcnt<2 * (DEPTH - 2)>();
-  else if (younger >= DEPTH / 2) wait_vmcnt<2 * (DEPTH / 2)>();
-  else if (younger >= 2) wait_vmcnt<4>();
-  else if (younger == 1) wait_vmcnt<2>();
-  else wait_vmcnt<0>();
-  cbar();
-}
+constexpr int kItemBytes = 2 * kUnitBytes;
 
 __device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 // [a0, a1): piece s of n things cut into kStreams nearly equal contiguous pieces
 __device__ __forceinline__ void piece(int n, int s, int& a0, int& a1) {
@@ -78,108 +43,150 @@ __device__ __forceinline__ void piece(int n, int s, int& a0, int& a1) {
   a1 = (int)((uint32_t)n * (uint32_t)(s + 1) / kStreams);
 }
 
-constexpr int kItemBytes = 2 * kUnitBytes;
-
 // ---------------------------------------------------------------------------
-// the copy cursor
+// pieces and blocks
 // ---------------------------------------------------------------------------
 
-struct Fetch {
-  int r, step;        // stream record and step of the task being copied
-  int t, n;           // next item of this wave in the task, and its item count
-  bool kv, done;
-  int pos0, last;     // attention: this lane's position in the piece's first block; last cached position
-  int ppi;            // attention: positions per item
-  const uint8_t* src; // matvec: this lane's 16 bytes of the next item; attention: the (layer, b, g) K rows
-  int issued;         // items copied so far (all tasks)
-  uint32_t soff;      // ring byte offset of the slot of item `issued`
+// Wave s's piece of one stream record at one step: its item count and where
+// item i lives. Both kinds are read through buffer resources: weights from
+// one resource (the item's two units are 1 KiB apart), attention from the K
+// rows and the V rows of its (layer, sequence, kv group).
+struct Piece {
+  int n;                 // items
+  bool kv;
+  rsrc_t ra, rb;         // resources of an item's first and second unit
+  int kpos, ppi, last;   // attention: this lane's position in item 0; positions per item; last streamed position
+  uint32_t lane_off;     // this lane's byte offset within a unit (weights) or a position's row (attention)
 };
 
-// Ring slots are visited in order: the next slot's byte offset.
-template <int DEPTH>
-__device__ __forceinline__ uint32_t next_slot_off(uint32_t off) {
-  off += kItemBytes;
-  return off == (uint32_t)DEPTH * kItemBytes ? 0u : off;
+// The streamed positions of attention chunk `chunk` for a sequence at position
+// p: [lo, end), the chunk's share of [0, p + 1) minus p - 1 and p.
+__device__ __forceinline__ void att_stream_range(int chunk, int p, int Nc, int& lo, int& end) {
+  const int64_t len = (int64_t)p + 1;
+  lo = chunk_bound(chunk, len, Nc);
+  end = max(lo, min(chunk_bound(chunk + 1, len, Nc), p - 1));
 }
 
-// Move to the next task (in queue order, across steps) that has items for
-// wave s. A matvec piece is whole items; an attention piece is a run of
-// position blocks of the chunk's cached positions [lo, end).
-__device__ __forceinline__ void fetch_next_task(const Params& P, const Ctx& cx, int s, Fetch& F) {
-  F.t = 0;
-  F.n = 0;
-  for (;;) {
-    if (++F.r >= cx.nrec) {
-      F.r = 0;
-      ++F.step;
-    }
-    if (F.step >= P.n_steps || cx.nrec == 0) {
-      F.done = true;
-      return;
-    }
-    const StreamRec R = cx.recs[F.r];
-    const uint32_t tsbg = rfl(R.tsbg);
-    F.kv = (tsbg & 15) == T_ATT;
-    if (F.kv) {
-      const int b = (tsbg >> 6) & 1023;
-      if (b >= P.batch) continue;
-      const int pos = ld_uniform(P.pos_in, b) + F.step;
-      if (pos < 0 || pos >= P.S) continue;
-      const uint32_t lc = rfl(R.lc);
-      const int layer = lc & 0xffff, chunk = lc >> 16, g = tsbg >> 16;
-      const int64_t len = (int64_t)pos + 1;
-      const int lo = chunk_bound(chunk, len, P.Nc);
-      const int end = min(chunk_bound(chunk + 1, len, P.Nc), pos);
-      const int lpp = P.D / 8;
-      F.ppi = 64 / lpp;
-      const int nb = end > lo ? (end - lo + F.ppi - 1) / F.ppi : 0;
-      int j0, j1;
-      piece(nb, s, j0, j1);
-      F.n = j1 - j0;
-      F.pos0 = lo + j0 * F.ppi + cx.lane / lpp;
-      F.last = end - 1;
-      F.src = reinterpret_cast<const uint8_t*>(P.kcache + (((size_t)layer * P.B + b) * P.Hkv + g) * (size_t)P.S * P.D) +
-              (cx.lane % lpp) * 16;
-    } else {
-      const int items = (int)rfl((uint32_t)R.n_units) / 2;
-      int i0, i1;
-      piece(items, s, i0, i1);
-      F.n = i1 - i0;
-      const int64_t woff =
-          (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
-      F.src = P.wpack + woff + (int64_t)i0 * kItemBytes + cx.lane * 16;
-    }
-    if (F.n > 0) return;
-  }
+__device__ __forceinline__ rsrc_t zero_rsrc(const Params& P, const Ctx& cx) {
+  return make_rsrc(P.zeros + (size_t)rfl((uint32_t)cx.cu & (kZeroBlocks - 1)) * 2 * kUnitBytes, 2 * kUnitBytes);
 }
 
-// Copy items until `limit` have been issued, the task sequence ends, or the
-// next item is a KV block of a step the stager has not opened yet.
-template <int DEPTH>
-__device__ __forceinline__ void fetch_upto(const Params& P, const Ctx& cx, int s, Fetch& F, int limit,
-                                           uint32_t ring) {
-  while (F.issued < limit) {
-    if (F.t == F.n) {
-      fetch_next_task(P, cx, s, F);
-      if (F.done) return;
+// Wave s's piece of a matvec record (an attention record has no ring items).
+__device__ __forceinline__ Piece make_piece(const Params& P, const Ctx& cx, int s, int r) {
+  Piece pc;
+  pc.n = 0;
+  pc.kv = false;
+  pc.ra = pc.rb = zero_rsrc(P, cx);
+  pc.kpos = 0;
+  pc.ppi = 1;
+  pc.last = 0;
+  pc.lane_off = (uint32_t)cx.lane * 16u;
+  const StreamRec R = cx.recs[r];
+  const uint32_t tsbg = rfl(R.tsbg);
+  if ((tsbg & 15) == T_ATT) return pc;
+  const int items = (int)rfl((uint32_t)R.n_units) / 2;
+  int i0, i1;
+  piece(items, s, i0, i1);
+  pc.n = i1 - i0;
+  const int64_t woff =
+      (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
+  pc.ra = pc.rb = make_rsrc(P.wpack + woff + (int64_t)i0 * kItemBytes, (uint32_t)pc.n * (uint32_t)kItemBytes);
+  return pc;
+}
+
+// Wave s's piece of attention task (layer, b, g, chunk) for a sequence at
+// position p: `n` blocks of ppi positions from lo + u0 * ppi, the last
+// streamed position `last`.
+__device__ __forceinline__ Piece make_kv_piece(const Params& P, const Ctx& cx, int layer, int b, int g, int lo, int end,
+                                               int u0, int n) {
+  Piece pc;
+  const int lpp = P.D / 8;
+  pc.n = n;
+  pc.kv = true;
+  pc.ppi = 64 / lpp;
+  pc.kpos = lo + u0 * pc.ppi + cx.lane / lpp;
+  pc.last = end - 1;
+  pc.lane_off = (uint32_t)(cx.lane % lpp) * 16u;
+  const size_t row = (((size_t)layer * P.B + b) * P.Hkv + g) * (size_t)P.S * P.D;
+  pc.ra = make_rsrc(P.kcache + row, (uint32_t)P.S * (uint32_t)P.D * 2u);
+  pc.rb = make_rsrc(P.vcache + row, (uint32_t)P.S * (uint32_t)P.D * 2u);
+  return pc;
+}
+
+// A block: up to RING consecutive items of one piece.
+struct Blk {
+  int r, step;  // stream record and step
+  int n;        // real items (0: a null block, nothing to compute)
+  int i0;       // its first item's index in the piece
+  int flags;    // kFirst, kLast, kEnd
+};
+enum { kFirst = 1, kLast = 2, kEnd = 4 };
+
+// The walk over this wave's pieces, in queue order, step by step (empty
+// pieces skipped).
+struct Walk {
+  int r, step, t;  // current piece, next item in it
+  Piece pc;
+};
+
+// Loads of item i of piece pc into one ring slot (a zero item when !real):
+// always the same two non-temporal loads (every byte is read once per step);
+// only the resources and offsets differ, selected without a branch, so the
+// compiler sees one instruction sequence per slot. Zero items read this
+// compute unit's own 2 KiB of zeros (they stay in its L2).
+//
+// KV entries need no device-coherent load: within a launch an entry is read
+// only in steps after the one that appended it (the streamed positions are
+// below p - 1), each position's row fills whole 128-byte lines of its own, so
+// no cache can hold a line of it from before the append; and kernel
+// boundaries write back and invalidate the caches.
+__device__ __forceinline__ void load_item(const Params& P, const Ctx& cx, const Piece& pc, int i, bool real, u32x4& a,
+                                          u32x4& b) {
+  const rsrc_t z = make_rsrc(P.zeros + (size_t)rfl((uint32_t)cx.cu & (kZeroBlocks - 1)) * 2 * kUnitBytes, 2 * kUnitBytes);
+  const bool kv = real && pc.kv;
+  const uint32_t koff = (uint32_t)min(pc.kpos + i * pc.ppi, pc.last) * (uint32_t)P.D * 2u + pc.lane_off;
+  const uint32_t woff = (uint32_t)i * (uint32_t)kItemBytes + pc.lane_off;
+  const uint32_t offa = kv ? koff : real ? woff : (uint32_t)cx.lane * 16u;
+  const uint32_t offb = kv ? koff : offa + kUnitBytes;
+  const rsrc_t ra = real ? pc.ra : z;
+  const rsrc_t rb = real ? pc.rb : z;
+  a = __builtin_amdgcn_raw_buffer_load_b128(ra, offa, 0, kAuxStream);
+  b = __builtin_amdgcn_raw_buffer_load_b128(rb, offb, 0, kAuxStream);
+}
+
+// The next block of the walk over this wave's matvec pieces (kEnd past the
+// last step).
+template <int RING>
+__device__ __forceinline__ Blk next_block(const Params& P, const Ctx& cx, int s, Walk& W) {
+  Blk B;
+  B.i0 = 0;
+  B.n = 0;
+  if (W.t >= W.pc.n) {
+    for (;;) {
+      if (++W.r >= cx.nrec) {
+        W.r = 0;
+        ++W.step;
+      }
+      if (W.step >= P.n_steps || cx.nrec == 0) {
+        B.r = W.r;
+        B.step = W.step;
+        B.flags = kEnd;
+        W.pc.n = 0;
+        W.t = 0;
+        return B;
+      }
+      W.pc = make_piece(P, cx, s, W.r);
+      W.t = 0;
+      if (W.pc.n > 0) break;
     }
-    const uint32_t dst = ring + F.soff;
-    if (!F.kv) {
-      copy_nt(F.src, dst);
-      copy_nt(F.src + kUnitBytes, dst + kUnitBytes);
-      F.src += kItemBytes;
-    } else {
-      if (F.t == 0 && lds_ld(&cx.ctl[C_STEPOK]) < F.step + 1) return;
-      const int pos = min(F.pos0 + F.t * F.ppi, F.last);
-      const uint8_t* kb = F.src + (size_t)pos * P.D * 2;
-      copy_sc1(kb, dst);
-      copy_sc1(kb + (reinterpret_cast<const uint8_t*>(P.vcache) - reinterpret_cast<const uint8_t*>(P.kcache)),
-               dst + kUnitBytes);
-    }
-    ++F.issued;
-    ++F.t;
-    F.soff = next_slot_off<DEPTH>(F.soff);
   }
+  B.r = W.r;
+  B.step = W.step;
+  B.i0 = W.t;
+  B.n = min(RING, W.pc.n - W.t);
+  B.flags = (W.t == 0 ? kFirst : 0) | (W.t + B.n == W.pc.n ? kLast : 0);
+  W.t += B.n;
+  return B;
 }
 
 // ---------------------------------------------------------------------------
@@ -188,14 +195,17 @@ __device__ __forceinline__ void fetch_upto(const Params& P, const Ctx& cx, int s
 
 struct Comp {
   int r, step;     // stream record and step of the task being computed
-  int slot, type;  // type -1: none
-  int left;        // items of this wave left in the task
+  int slot, type;  // staging slot; type -1: none
   int rb, kb, KB;  // matvec: row block and column block of the next item, column blocks
   int rb0;         // matvec: first row block of this wave's piece (its partial sums start there)
-  int k0;          // items consumed before the task (profile)
   bool pend;       // matvec: sums of an unfinished row block are held
-  int t, lo, end;  // attention: next block, cached positions [lo, end) of the chunk
-  int u0;          // attention: first block of this wave
+  bool any;        // the piece has items
+  int lo, end, u0; // attention: streamed positions [lo, end) of the chunk, first block of this wave
+  int natt;        // attention: blocks of this wave
+  int layer, b, g; // attention: the task's layer, sequence and kv group
+  float* part;     // partial sums (LDS)
+  const float* hin;
+  int kp;
 };
 
 template <int NC>
@@ -216,58 +226,12 @@ __device__ __forceinline__ float dot8(const u32x4 w, const float4 x, const float
   return a + b;
 }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 to_f4(const f32x4 v) { return make_float4(v.x, v.y, v.z, v.w); }
-
-// One column's LDS operands of two items at once: both items' weight units and
-// the activations of their column blocks, all twelve reads issued before one
-// wait (inside the block, so no read is in flight when it ends). w: the items'
-// slots (this lane's 16 bytes); ha, hb: the column blocks' activations (this
-// lane's first float).
-__device__ __forceinline__ void lds_two_items(uint32_t i0, uint32_t i1, uint32_t ha, uint32_t hb, u32x4 (&w)[4],
-                                              f32x4 (&a)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %12 offset:1024\n\t"
-      "ds_read_b128 %2, %13\n\t"
-      "ds_read_b128 %3, %13 offset:1024\n\t"
-      "ds_read_b128 %4, %14\n\t"
-      "ds_read_b128 %5, %14 offset:256\n\t"
-      "ds_read_b128 %6, %14 offset:512\n\t"
-      "ds_read_b128 %7, %14 offset:768\n\t"
-      "ds_read_b128 %8, %15\n\t"
-      "ds_read_b128 %9, %15 offset:256\n\t"
-      "ds_read_b128 %10, %15 offset:512\n\t"
-      "ds_read_b128 %11, %15 offset:768\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
-        "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
-      : "v"(i0), "v"(i1), "v"(ha), "v"(hb)
-      : "memory");
-}
-
-// The same for one item: its two weight units and its column blocks' activations.
-__device__ __forceinline__ void lds_one_item(uint32_t i0, uint32_t ha, u32x4 (&w)[2], f32x4 (&a)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %6 offset:1024\n\t"
-      "ds_read_b128 %2, %7\n\t"
-      "ds_read_b128 %3, %7 offset:256\n\t"
-      "ds_read_b128 %4, %7 offset:512\n\t"
-      "ds_read_b128 %5, %7 offset:768\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-      : "v"(i0), "v"(ha)
-      : "memory");
-}
-
 // The row sums of row block rb (counted from the piece's first), reduced over
-// the 16 lanes of each row, as this wave's partial sums. Every lane of row j holds the sum and all of them
-// store it to row j's word: no lane-dependent branch in the stream loop (a
-// divergent branch there would make the loop's own control divergent).
+// the 16 lanes of each row, as this wave's partial sums. Every lane of row j
+// holds the sum and all of them store it to row j's word (no lane-dependent
+// branch).
 template <int NC>
-__device__ __forceinline__ void mv_flush(Acc<NC>& A, float* pout, int cs, int rb, int icol) {
-  (void)icol;
+__device__ __forceinline__ void mv_flush(Acc<NC>& A, float* pout, int cs, int rb) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     pout[c * cs + rb * 4] = sum16(A.a[c]);
@@ -275,19 +239,20 @@ __device__ __forceinline__ void mv_flush(Acc<NC>& A, float* pout, int cs, int rb
   }
 }
 
-// Attention state of one wave over its piece: G query heads, this lane's 8
-// dims of the query and of the output accumulator, and the running maximum and
-// denominator of this lane's position group (the lanes that share a
-// position). The groups are merged once, at the end of the piece.
+// Attention state of one wave over its piece: for G query heads, this lane's 8
+// dims of the output accumulator, and the running maximum and denominator of
+// this lane's position group (the lanes that share a position). The groups are
+// merged once, at the end of the piece. The scaled queries are read from the
+// staging slot (qs, this lane's 8 dims at de).
 struct AttState {
-  float q[kMaxG][8], acc[kMaxG][8], m[kMaxG], l[kMaxG];
+  float acc[kMaxG][8], m[kMaxG], l[kMaxG];
+  const float* qs;
 };
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Reduce over the position groups of a wave (lanes equal modulo lpp, which is
-// 8 or 16; l16: lpp is 16): max or sum. One code path for both head widths
-// keeps the kernel small.
+// 8 or 16; l16: lpp is 16): max or sum.
 template <bool MAX>
 __device__ __forceinline__ float across_groups(float v, bool l16) {
   float lo, hi;
@@ -321,9 +286,11 @@ __device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     if (h < P.G) {
+      const float4 q0 = ld_f4(S.qs + h * P.D), q1 = ld_f4(S.qs + h * P.D + 4);
+      const float q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(S.q[h][e], kf[e], d);
+      for (int e = 0; e < 8; ++e) d = fmaf(q[e], kf[e], d);
       const float sc = valid ? in_group(d, l16) : -INFINITY;
       const float mn = fmaxf(S.m[h], sc);
       const float al = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(S.m[h] - mn);
@@ -368,280 +335,245 @@ __device__ __forceinline__ void att_finish(const Params& P, AttState& S, float* 
   }
 }
 
-// Items of a matvec piece, two at a time while both have been copied,
-// refilling the ring from the same copy task; returns to the caller (which
-// owns the slow paths) when the compute task ends, the next item is not copied
-// yet, or the copy cursor reaches the end of its task. koff: ring byte offset
-// of item k's slot.
-template <int DEPTH, int NC>
-__device__ __forceinline__ void matvec_run(const Params& P, Comp& C, Fetch& F, int& k, uint32_t& koff,
-                                           uint32_t ring, const uint8_t* rp, const float* hin, int kp, float* pout,
-                                           int icol, Acc<NC>& A, uint32_t& t_first, bool prof) {
-  const int KB = C.KB;
-  const float* h = hin + icol * 4;
-  if (prof && t_first == 0 && F.issued > k) {
-    wait_item<DEPTH>(F.issued - k - 1);
-    t_first = rfl((uint32_t)wall_clock64());
-  }
-  for (;;) {
-    const int ready = F.issued - k;
-    if (ready >= 2 && C.left >= 2) {
-      wait_item<DEPTH>(ready - 2);
-      const uint32_t k1off = next_slot_off<DEPTH>(koff);
-      const uint8_t* i0 = rp + koff;
-      const uint8_t* i1 = rp + k1off;
-      const int kb1 = C.kb + 2 == KB ? 0 : C.kb + 2;
-      float d0[NC], d1[NC];
-      if constexpr (NC == 1) {
-        u32x4 w[4];
-        f32x4 a[8];
-        lds_two_items(lds_addr(i0), lds_addr(i1), lds_addr(h + C.kb * kUnitCols), lds_addr(h + kb1 * kUnitCols), w, a);
-        d0[0] = dot8(w[0], to_f4(a[0]), to_f4(a[1])) + dot8(w[1], to_f4(a[2]), to_f4(a[3]));
-        d1[0] = dot8(w[2], to_f4(a[4]), to_f4(a[5])) + dot8(w[3], to_f4(a[6]), to_f4(a[7]));
-      } else {
-        const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
-        const u32x4 w2 = ld_u32x4(i1), w3 = ld_u32x4(i1 + kUnitBytes);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float* ha = h + c * kp + C.kb * kUnitCols;
-          const float* hb = h + c * kp + kb1 * kUnitCols;
-          d0[c] = dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
-          d1[c] = dot8(w2, ld_f4(hb), ld_f4(hb + 64)) + dot8(w3, ld_f4(hb + kUnitCols), ld_f4(hb + kUnitCols + 64));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) A.a[c] += d0[c];
-      C.kb += 2;
-      if (C.kb == KB) {
-        mv_flush<NC>(A, pout, P.wave_vrows, C.rb - C.rb0, icol);
-        C.kb = 0;
-        ++C.rb;
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) A.a[c] += d1[c];
-      C.kb += 2;
-      C.pend = true;
-      if (C.kb == KB) {
-        mv_flush<NC>(A, pout, P.wave_vrows, C.rb - C.rb0, icol);
-        C.kb = 0;
-        ++C.rb;
-        C.pend = false;
-      }
-      k += 2;
-      koff = next_slot_off<DEPTH>(k1off);
-      C.left -= 2;
-      // steady state: the two slots just read take the copy task's next two items
-      if (!F.kv && F.t + 2 <= F.n && F.issued + 2 <= k + DEPTH) {
-        const uint32_t d0s = ring + F.soff;
-        const uint32_t s1 = next_slot_off<DEPTH>(F.soff);
-        const uint32_t d1s = ring + s1;
-        copy_nt(F.src, d0s);
-        copy_nt(F.src + kUnitBytes, d0s + kUnitBytes);
-        copy_nt(F.src + kItemBytes, d1s);
-        copy_nt(F.src + kItemBytes + kUnitBytes, d1s + kUnitBytes);
-        F.src += 2 * kItemBytes;
-        F.issued += 2;
-        F.t += 2;
-        F.soff = next_slot_off<DEPTH>(s1);
-        continue;
-      }
-    } else if (ready >= 1 && C.left >= 1) {
-      wait_item<DEPTH>(ready - 1);
-      const uint8_t* i0 = rp + koff;
-      if constexpr (NC == 1) {
-        u32x4 w[2];
-        f32x4 a[4];
-        lds_one_item(lds_addr(i0), lds_addr(h + C.kb * kUnitCols), w, a);
-        A.a[0] += dot8(w[0], to_f4(a[0]), to_f4(a[1])) + dot8(w[1], to_f4(a[2]), to_f4(a[3]));
-      } else {
-        const u32x4 w0 = ld_u32x4(i0), w1 = ld_u32x4(i0 + kUnitBytes);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float* ha = h + c * kp + C.kb * kUnitCols;
-          A.a[c] += dot8(w0, ld_f4(ha), ld_f4(ha + 64)) + dot8(w1, ld_f4(ha + kUnitCols), ld_f4(ha + kUnitCols + 64));
-        }
-      }
-      C.kb += 2;
-      C.pend = true;
-      if (C.kb == KB) {
-        mv_flush<NC>(A, pout, P.wave_vrows, C.rb - C.rb0, icol);
-        C.kb = 0;
-        ++C.rb;
-        C.pend = false;
-      }
-      k += 1;
-      koff = next_slot_off<DEPTH>(koff);
-      C.left -= 1;
-    } else {
-      return;
-    }
-    // refill the read slots from the current copy task (weights only)
-    if (F.kv) return;
-    while (F.issued < k + DEPTH && F.t < F.n) {
-      const uint32_t dst = ring + F.soff;
-      copy_nt(F.src, dst);
-      copy_nt(F.src + kUnitBytes, dst + kUnitBytes);
-      F.src += kItemBytes;
-      ++F.issued;
-      ++F.t;
-      F.soff = next_slot_off<DEPTH>(F.soff);
-    }
-    if (C.left == 0 || F.issued < k + DEPTH) return;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // stream wave
 // ---------------------------------------------------------------------------
 
-template <int DEPTH, int NC, bool PROF>
+// Start computing record r at `step`: wait for its staging, then set up the
+// matvec cursor or the attention state.
+template <int NC, bool PROF>
+__device__ __forceinline__ bool comp_start(const Params& P, const Ctx& cx, int s, Comp& C, Acc<NC>& A, AttState& S,
+                                           Waits& wt, bool prof) {
+  const int lane = cx.lane;
+  const StreamRec R = cx.recs[C.r];
+  const uint32_t tsbg = rfl(R.tsbg), kq = rfl(R.kq);
+  C.type = tsbg & 15;
+  C.slot = (tsbg >> 4) & 3;
+  if (C.slot < 2) C.slot ^= (int)rfl((uint32_t)R.flip) & C.step;
+  {
+    const uint64_t s0 = waits_now(wt);
+    if (!spin_ctl(P, cx, C_STAGED, C.step * (cx.q1 - cx.q0) + (int)(kq >> 16) + 1)) return false;
+    waits_add(wt, 2, s0);
+  }
+  if (prof) prof_words(cx, C.slot, s)[0] = rfl((uint32_t)wall_clock64());
+  C.hin = slot_ptr(cx, C.slot) + kHdr;
+  if (C.type == T_ATT) {
+    C.part = att_part_ptr(P, cx, C.slot);
+    const int* ih = reinterpret_cast<const int*>(slot_ptr(cx, C.slot));
+    const int flags = lds_ld(&ih[H_FLAGS]);
+    C.lo = lds_ld(&ih[H_LO]);
+    C.end = lds_ld(&ih[H_END]);
+    const int lpp = P.D / 8, ppi = 64 / lpp;
+    const int nb = (flags & 1) && C.end > C.lo ? (C.end - C.lo + ppi - 1) / ppi : 0;
+    int j1;
+    piece(nb, s, C.u0, j1);
+    C.natt = j1 - C.u0;
+    const uint32_t lc = rfl(R.lc);
+    C.layer = lc & 0xffff;
+    C.b = (tsbg >> 6) & 1023;
+    C.g = tsbg >> 16;
+    S.qs = att_qs_ptr(P, cx, C.slot) + (lane % lpp) * 8;
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      S.m[h] = -INFINITY;
+      S.l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) S.acc[h][e] = 0.f;
+    }
+  } else {
+    C.part = part_ptr(cx, C.slot) + (size_t)s * P.ncap * P.wave_vrows + (lane >> 4);
+    const int items = (int)rfl((uint32_t)R.n_units) / 2;
+    int i0, i1;
+    piece(items, s, i0, i1);
+    C.KB = kq & 0xffff;
+    C.rb = (2 * i0) / C.KB;
+    C.rb0 = C.rb;
+    C.kb = 2 * i0 - C.rb * C.KB;
+    C.pend = false;
+    C.kp = slot_kp(P, C.slot);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) A.a[c] = 0.f;
+  }
+  C.any = false;
+  return true;
+}
+
+// Finish the task being computed: store this wave's partials (and the row
+// blocks they cover) and count the wave done.
+template <int NC>
+__device__ __forceinline__ void comp_finish(const Params& P, const Ctx& cx, int s, Comp& C, Acc<NC>& A, AttState& S,
+                                            bool prof, uint32_t t_first) {
+  if (C.type == T_ATT) {
+    att_finish(P, S, C.part, s, cx.lane, !C.any);
+  } else {
+    if (C.pend) mv_flush<NC>(A, C.part, P.wave_vrows, C.rb - C.rb0);
+    // the row blocks this piece touched (b < a: none), for the retirer's sums
+    int* pr = piece_words(cx, C.slot, s);
+    pr[0] = C.rb0;
+    pr[1] = !C.any ? C.rb0 - 1 : (C.pend ? C.rb : C.rb - 1);
+  }
+  if (prof) {
+    uint32_t* pw = prof_words(cx, C.slot, s);
+    pw[1] = t_first;
+    pw[2] = rfl((uint32_t)wall_clock64());
+  }
+  lds_add_lane0(&cx.ctl[C_DONE + ctl_slot(C.slot)], 1);
+  C.type = -1;
+}
+
+// One matvec item (weight units w0, w1 = column blocks kb, kb + 1 of row block
+// rb) against the staged activations of NC columns.
+template <int NC>
+__device__ __forceinline__ void mv_item(const Params& P, Comp& C, Acc<NC>& A, const u32x4 w0, const u32x4 w1,
+                                        int icol) {
+  const float* h = C.hin + icol * 4 + C.kb * kUnitCols;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float* hc = h + c * C.kp;
+    A.a[c] += dot8(w0, ld_f4(hc), ld_f4(hc + 64)) + dot8(w1, ld_f4(hc + kUnitCols), ld_f4(hc + kUnitCols + 64));
+  }
+  C.kb += 2;
+  C.pend = true;
+  if (C.kb == C.KB) {
+    mv_flush<NC>(A, C.part, P.wave_vrows, C.rb - C.rb0);
+    C.kb = 0;
+    ++C.rb;
+    C.pend = false;
+  }
+}
+
+// An attention task's piece: the chunk's streamed KV blocks of this wave,
+// through a ring of kAttRing register slots (the same unrolled pass as the
+// weight ring: compute the slot's block, then refill the slot).
+constexpr int kAttRing = 4;
+__device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C, AttState& S) {
+  const int lane = cx.lane, lpp = P.D / 8, ppi = 64 / lpp;
+  const bool l16 = lpp == 16;
+  const Piece pc = make_kv_piece(P, cx, C.layer, C.b, C.g, C.lo, C.end, C.u0, C.natt);
+  u32x4 ka[kAttRing], kv[kAttRing];
+#pragma unroll
+  for (int j = 0; j < kAttRing; ++j) ka[j] = kv[j] = u32x4{0u, 0u, 0u, 0u};
+  int cn = 0, cbase = 0, base = 0;  // blocks computed in this pass (loaded in the last), their first; next to load
+  for (;;) {
+    cn = (int)rfl((uint32_t)cn);
+    asm volatile("" : "+s"(cn));  // opaque: no peeled first pass
+    const int ln = min(kAttRing, max(0, pc.n - base));
+#pragma unroll
+    for (int j = 0; j < kAttRing; ++j) {
+      asm volatile("" : : "v"(ka[j]), "v"(kv[j]));
+      if (j < cn) {
+        const bool valid = C.lo + (C.u0 + cbase + j) * ppi + lane / lpp < C.end;
+        att_item(P, S, ka[j], kv[j], valid, l16);
+      }
+      load_item(P, cx, pc, base + j, j < ln, ka[j], kv[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ln == 0) break;
+    cbase = base;
+    cn = ln;
+    base += kAttRing;
+  }
+  // the last pass's zero loads: let them land here, so that the weight ring's
+  // waits after this path keep their exact counts
+  wait_all();
+  C.any = pc.n > 0;
+}
+
+template <int RING, int NC, bool PROF>
 __device__ __forceinline__ void run_stream(const Params& P0, const Ctx& cx, int s) {
   const Params& P = P0;
-  const int lane = cx.lane, jrow = lane >> 4, icol = lane & 15;
-  const uint32_t ring = lds_addr(cx.ring) + (uint32_t)s * DEPTH * kItemBytes;
-  const uint8_t* rp = cx.ring + (size_t)s * DEPTH * kItemBytes + lane * 16;  // this lane's bytes of slot 0
+  const int lane = cx.lane, icol = lane & 15;
   const bool prof = PROF && P.profile != nullptr;
-  const int lpp = P.D / 8, ppi = 64 / lpp;
-  Waits wt;  // j0: KV step not open; j2: task not staged; j3: items
+  Waits wt;  // j2: task not staged; j3: items
   waits_init<PROF>(P, cx, wt);
 
-  Fetch F;
-  F.r = -1;
-  F.step = 0;
-  F.t = F.n = 0;
-  F.issued = 0;
-  F.done = false;
+  Walk W;
+  W.r = -1;
+  W.step = 0;
+  W.t = 0;
+  W.pc = make_piece(P, cx, s, 0);
+  W.pc.n = 0;
 
   Comp C;
   C.r = -1;
   C.step = 0;
-  C.left = 0;
   C.type = -1;
   C.slot = 0;
-  int k = 0;  // items consumed
-  const float* hin = nullptr;
-  float* part = nullptr;
-  int kp = 0;
+  C.any = false;
   Acc<NC> A;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) A.a[c] = 0.f;
   AttState S;
   uint32_t t_first = 0;
-  uint32_t koff = 0;  // ring byte offset of item k's slot
-  F.soff = 0;
 
+  u32x4 ra[RING], rb[RING];
+#pragma unroll
+  for (int j = 0; j < RING; ++j) ra[j] = rb[j] = u32x4{0u, 0u, 0u, 0u};
+
+  bool fin = false;  // the task being computed has had all its items: finish it
+  Blk cur;           // the block the ring holds, computed in this pass (none in the first pass)
+  cur.r = 0;
+  cur.step = 0;
+  cur.n = 0;
+  cur.i0 = 0;
+  cur.flags = 0;
   for (;;) {
+    cur.n = (int)rfl((uint32_t)cur.n);
+    cur.flags = (int)rfl((uint32_t)cur.flags);
+    asm volatile("" : "+s"(cur.n), "+s"(cur.flags));  // opaque: no peeled first pass (it would load in another order)
     const Params& P = fresh_params();
-    // refill every slot whose item has been read
-    wait_lgkm();
-    fetch_upto<DEPTH>(P, cx, s, F, k + DEPTH, ring);
-
-    if (C.left == 0) {
-      // ---- the compute cursor's task change: finish the task, start the next
-      if (C.type >= 0) {
+    if (fin || (cur.flags & (kFirst | kEnd))) {
+      // The compute cursor's task changes, all here (one copy of the code):
+      // finish the task whose items are done; walk the records up to this
+      // block's piece (and start it) or to the end. Records on the way have no
+      // ring items for this wave: attention tasks run here, matvec pieces
+      // without items are started and finished at once (the retirer waits for
+      // every stream wave on every stream task).
+      for (;;) {
+        if (fin) {
+          comp_finish<NC>(P, cx, s, C, A, S, prof, t_first);
+          fin = false;
+        }
+        if (C.type >= 0) break;
+        int r = C.r + 1, st = C.step;
+        if (r >= cx.nrec) {
+          r = 0;
+          ++st;
+        }
+        if (st >= P.n_steps || cx.nrec == 0) break;
+        const bool at = r == cur.r && st == cur.step;
+        C.r = r;
+        C.step = st;
+        if (!comp_start<NC, PROF>(P, cx, s, C, A, S, wt, prof)) return;
+        t_first = 0;
+        if (at) break;
         if (C.type == T_ATT) {
-          att_finish(P, S, part, s, lane, C.t == 0);
-        } else {
-          if (C.pend) mv_flush<NC>(A, part + (size_t)s * P.ncap * P.wave_vrows + jrow, P.wave_vrows, C.rb - C.rb0, icol);
-          // the row blocks this piece touched (b < a: none), for the retirer's sums
-          int* pr = piece_words(cx, C.slot, s);
-          pr[0] = C.rb0;
-          pr[1] = C.k0 == k ? C.rb0 - 1 : (C.pend ? C.rb : C.rb - 1);
+          if (prof) t_first = rfl((uint32_t)wall_clock64());
+          att_run(P, cx, C, S);
         }
-        if (prof) {
-          uint32_t* pw = prof_words(cx, C.slot, s);
-          pw[1] = t_first;
-          pw[2] = rfl((uint32_t)wall_clock64());
-        }
-        lds_add_lane0(&cx.ctl[C_DONE + ctl_slot(C.slot)], 1);
-        C.type = -1;
+        fin = true;
       }
-      if (++C.r >= cx.nrec) {
-        C.r = 0;
-        ++C.step;
-      }
-      if (C.step >= P.n_steps || cx.nrec == 0) break;
-      const StreamRec R = cx.recs[C.r];
-      const uint32_t tsbg = rfl(R.tsbg), kq = rfl(R.kq);
-      C.type = tsbg & 15;
-      C.slot = (tsbg >> 4) & 3;
-      if (C.slot < 2) C.slot ^= (int)rfl((uint32_t)R.flip) & C.step;
-      {
-        const uint64_t s0 = waits_now(wt);
-        if (!spin_ctl(P, cx, C_STAGED, C.step * (cx.q1 - cx.q0) + (int)(kq >> 16) + 1)) return;
-        waits_add(wt, 2, s0);
-      }
-      t_first = 0;
-      C.k0 = k;
-      if (prof) prof_words(cx, C.slot, s)[0] = rfl((uint32_t)wall_clock64());
-      hin = slot_ptr(cx, C.slot) + kHdr;
-      part = C.type == T_ATT ? att_part_ptr(P, cx, C.slot) : part_ptr(cx, C.slot);
-      if (C.type == T_ATT) {
-        const int* ih = reinterpret_cast<const int*>(slot_ptr(cx, C.slot));
-        const int flags = lds_ld(&ih[H_FLAGS]);
-        C.lo = lds_ld(&ih[H_LO]);
-        C.end = lds_ld(&ih[H_END]);
-        const int nb = (flags & 1) && C.end > C.lo ? (C.end - C.lo + ppi - 1) / ppi : 0;
-        int j1;
-        piece(nb, s, C.u0, j1);
-        C.left = j1 - C.u0;
-        C.t = 0;
-        const float* q = hin + att_raw_floats(P);
-        const int de = (lane % lpp) * 8;
-        const float qs = P.attn_scale * kLog2e;  // scores in base-2 units
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-          S.m[h] = -INFINITY;
-          S.l[h] = 0.f;
-          float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
-          if (h < P.G) {
-            x = ld_f4(q + h * P.D + de);
-            y = ld_f4(q + h * P.D + de + 4);
-          }
-          S.q[h][0] = x.x * qs; S.q[h][1] = x.y * qs; S.q[h][2] = x.z * qs; S.q[h][3] = x.w * qs;
-          S.q[h][4] = y.x * qs; S.q[h][5] = y.y * qs; S.q[h][6] = y.z * qs; S.q[h][7] = y.w * qs;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) S.acc[h][e] = 0.f;
-        }
-      } else {
-        const int items = (int)rfl((uint32_t)R.n_units) / 2;
-        int i0, i1;
-        piece(items, s, i0, i1);
-        C.left = i1 - i0;
-        C.KB = kq & 0xffff;
-        C.rb = (2 * i0) / C.KB;
-        C.rb0 = C.rb;
-        C.kb = 2 * i0 - C.rb * C.KB;
-        C.pend = false;
-        kp = slot_kp(P, C.slot);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) A.a[c] = 0.f;
-      }
-      waits_count(wt, 3, C.left);
-      continue;  // the new task may have no items for this wave
+      if (cur.flags & kEnd) break;
     }
-
-    // ---- item k
-    if (F.issued <= k) {
-      // not copied yet: a KV block of a step the stager has not opened
-      const uint64_t s0 = waits_now(wt);
-      if (!spin_ctl(P, cx, C_STEPOK, F.step + 1)) return;
-      waits_add(wt, 0, s0);
-      continue;
+    if (prof && t_first == 0 && cur.n > 0) t_first = rfl((uint32_t)wall_clock64());
+    waits_count(wt, 3, cur.n);
+    // the block to load in this pass
+    const Blk nxt = next_block<RING>(P, cx, s, W);
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      // every slot's item is waited for at its position, computed or not (a
+      // padding item): its registers are then free, and no later write to them
+      // has to wait for a load still in flight
+      asm volatile("" : : "v"(ra[j]), "v"(rb[j]));
+      if (j < cur.n) {
+        C.any = true;
+        mv_item<NC>(P, C, A, ra[j], rb[j], icol);
+      }
+      load_item(P, cx, W.pc, nxt.i0 + j, j < nxt.n, ra[j], rb[j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (C.type == T_ATT) {
-      wait_item<DEPTH>(F.issued - k - 1);
-      if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
-      const uint8_t* it = rp + koff;
-      const u32x4 w0 = ld_u32x4(it), w1 = ld_u32x4(it + kUnitBytes);
-      const bool valid = C.lo + (C.u0 + C.t) * ppi + lane / lpp < C.end;
-      att_item(P, S, w0, w1, valid, lpp == 16);
-      ++C.t;
-      ++k;
-      koff = next_slot_off<DEPTH>(koff);
-      --C.left;
-    } else {
-      matvec_run<DEPTH, NC>(P, C, F, k, koff, ring, rp, hin, kp, part + (size_t)s * P.ncap * P.wave_vrows + jrow,
-                            icol, A, t_first, prof);
-    }
+    if (cur.flags & kLast) fin = true;
+    cur = nxt;
   }
   wait_all();
   waits_put(P, cx, wt);

@@ -197,8 +197,8 @@ int mk_set_wait_counters(mk_model *m, void *d_buf, size_t bytes);
  *   packed_weight_bytes  device bytes of the packed weight copy (padding
  *                        included);
  *   num_cus, n_tasks     workgroups of the persistent launch, tasks per step;
- *   ring_slots           2 KiB ring slots per stream wave (the kernel variant
- *                        mk_persistent_b<batch>_d<ring_slots> runs a call);
+ *   ring_slots           2 KiB items each stream wave keeps in flight (its
+ *                        register ring);
  *   lds_bytes            dynamic LDS per workgroup;
  *   batch_per_launch     the most sequences one launch handles (larger calls
  *                        run in groups of this size).
