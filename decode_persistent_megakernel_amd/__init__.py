@@ -39,7 +39,8 @@ class MKError(RuntimeError):
 class ModelDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
-        "tied_embeddings", "max_batch", "max_seq")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+        "tied_embeddings", "max_batch", "max_seq")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                                                       ("qk_norm", ctypes.c_int32)]
 
 
 class GraphOpts(ctypes.Structure):
@@ -49,7 +50,8 @@ class GraphOpts(ctypes.Structure):
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "g_attn", "g_mlp")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "g_attn", "g_mlp",
+                                               "q_norm", "k_norm")]
 
 
 class Weights(ctypes.Structure):
@@ -133,7 +135,7 @@ def _stream(s) -> int:
 def desc_from_shape(shape, max_batch: int, max_seq: int) -> ModelDesc:
     return ModelDesc(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                      shape.ffn, shape.vocab, int(shape.tied), max_batch, max_seq,
-                     float(shape.rms_eps), float(shape.rope_theta))
+                     float(shape.rms_eps), float(shape.rope_theta), int(getattr(shape, "qk_norm", False)))
 
 
 def mk_build_task_graph(desc: ModelDesc, opts: Optional[GraphOpts] = None) -> int:
@@ -162,11 +164,12 @@ def mk_free_graph(graph: int) -> None:
 
 def mk_load_weights(graph: int, w: Dict[str, object], k_cache, v_cache, n_layers: int, stream=None) -> int:
     """``w`` maps the names embed, lm_head (absent or None when tied), g_final
-    and l{i}.wq ... l{i}.g_mlp to device bf16 tensors (or int pointers)."""
+    and l{i}.wq ... l{i}.g_mlp (and l{i}.q_norm, l{i}.k_norm for a qk_norm
+    model) to device bf16 tensors (or int pointers)."""
     layers = (LayerWeights * n_layers)()
     for l in range(n_layers):
-        for f in ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "g_attn", "g_mlp"):
-            setattr(layers[l], f, _ptr(w[f"l{l}.{f}"]))
+        for f in ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "g_attn", "g_mlp", "q_norm", "k_norm"):
+            setattr(layers[l], f, _ptr(w.get(f"l{l}.{f}")))
     ws = Weights(_ptr(w["embed"]), _ptr(w.get("lm_head")), _ptr(w["g_final"]),
                  ctypes.cast(layers, ctypes.POINTER(LayerWeights)), _ptr(k_cache), _ptr(v_cache))
     m = ctypes.c_void_p()

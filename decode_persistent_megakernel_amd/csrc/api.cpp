@@ -120,6 +120,8 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     const mk_layer_weights& L = w->layers[l];
     if (!L.wq || !L.wk || !L.wv || !L.wo || !L.wg || !L.wu || !L.wd || !L.g_attn || !L.g_mlp)
       return fail(MK_EINVAL, "mk_load_weights: NULL layer weight");
+    if (d.qk_norm && (!L.q_norm || !L.k_norm))
+      return fail(MK_EINVAL, "mk_load_weights: qk_norm model with a NULL q_norm or k_norm");
   }
   const int G = d.n_q_heads / d.n_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -321,7 +323,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   uint16_t *d_embed, *d_gains;
   float2* d_rope;
   if ((rc = m->alloc(&d_wpack, m->packed_bytes, "packed weights")) || (rc = m->alloc(&d_embed, V * H + 512, "embedding")) ||
-      (rc = m->alloc(&d_gains, (2 * L + 1) * H, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")) ||
+      (rc = m->alloc(&d_gains, (2 * L + 1) * H + 2 * L * D, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")) ||
       (rc = m->alloc(&d_zeros, size_t(kZeroBlocks) * 2 * kUnitBytes, "zero blocks")))
     return rc;
   HIP_TRY(hipMemset(d_zeros, 0, size_t(kZeroBlocks) * 2 * kUnitBytes), "clear zero blocks");
@@ -331,6 +333,12 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     HIP_TRY(hipMemcpyAsync(d_gains + (2 * l + 1) * H, w->layers[l].g_mlp, H * 2, hipMemcpyDeviceToDevice, s), "copy gain");
   }
   HIP_TRY(hipMemcpyAsync(d_gains + 2 * L * H, w->g_final, H * 2, hipMemcpyDeviceToDevice, s), "copy gain");
+  if (d.qk_norm)  // per-head q/k gains [L][2][D] after the hidden-size gains
+    for (int l = 0; l < L; ++l) {
+      uint16_t* dst = d_gains + (2 * L + 1) * H + 2 * l * D;
+      HIP_TRY(hipMemcpyAsync(dst, w->layers[l].q_norm, D * 2, hipMemcpyDeviceToDevice, s), "copy q norm gain");
+      HIP_TRY(hipMemcpyAsync(dst + D, w->layers[l].k_norm, D * 2, hipMemcpyDeviceToDevice, s), "copy k norm gain");
+    }
   {  // RoPE: angle p * theta^(-2j/D) in double, cos/sin rounded to float
     std::vector<float2> cs(size_t(S) * (D / 2));
     for (int64_t p = 0; p < S; ++p)
@@ -396,6 +404,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   P.L = d.n_layers; P.H = d.hidden; P.Hq = d.n_q_heads; P.Hkv = d.n_kv_heads; P.D = d.head_dim; P.F = d.ffn;
   P.V = d.vocab; P.G = G; P.B = cache_batch; P.S = d.max_seq; P.Nc = g.opts.attn_chunks; P.n_lm = nlm;
   P.eps = d.rms_eps;
+  P.qk_norm = d.qk_norm;
   P.small_floats = static_cast<int32_t>(small_floats);
   P.big_floats = static_cast<int32_t>(big_floats);
   P.kp_big = kp_big;

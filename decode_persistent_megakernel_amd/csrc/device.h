@@ -85,6 +85,7 @@ struct Params {
   int32_t L, H, Hq, Hkv, D, F, V, G, B, S, Nc, n_lm;
   float eps;
   float attn_scale;
+  int32_t qk_norm;      // per-head q/k RMSNorm before RoPE (gains after the hidden-size ones)
   int32_t kp;           // staged floats per column in the small slots (K rounded up to 256)
   int32_t kp_big;       // staged floats per column in the big slot (FFN rounded up to 256)
   int32_t wave_vrows;   // partial-sum rows per (stream wave, column): the row blocks its piece touches
@@ -97,7 +98,7 @@ struct Params {
   const uint8_t* wpack;
   const uint8_t* zeros;       // [kZeroBlocks][2 KiB] of zeros: the loads that fill a stream block up
   const uint16_t* embed;      // [V][H] bf16 (library copy)
-  const uint16_t* gains;      // [L][2][H] then [H] final, bf16
+  const uint16_t* gains;      // [L][2][H], [H] final, then [L][2][D] q/k head gains, bf16
   uint16_t* kcache;           // [L][B][Hkv][S][D] bf16 (caller-owned)
   uint16_t* vcache;
   const float2* rope_cs;      // [S][D/2] (cos, sin)

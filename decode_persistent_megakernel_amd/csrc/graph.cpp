@@ -58,6 +58,7 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   if (d.head_dim % 8) return fail("head_dim must be a multiple of 8");
   if (d.hidden % 8 || d.ffn % 8) return fail("hidden and ffn must be multiples of 8");
   if (!(d.rms_eps >= 0.f) || !(d.rope_theta > 0.f)) return fail("rms_eps >= 0 and rope_theta > 0 required");
+  if (d.qk_norm != 0 && d.qk_norm != 1) return fail("qk_norm must be 0 or 1");
   mk_graph_opts o{};
   if (in) o = *in;
   if (o.num_cus < 0 || o.qkv_tasks_per_group < 0 || o.o_tasks < 0 || o.gu_tasks < 0 || o.d_tasks < 0 ||
@@ -208,13 +209,14 @@ std::vector<uint8_t> serialize(const Graph& g) {
   Writer w;
   const char magic[8] = {'M', 'K', 'G', 'R', 'A', 'P', 'H', '1'};
   w.b.insert(w.b.end(), magic, magic + 8);
-  w.u32(1);
+  w.u32(2);  // version 2: the desc carries qk_norm
   const mk_model_desc& d = g.desc;
   for (int32_t v : {d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab,
                     d.tied_embeddings, d.max_batch, d.max_seq})
     w.i32(v);
   w.f32(d.rms_eps);
   w.f32(d.rope_theta);
+  w.i32(d.qk_norm);
   const mk_graph_opts& o = g.opts;
   for (int32_t v : {o.num_cus, o.qkv_tasks_per_group, o.o_tasks, o.gu_tasks, o.d_tasks, o.lm_tasks,
                     o.attn_chunks, o.row_block})

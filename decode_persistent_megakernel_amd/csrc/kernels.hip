@@ -594,6 +594,19 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
     }
   }
   stage_copy(cx, P.qkv + ((size_t)T.b * P.Hkv + T.g) * GR, raw, GR);
+  if (P.qk_norm) {
+    // per-head RMSNorm of the G query heads and the key head, each over D with
+    // its [D] gain, before RoPE (the raw q|k rows are contiguous)
+    const uint16_t* gq = P.gains + (size_t)(2 * P.L + 1) * P.H + (size_t)T.layer * 2 * D;
+    for (int h = 0; h <= G; ++h) {
+      float ss = 0.f;
+      for (int d = lane; d < D; d += 64) ss = fmaf(raw[h * D + d], raw[h * D + d], ss);
+      const float f = 1.0f / sqrtf(wave_sum(ss) / (float)D + P.eps);
+      const uint16_t* g = gq + (h < G ? 0 : D);
+      for (int d = lane; d < D; d += 64) raw[h * D + d] = raw[h * D + d] * f * bf2f(g[d]);
+    }
+    wait_lgkm();
+  }
   // whole-wave iterations: the (cos, sin) pair comes from lane jj of pre
   for (int base = 0; base < (G + 1) * Dh; base += 64) {
     const int idx = base + lane;

@@ -113,6 +113,22 @@ __device__ __forceinline__ Piece make_kv_piece(const Params& P, const Ctx& cx, i
   return pc;
 }
 
+// The same piece computed from an attention record and the call's positions,
+// before the task is staged (the staged header gives the same bounds).
+__device__ __forceinline__ Piece kv_piece_of(const Params& P, const Ctx& cx, int s, int r, int step) {
+  const StreamRec R = cx.recs[r];
+  const uint32_t tsbg = rfl(R.tsbg), lc = rfl(R.lc);
+  const int b = (tsbg >> 6) & 1023, g = tsbg >> 16, layer = lc & 0xffff, chunk = lc >> 16;
+  const int pos = b < P.batch ? ld_uniform(P.pos_in, b) + step : -1;
+  int lo = 0, end = 0, j0 = 0, j1 = 0;
+  if (pos >= 0 && pos < P.S) {
+    att_stream_range(chunk, pos, P.Nc, lo, end);
+    const int ppi = 64 / (P.D / 8);
+    piece(end > lo ? (end - lo + ppi - 1) / ppi : 0, s, j0, j1);
+  }
+  return make_kv_piece(P, cx, layer, b < P.batch ? b : 0, g, lo, end, j0, j1 - j0);
+}
+
 // A block: up to RING consecutive items of one piece.
 struct Blk {
   int r, step;  // stream record and step
@@ -444,16 +460,23 @@ __device__ __forceinline__ void mv_item(const Params& P, Comp& C, Acc<NC>& A, co
 
 // An attention task's piece: the chunk's streamed KV blocks of this wave,
 // through a ring of kAttRing register slots (the same unrolled pass as the
-// weight ring: compute the slot's block, then refill the slot).
-constexpr int kAttRing = 4;
-__device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C, AttState& S) {
+// weight ring: compute the slot's block, then refill the slot). The first
+// kAttRing blocks are loaded before the task is staged (att_prefetch): the
+// step is open by then, since this compute unit's previous task was staged.
+constexpr int kAttRing = 8;
+__device__ __forceinline__ void att_prefetch(const Params& P, const Ctx& cx, const Piece& pc, u32x4 (&ka)[kAttRing],
+                                             u32x4 (&kv)[kAttRing]) {
+#pragma unroll
+  for (int j = 0; j < kAttRing; ++j) {
+    load_item(P, cx, pc, j, j < pc.n, ka[j], kv[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+__device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C, AttState& S, const Piece& pc,
+                                        u32x4 (&ka)[kAttRing], u32x4 (&kv)[kAttRing]) {
   const int lane = cx.lane, lpp = P.D / 8, ppi = 64 / lpp;
   const bool l16 = lpp == 16;
-  const Piece pc = make_kv_piece(P, cx, C.layer, C.b, C.g, C.lo, C.end, C.u0, C.natt);
-  u32x4 ka[kAttRing], kv[kAttRing];
-#pragma unroll
-  for (int j = 0; j < kAttRing; ++j) ka[j] = kv[j] = u32x4{0u, 0u, 0u, 0u};
-  int cn = 0, cbase = 0, base = 0;  // blocks computed in this pass (loaded in the last), their first; next to load
+  int cn = min(kAttRing, pc.n), cbase = 0, base = kAttRing;  // blocks computed in this pass, their first; next to load
   for (;;) {
     cn = (int)rfl((uint32_t)cn);
     asm volatile("" : "+s"(cn));  // opaque: no peeled first pass
@@ -544,12 +567,20 @@ __device__ __forceinline__ void run_stream(const Params& P0, const Ctx& cx, int 
         const bool at = r == cur.r && st == cur.step;
         C.r = r;
         C.step = st;
+        // an attention task: its first KV blocks load while it is staged
+        const bool att = !at && (rfl(cx.recs[r].tsbg) & 15) == T_ATT;
+        Piece kpc;
+        u32x4 ka[kAttRing], kv[kAttRing];
+        if (att) {
+          kpc = kv_piece_of(P, cx, s, r, st);
+          att_prefetch(P, cx, kpc, ka, kv);
+        }
         if (!comp_start<NC, PROF>(P, cx, s, C, A, S, wt, prof)) return;
         t_first = 0;
         if (at) break;
-        if (C.type == T_ATT) {
+        if (att) {
           if (prof) t_first = rfl((uint32_t)wall_clock64());
-          att_run(P, cx, C, S);
+          att_run(P, cx, C, S, kpc, ka, kv);
         }
         fin = true;
       }

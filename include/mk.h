@@ -41,11 +41,16 @@ extern "C" {
 /* Model shape (MPK walk-through 3.3.1: hidden size, heads, kv heads, head dim,
  * vocab; max_seq_length in the PersistentKernel constructor). tied_embeddings
  * = 1 uses the embedding as LM head. rms_eps is added inside the square root of
- * RMSNorm; rope_theta is the RoPE base (half-split pairs, no scaling). */
+ * RMSNorm; rope_theta is the RoPE base (half-split pairs, no scaling).
+ * qk_norm = 1: each query and key head vector is RMS-normalised over head_dim
+ * with its layer's [head_dim] gain (q_norm / k_norm weights) after the
+ * projection and before RoPE (MPK walk-through 3.3.1: attention_layer takes
+ * q_norm and k_norm); 0: no such norm (Llama). */
 typedef struct mk_model_desc {
     int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
     int32_t tied_embeddings, max_batch, max_seq;
     float rms_eps, rope_theta;
+    int32_t qk_norm;
 } mk_model_desc;
 
 /* Task-graph knobs (MPK walk-through 3.3.1: per-layer grid sizes and worker
@@ -65,9 +70,11 @@ typedef struct mk_model mk_model;   /* graph + packed weights + device state */
 
 /* Per-layer weights: device pointers to bf16, HF layout [out, in] row-major.
  * wq [Hq*D, H], wk/wv [Hkv*D, H], wo [H, Hq*D], wg/wu [F, H], wd [H, F],
- * g_attn/g_mlp [H] (RMSNorm gains). */
+ * g_attn/g_mlp [H] (RMSNorm gains); q_norm/k_norm [D] (per-head q/k RMSNorm
+ * gains, read only when the desc has qk_norm = 1, else may be NULL). */
 typedef struct mk_layer_weights {
     const void *wq, *wk, *wv, *wo, *wg, *wu, *wd, *g_attn, *g_mlp;
+    const void *q_norm, *k_norm;
 } mk_layer_weights;
 
 /* All model tensors (MPK walk-through 3.3.1: attach_input of every weight and
@@ -89,7 +96,7 @@ typedef struct mk_weights {
  * EventDesc). Host only; touches no device. *out receives a new graph the
  * caller frees with mk_free_graph. opts may be NULL (all defaults).
  * Errors: MK_EINVAL for an inconsistent shape (Hq not a multiple of Hkv, odd
- * head_dim, K dims not multiples of 8, ...), MK_ENOMEM. */
+ * head_dim, K dims not multiples of 8, qk_norm not 0 or 1, ...), MK_ENOMEM. */
 int mk_build_task_graph(const mk_model_desc *desc, const mk_graph_opts *opts, mk_graph **out);
 
 /* Canonical little-endian bytes of the graph (header, tasks, events, queues).
@@ -118,7 +125,8 @@ void mk_free_graph(mk_graph *g);
  * model whose max_batch exceeds batch_per_launch runs, on each group of
  * sequences, the graph these options give for a batch_per_launch-sequence desc
  * (mk_model_info's n_tasks counts that graph's tasks).
- * Errors: MK_EINVAL (NULL pointer), MK_EUNSUPPORTED (fewer resident compute
+ * Errors: MK_EINVAL (NULL pointer, a NULL q_norm/k_norm with qk_norm = 1),
+ * MK_EUNSUPPORTED (fewer resident compute
  * units than num_cus, shape outside this build), MK_ENOMEM, MK_EHIP. */
 int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_model **out);
 

@@ -20,6 +20,11 @@ Where the pages leave a step open, the readings used are:
   from the cache, including the entry just written.
 * Logits stay in full precision; argmax returns the lowest index among ties.
 * SiLU: ``z / (1 + exp(-z))``.
+* Optional per-head q/k RMSNorm (``shape.qk_norm``): the attention layer of the
+  MPK walk-through's demo takes q_norm and k_norm weights (section 3.3.1,
+  ``attention_layer``); each query and key head vector (length D) is RMS
+  normalised with its [D] gain and the same eps, after the projection and
+  before RoPE (the Qwen3 order; the pages name the weights only).
 
 Numbers: float64 throughout; weights are bf16 bit patterns decoded exactly.
 """
@@ -134,6 +139,15 @@ class Model:
             self._cache[name] = m
         return m
 
+    def _qk_norm(self, l: int, q: np.ndarray, k: np.ndarray):
+        """Per-head RMSNorm of query and key head vectors (last axis, D), when
+        the shape has it; identity otherwise."""
+        if not getattr(self.s, "qk_norm", False):
+            return q, k
+        gq = bf16.decode(self.w[f"l{l}.q_norm"])
+        gk = bf16.decode(self.w[f"l{l}.k_norm"])
+        return rmsnorm(q, gq, self.s.rms_eps), rmsnorm(k, gk, self.s.rms_eps)
+
     def embed_row(self, tok: int) -> np.ndarray:
         return bf16.decode(self.w["embed"][int(tok)])
 
@@ -169,6 +183,7 @@ class Model:
             qs = (h @ wq.T).reshape(B, s.n_q_heads, D)
             ks = (h @ wk.T).reshape(B, s.n_kv_heads, D)
             vs = (h @ wv.T).reshape(B, s.n_kv_heads, D)
+            qs, ks = self._qk_norm(l, qs, ks)
             for b in range(B):
                 p = int(pos[b])
                 q = rope(qs[b], p, s.rope_theta)
@@ -208,6 +223,7 @@ class Model:
             q = (h @ self.W(f"l{l}.wq").T).reshape(P, s.n_q_heads, D)
             k = (h @ self.W(f"l{l}.wk").T).reshape(P, s.n_kv_heads, D)
             v = (h @ self.W(f"l{l}.wv").T).reshape(P, s.n_kv_heads, D)
+            q, k = self._qk_norm(l, q, k)
             q = np.stack([rope(q[p], p, s.rope_theta) for p in range(P)])
             k = np.stack([rope(k[p], p, s.rope_theta) for p in range(P)])
             kb = self._store(k).transpose(1, 0, 2)                  # [Hkv, P, D]

@@ -48,7 +48,7 @@ TYPE_NAMES = ["EMB", "QKV", "ATT", "COMB", "O", "GU", "D", "LM", "ARGMAX"]
 GROUP_COLS = 4
 
 MAGIC = b"MKGRAPH1"
-VERSION = 1
+VERSION = 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -65,6 +65,7 @@ class Desc:
     max_seq: int
     rms_eps: float
     rope_theta: float
+    qk_norm: int = 0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -112,7 +113,8 @@ class Graph:
 def desc_from_shape(shape, max_batch: int, max_seq: int) -> Desc:
     return Desc(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads,
                 shape.head_dim, shape.ffn, shape.vocab, int(shape.tied), max_batch,
-                max_seq, float(shape.rms_eps), float(shape.rope_theta))
+                max_seq, float(shape.rms_eps), float(shape.rope_theta),
+                int(getattr(shape, "qk_norm", False)))
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -229,6 +231,7 @@ def serialize(gr: Graph) -> bytes:
     out += struct.pack("<10i", d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim,
                        d.ffn, d.vocab, d.tied, d.max_batch, d.max_seq)
     out += struct.pack("<2f", d.rms_eps, d.rope_theta)
+    out += struct.pack("<i", d.qk_norm)
     out += struct.pack("<8i", o.num_cus, o.qkv_tasks_per_group, o.o_tasks, o.gu_tasks,
                        o.d_tasks, o.lm_tasks, o.attn_chunks, o.row_block)
     out += struct.pack("<2i", len(gr.tasks), len(gr.events))

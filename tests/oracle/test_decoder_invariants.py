@@ -170,3 +170,68 @@ def test_kv_given_reads_the_entries_it_is_given():
     other = m.decode_step(st3, [int(prompt[4])], [4], kv_given=True)
     assert not np.allclose(other, ref)
     assert np.array_equal(st3.kcache, st.kcache)            # nothing written
+
+
+def hf_qwen3(shape, w, tied):
+    """HF Qwen3ForCausalLM in float64 with the workload's weights: the same
+    pre-norm decoder with per-head q/k RMSNorm before RoPE."""
+    from transformers import Qwen3Config, Qwen3ForCausalLM
+    cfg = Qwen3Config(vocab_size=shape.vocab, hidden_size=shape.hidden, intermediate_size=shape.ffn,
+                      num_hidden_layers=shape.n_layers, num_attention_heads=shape.n_q_heads,
+                      num_key_value_heads=shape.n_kv_heads, head_dim=shape.head_dim,
+                      rms_norm_eps=shape.rms_eps, rope_theta=shape.rope_theta, tie_word_embeddings=tied,
+                      attention_bias=False, max_position_embeddings=128, use_sliding_window=False,
+                      attn_implementation="eager")
+    m = Qwen3ForCausalLM(cfg).double().eval()
+    sd = {"model.embed_tokens.weight": w["embed"], "model.norm.weight": w["g_final"]}
+    for l in range(shape.n_layers):
+        p = f"model.layers.{l}."
+        sd.update({p + "self_attn.q_proj.weight": w[f"l{l}.wq"], p + "self_attn.k_proj.weight": w[f"l{l}.wk"],
+                   p + "self_attn.v_proj.weight": w[f"l{l}.wv"], p + "self_attn.o_proj.weight": w[f"l{l}.wo"],
+                   p + "self_attn.q_norm.weight": w[f"l{l}.q_norm"], p + "self_attn.k_norm.weight": w[f"l{l}.k_norm"],
+                   p + "mlp.gate_proj.weight": w[f"l{l}.wg"], p + "mlp.up_proj.weight": w[f"l{l}.wu"],
+                   p + "mlp.down_proj.weight": w[f"l{l}.wd"],
+                   p + "input_layernorm.weight": w[f"l{l}.g_attn"],
+                   p + "post_attention_layernorm.weight": w[f"l{l}.g_mlp"]})
+    sd["lm_head.weight"] = w["embed"] if tied else w["lm_head"]
+    sd = {k: v.double() for k, v in sd.items()}
+    missing, unexpected = m.load_state_dict(sd, strict=False)
+    assert not unexpected and all("rotary" in k for k in missing), (missing, unexpected)
+    return m
+
+
+def test_qk_norm_matches_transformers_qwen3():
+    """The q/k-norm variant (MPK walk-through 3.3.1, attention_layer with
+    q_norm and k_norm) against HF's Qwen3 decoder, which normalises each query
+    and key head over head_dim before RoPE; random gains, so the [D] gains are
+    pinned too. HF computes its norms in float32, hence the 1e-5 tolerance."""
+    wl, w = weights(6, "random")
+    toks = workload.make_prompt(wl)[0]
+    with torch.no_grad():
+        ref = hf_qwen3(wl.shape, w, False)(torch.tensor(toks)[None], use_cache=False).logits[0].numpy()
+    om = Model(wl.shape, {k: to_u16(v) for k, v in w.items()}, cache=True, kv_round=False)
+    full, _, _ = om.forward_full(toks)
+    assert np.max(np.abs(full - ref)) < 1e-5, np.max(np.abs(full - ref))
+    st = om.new_state(1, wl.max_seq)
+    for p, t in enumerate(toks):
+        lg = om.decode_step(st, [t], [p])[0]
+        assert np.max(np.abs(lg - ref[p])) < 1e-5
+
+
+def test_qk_norm_scale_invariance():
+    """Per-head RMSNorm makes attention independent of the scale of W_q and
+    W_k (up to eps): doubling both leaves the logits unchanged to ~1e-4, while
+    the same change without the norm moves them far."""
+    base = {}
+    for cfg in (6, 0):
+        wl, w = weights(cfg, "random")
+        toks = workload.make_prompt(wl)[0]
+        w2 = dict(w)
+        for l in range(wl.shape.n_layers):
+            w2[f"l{l}.wq"] = (w[f"l{l}.wq"].float() * 2).to(torch.bfloat16)
+            w2[f"l{l}.wk"] = (w[f"l{l}.wk"].float() * 2).to(torch.bfloat16)
+        a = Model(wl.shape, {k: to_u16(v) for k, v in w.items()}, cache=True).forward_full(toks)[0]
+        b = Model(wl.shape, {k: to_u16(v) for k, v in w2.items()}, cache=True).forward_full(toks)[0]
+        base[cfg] = np.linalg.norm(a - b) / np.linalg.norm(a)
+    assert base[6] < 1e-3, base
+    assert base[0] > 1e-2, base

@@ -105,3 +105,12 @@ def test_serialize_small_buffer_and_nulls():
     assert L.mk_generate(None, None, None, 1, 1, None, None, None) == mk.MK_EINVAL
     assert L.mk_check(None, None) == mk.MK_EINVAL
     mk.mk_free_graph(g)
+
+
+def test_bad_qk_norm_is_einval():
+    wl = workload.config(0)
+    d = mk.desc_from_shape(wl.shape, 1, 64)
+    d.qk_norm = 2
+    with pytest.raises(mk.MKError) as e:
+        mk.mk_build_task_graph(d)
+    assert e.value.code == mk.MK_EINVAL

@@ -11,8 +11,9 @@ Recipe (stated once, used everywhere):
   tensor's index in :func:`tensor_index` (a fixed enumeration).
 * Weight matrices (HF layout ``[out, in]``): ``standard_normal(float32) * 0.02``
   then rounded to bfloat16 (round to nearest even, done by torch's dtype cast).
-* Norm gains are 1.0 (HF initialisation) unless ``gains="random"``, in which
-  case they are ``1 + 0.1 * standard_normal`` rounded to bfloat16.
+* Norm gains (the per-head q/k norm gains of a qk_norm shape included) are 1.0
+  (HF initialisation) unless ``gains="random"``, in which case they are
+  ``1 + 0.1 * standard_normal`` rounded to bfloat16.
 * Prompt / first tokens: ``integers(0, vocab)``.
 * Prefilled KV (long-context and batch configs): ``standard_normal(float32)``
   rounded to bfloat16, for positions ``< kv_len[b]``; context lengths of the
@@ -47,6 +48,7 @@ class ModelShape:
     tied: bool
     rope_theta: float
     rms_eps: float = 1e-5
+    qk_norm: bool = False     # per-head RMSNorm of queries and keys before RoPE
 
     @property
     def group(self) -> int:
@@ -83,6 +85,9 @@ CONFIGS: List[Workload] = [
     # test-only: the tiny config's size with the 8B shape's head width (128),
     # four query heads per kv head and an untied LM head
     Workload(5, "tiny-2L-h512-d128", _TINY_D128, 1, 64, 8, 16, "none"),
+    # test-only: the tiny config with per-head q/k RMSNorm (the attention of
+    # the MPK walk-through's demo model)
+    Workload(6, "tiny-2L-h256-qknorm", dataclasses.replace(_TINY, qk_norm=True), 1, 64, 8, 16, "none"),
 ]
 
 
@@ -99,6 +104,8 @@ def weight_names(s: ModelShape) -> List[str]:
     names += ["lm_head", "g_final", "prompt", "first_token", "kv_len"]
     names += [f"l{l}.kcache" for l in range(s.n_layers)]
     names += [f"l{l}.vcache" for l in range(s.n_layers)]
+    # appended last so that every earlier tensor keeps its seed index
+    names += [f"l{l}.{n}" for l in range(s.n_layers) for n in ("q_norm", "k_norm")]
     return names
 
 
@@ -120,6 +127,7 @@ def _shape_of(s: ModelShape, name: str):
         "wv": (s.n_kv_heads * D, H), "wo": (H, s.n_q_heads * D),
         "wg": (F, H), "wu": (F, H), "wd": (H, F),
         "g_attn": (H,), "g_mlp": (H,), "g_final": (H,),
+        "q_norm": (D,), "k_norm": (D,),
     }[base]
 
 
@@ -158,6 +166,8 @@ def make_weights(wl: Workload, gains: str = "ones", threads: int = 8) -> Dict[st
         for name, t in zip(jobs, ex.map(lambda n: _draw_bf16(wl, n, 0.02), jobs)):
             out[name] = t
     norms = [f"l{l}.{n}" for l in range(s.n_layers) for n in ("g_attn", "g_mlp")] + ["g_final"]
+    if s.qk_norm:
+        norms += [f"l{l}.{n}" for l in range(s.n_layers) for n in ("q_norm", "k_norm")]
     for name in norms:
         if gains == "random":
             out[name] = _draw_bf16(wl, name, 0.1, 1.0)
