@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "mk_load_weights": [vp, ctypes.POINTER(Weights), vp, ctypes.POINTER(vp)],
         "mk_decode_step": [vp, vp, vp, i32, vp, vp, i32, vp],
         "mk_generate": [vp, vp, vp, i32, i32, vp, vp, vp],
+        "mk_generate_noalloc": [vp, vp, vp, i32, i32, vp, vp, vp],
         "mk_check": [vp, vp],
         "mk_set_watchdog_ms": [vp, i32],
         "mk_debug_drop_signal": [vp, i32],
@@ -187,6 +188,12 @@ def mk_generate(model: int, tokens0, pos0, batch: int, n_steps: int, out_tokens,
                 stream=None) -> None:
     _ok(lib().mk_generate(model, _ptr(tokens0), _ptr(pos0), batch, n_steps, _ptr(out_tokens),
                           _ptr(last_logits), _stream(stream)))
+
+
+def mk_generate_noalloc(model: int, tokens0, pos0, batch: int, n_steps: int, out_tokens, last_logits=None,
+                        stream=None) -> None:
+    _ok(lib().mk_generate_noalloc(model, _ptr(tokens0), _ptr(pos0), batch, n_steps, _ptr(out_tokens),
+                                  _ptr(last_logits), _stream(stream)))
 
 
 def mk_check(model: int, stream=None) -> None:

@@ -39,6 +39,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static_assert(mk::kMaxCols == mk::kGroupCols, "the graph's group size is the launch's column capacity");
 
+// The launch scratch of a model, in the order mk_generate_noalloc lays it out:
+// the event counters and the abort flag first (cleared at every call), then
+// the activations, attention partials, LM partials and the token buffer.
+enum { kWsCounters, kWsAbort, kWsX, kWsQkv, kWsPartMl, kWsPartAcc, kWsAttn, kWsMlp, kWsLmVal, kWsLmIdx, kWsTok, kWsN };
+
 struct mk_model {
   mk::Graph g;
   int device = 0;
@@ -55,6 +60,9 @@ struct mk_model {
   size_t profile_bytes = 0;
   uint64_t* waits = nullptr;
   mk::Params base{};                      // everything but the per-call fields
+  // 4-byte words of the buffers one launch uses as scratch, in the order of
+  // kWs* below (what mk_generate_noalloc lays out in its static workspace)
+  size_t ws_words[kWsN] = {};
   std::vector<void*> allocs;              // device buffers owned by the model
 
   ~mk_model() {
@@ -136,6 +144,8 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   m->max_batch = cache_batch;
   const Graph& g = m->g;
   HIP_TRY(hipGetDevice(&m->device), "hipGetDevice");
+  // set-up of mk_generate_noalloc's static workspace on this device (once per device)
+  HIP_TRY(noalloc_scratch_init(m->device), "hipGetSymbolAddress(static workspace)");
   hipDeviceProp_t prop;
   HIP_TRY(hipGetDeviceProperties(&prop, m->device), "hipGetDeviceProperties");
 
@@ -387,6 +397,13 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
       (rc = m->alloc(&d_tok, B + 64, "tokens")) ||
       (rc = m->alloc(&d_status, 1, "status")) || (rc = m->alloc(&d_abort, 1, "abort flag")))
     return rc;
+  {
+    const size_t w[kWsN] = {g.events.size() * kEventWords, 1, size_t(B * H + slack),
+                            size_t(B * Hkv * (G + 2) * D + slack), size_t(B * Hq * Nc * 2 + slack),
+                            size_t(B * Hq * Nc * D + slack), size_t(B * Hq * D + slack), size_t(B * F + slack),
+                            size_t(B * nlm + slack), size_t(B * nlm + slack), size_t(B + 64)};
+    std::copy(w, w + kWsN, m->ws_words);
+  }
   HIP_TRY(hipMemset(d_status, 0, 4), "clear status");
   HIP_TRY(hipMemset(d_abort, 0, 4), "clear abort flag");
   HIP_TRY(hipMemset(d_tok, 0, B * 4), "clear tokens");
@@ -543,6 +560,51 @@ int mk_generate(mk_model* m, const int32_t* d_tokens0, const int32_t* d_pos0, in
   if (n_steps < 1) return fail(MK_EINVAL, "mk_generate: n_steps must be >= 1");
   return run_megakernel(m, d_tokens0, d_pos0, batch, n_steps, d_out_tokens, d_last_logits,
                         static_cast<hipStream_t>(stream));
+}
+
+int mk_generate_noalloc(mk_model* m, const int32_t* d_tokens0, const int32_t* d_pos0, int32_t batch,
+                        int32_t n_steps, int32_t* d_out_tokens, float* d_last_logits, void* stream) {
+  int rc = check_call(m, d_tokens0, d_pos0, batch, d_out_tokens);
+  if (rc) return rc;
+  if (n_steps < 1) return fail(MK_EINVAL, "mk_generate_noalloc: n_steps must be >= 1");
+  if ((uint64_t(n_steps) + 1) * m->max_threshold >= (1ull << 31))
+    return fail(MK_EINVAL, "mk_generate_noalloc: n_steps too large for the event counters");
+  uint8_t* base = static_cast<uint8_t*>(mk::noalloc_scratch(m->device));
+  if (!base) return fail(MK_EHIP, "mk_generate_noalloc: the static workspace was not resolved on this device");
+  size_t off[kWsN], total = 0;
+  for (int i = 0; i < kWsN; ++i) {
+    off[i] = total;
+    total += (m->ws_words[i] * 4 + 255) / 256 * 256;
+  }
+  if (total > MK_NOALLOC_SCRATCH_BYTES)
+    return fail(MK_EINVAL, "mk_generate_noalloc: one launch of this model needs " + std::to_string(total) +
+                               " bytes of scratch; the static workspace holds " +
+                               std::to_string(size_t(MK_NOALLOC_SCRATCH_BYTES)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t b0 = 0; b0 < batch; b0 += m->ncap) {
+    // counters and abort flag sit at the front: every launch starts them at 0
+    HIP_TRY(mk::launch_fill_zero(reinterpret_cast<uint32_t*>(base), off[kWsX] / 4, s), "hipLaunchKernel(mk_fill_zero)");
+    mk::Params P = group_params(m, d_tokens0, d_pos0, batch, b0, std::min(m->ncap, batch - b0), n_steps,
+                                d_out_tokens, d_last_logits);
+    P.counters = reinterpret_cast<uint32_t*>(base + off[kWsCounters]);
+    P.abort_flag = reinterpret_cast<int32_t*>(base + off[kWsAbort]);
+    P.x = reinterpret_cast<float*>(base + off[kWsX]);
+    P.qkv = reinterpret_cast<float*>(base + off[kWsQkv]);
+    P.part_ml = reinterpret_cast<float*>(base + off[kWsPartMl]);
+    P.part_acc = reinterpret_cast<float*>(base + off[kWsPartAcc]);
+    P.attn = reinterpret_cast<float*>(base + off[kWsAttn]);
+    P.mlp = reinterpret_cast<float*>(base + off[kWsMlp]);
+    P.lm_val = reinterpret_cast<float*>(base + off[kWsLmVal]);
+    P.lm_idx = reinterpret_cast<int32_t*>(base + off[kWsLmIdx]);
+    P.tok_cur = reinterpret_cast<int32_t*>(base + off[kWsTok]);
+    P.epoch0 = 0;
+    P.use_events = 1;
+    P.drop_task = m->drop_task;
+    P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * mk::kProfWords * 8) ? m->profile : nullptr;
+    P.waits = m->waits;
+    HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
+  }
+  return MK_OK;
 }
 
 int mk_check(mk_model* m, void* stream) {

@@ -31,8 +31,12 @@
 // the pages compare against). mk_pack repacks the weights into units.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
+#include "mk.h"
 #include "device.h"
 #include "graph.h"
 #include "launch.h"
@@ -1245,6 +1249,58 @@ hipError_t launch_pack(const PackJob* jobs, int n_jobs, const PackSrc* src, uint
                        hipStream_t s) {
   hipLaunchKernelGGL(mk_pack, dim3(n_jobs), dim3(256), 0, s, jobs, src, dst, G, D, L);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// static workspace of the no-allocation entry point
+// ---------------------------------------------------------------------------
+
+// Zero-fill used to clear the static workspace's counters at every call (a
+// kernel rather than a memset, so that a caller may capture the call).
+__global__ void mk_fill_zero(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t s) {
+  if (words == 0) return hipSuccess;
+  if (words > 0xffffffffu) return hipErrorInvalidValue;
+  const size_t blocks = std::min<size_t>((words + 255) / 256, 1024);
+  hipLaunchKernelGGL(mk_fill_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
+                     static_cast<uint32_t>(words));
+  return hipGetLastError();
+}
+
+}  // namespace mk
+
+// The array itself. In host code its name is only a stand-in for the device
+// symbol; its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[MK_NOALLOC_SCRATCH_BYTES];
+
+namespace mk {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch_init(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev].load(std::memory_order_acquire)) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != dev) return hipErrorInvalidDevice;  // the device must be current
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_scratch[dev].store(ptr, std::memory_order_release);
+  return hipSuccess;
+}
+
+void* noalloc_scratch(int dev) {
+  return dev >= 0 && dev < kMaxDevices ? g_scratch[dev].load(std::memory_order_acquire) : nullptr;
 }
 
 }  // namespace mk

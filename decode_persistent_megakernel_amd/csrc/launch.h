@@ -11,6 +11,12 @@ hipError_t set_lds_limit(int bytes);
 hipError_t persistent_occupancy(int lds, int* blocks_per_cu);
 hipError_t launch_persistent(const Params& P, int grid, int lds, hipStream_t s);
 hipError_t launch_op(const Params& P, int first, int count, int lds, hipStream_t s);
+// Static workspace of mk_generate_noalloc: resolve the device address of the
+// array on `dev` (which must be current) once; later calls return at once.
+hipError_t noalloc_scratch_init(int dev);
+// The address resolved for `dev`, or nullptr before noalloc_scratch_init.
+void* noalloc_scratch(int dev);
+hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t s);
 hipError_t launch_pack(const PackJob* jobs, int n_jobs, const PackSrc* src, uint8_t* dst, int G, int D, int L,
                        hipStream_t s);
 

@@ -6,7 +6,7 @@ from __future__ import annotations
 from typing import Dict, Optional
 
 from . import (GraphOpts, MK_MODE_MEGAKERNEL, desc_from_shape, mk_build_task_graph, mk_check,
-               mk_decode_step, mk_free_graph, mk_free_model, mk_generate, mk_graph_info,
+               mk_decode_step, mk_free_graph, mk_free_model, mk_generate, mk_generate_noalloc, mk_graph_info,
                mk_graph_serialize, mk_load_weights, mk_model_info)
 
 
@@ -64,11 +64,14 @@ class Session:
         mk_decode_step(self.model, self.tok, self.pos, b, self.logits if logits else None, self.next, mode)
         return self.next[:b], self.logits[:b]
 
-    def generate(self, tokens0, pos0, n_steps: int, out=None, last_logits: bool = False):
+    def generate(self, tokens0, pos0, n_steps: int, out=None, last_logits: bool = False, noalloc: bool = False):
+        """n_steps greedy steps in one launch; ``noalloc`` calls the entry point
+        whose launch scratch is the library's static workspace."""
         b = self.set_inputs(tokens0, pos0)
         if out is None:
             out = self.torch.zeros((n_steps, b), dtype=self.torch.int32, device=self.tok.device)
-        mk_generate(self.model, self.tok, self.pos, b, n_steps, out, self.logits if last_logits else None)
+        fn = mk_generate_noalloc if noalloc else mk_generate
+        fn(self.model, self.tok, self.pos, b, n_steps, out, self.logits if last_logits else None)
         return out
 
     def check(self):

@@ -35,6 +35,8 @@ extern "C" {
 #define MK_EDEVICE      (-6)   /* device-side argument error (token or position out of range) */
 
 /* decode modes for mk_decode_step */
+#define MK_NOALLOC_SCRATCH_BYTES (16u << 20) /* static workspace of mk_generate_noalloc, per GPU */
+
 #define MK_MODE_MEGAKERNEL 0   /* one persistent launch runs the whole step */
 #define MK_MODE_OPLAUNCH   1   /* one launch per operator, same task bodies (baseline) */
 
@@ -156,6 +158,28 @@ int mk_decode_step(mk_model *m, const int32_t *d_tokens, const int32_t *d_pos, i
  * mk_decode_step. */
 int mk_generate(mk_model *m, const int32_t *d_tokens0, const int32_t *d_pos0, int32_t batch,
                 int32_t n_steps, int32_t *d_out_tokens, float *d_last_logits, void *stream);
+
+/* mk_generate for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, outputs and errors as mk_generate, and the same kernels, so the
+ * same tokens, logits and KV-cache entries bit for bit. The launch's scratch
+ * (event counters, abort flag, activations, attention and LM partials, token
+ * buffer) lives in one static device array of MK_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * per GPU, which that GPU holds until the process ends, instead of in the
+ * model's own workspace; this call allocates and frees nothing and records no
+ * memset (a fill kernel clears the counters at the start of every launch). The
+ * array's address on a device is resolved once, by the first mk_load_weights
+ * on that device. Every call on one GPU shares the array and finds it as the
+ * last call left it: calls that overlap on one GPU (other streams, other
+ * threads) race; order them on one stream. The model's status word still
+ * reports device errors (mk_check). Errors: as mk_generate; MK_EINVAL also
+ * when one launch of this model needs more scratch than the array holds (the
+ * message gives both sizes; the Llama-3.2-1B and Llama-3-8B shapes need about
+ * 2.7 and 5.3 MiB at one sequence per launch, 12.1 MiB at four) or
+ * n_steps is too large for the event counters; MK_EHIP if the array's address
+ * was not resolved on the current device. */
+int mk_generate_noalloc(mk_model *m, const int32_t *d_tokens0, const int32_t *d_pos0, int32_t batch,
+                        int32_t n_steps, int32_t *d_out_tokens, float *d_last_logits, void *stream);
 
 /* Synchronise `stream`, then read and clear the model's device status word.
  * Returns MK_OK, MK_EDEVICE (token or position out of range was seen; the

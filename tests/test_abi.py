@@ -103,6 +103,7 @@ def test_serialize_small_buffer_and_nulls():
     assert L.mk_load_weights(g, None, None, ctypes.byref(m)) == mk.MK_EINVAL
     assert L.mk_decode_step(None, None, None, 1, None, None, 0, None) == mk.MK_EINVAL
     assert L.mk_generate(None, None, None, 1, 1, None, None, None) == mk.MK_EINVAL
+    assert L.mk_generate_noalloc(None, None, None, 1, 1, None, None, None) == mk.MK_EINVAL
     assert L.mk_check(None, None) == mk.MK_EINVAL
     mk.mk_free_graph(g)
 
