@@ -46,7 +46,7 @@ class ModelDesc(ctypes.Structure):
 class GraphOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_cus", "qkv_tasks_per_group", "o_tasks", "gu_tasks", "d_tasks", "lm_tasks",
-        "attn_chunks", "row_block")]
+        "attn_chunks", "row_block", "use_mfma")]
 
 
 class LayerWeights(ctypes.Structure):

@@ -38,17 +38,20 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 static_assert(mk::kMaxCols == mk::kGroupCols, "the graph's group size is the launch's column capacity");
+static_assert(mk::kMfmaCols == 16, "the matrix-core bodies' M dimension");
 
 // The launch scratch of a model, in the order mk_generate_noalloc lays it out:
 // the event counters and the abort flag first (cleared at every call), then
 // the activations, attention partials, LM partials and the token buffer.
-enum { kWsCounters, kWsAbort, kWsX, kWsQkv, kWsPartMl, kWsPartAcc, kWsAttn, kWsMlp, kWsLmVal, kWsLmIdx, kWsTok, kWsN };
+enum { kWsCounters, kWsAbort, kWsX, kWsQkv, kWsPartMl, kWsPartAcc, kWsAttn, kWsMlp, kWsLmVal, kWsLmIdx, kWsTok, kWsSsq,
+       kWsN };
 
 struct mk_model {
   mk::Graph g;
   int device = 0;
   int lds_bytes = 0;
   int ncap = 1;       // sequences one launch stages (a call with more runs them in groups)
+  bool mfma = false;  // matrix-core bodies (graph option use_mfma = 2)
   int max_batch = 1;  // sequences the KV caches hold
   uint64_t packed_bytes = 0;
   uint32_t epoch = 0;
@@ -152,9 +155,19 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   // --- task descriptors and packed-weight offsets ---------------------------
   // column blocks per row block, rounded up to even (zero weights pad K): a
   // streamed item is two units of one row block
-  const int kb_h = static_cast<int>(cdiv(d.hidden, 2 * kUnitCols) * 2);
-  const int kb_qd = static_cast<int>(cdiv(int64_t(d.n_q_heads) * d.head_dim, 2 * kUnitCols) * 2);
-  const int kb_f = static_cast<int>(cdiv(d.ffn, 2 * kUnitCols) * 2);
+  const bool mf = g.opts.use_mfma == 2;
+  m->mfma = mf;
+  if (mf && (d.hidden % kMfmaItemCols || (int64_t(d.n_q_heads) * d.head_dim) % kMfmaItemCols || d.ffn % kMfmaItemCols ||
+             std::min({d.hidden, d.n_q_heads * d.head_dim, d.ffn}) < 4 * kMfmaItemCols))
+    return fail(MK_EUNSUPPORTED,
+                "mk_load_weights: the matrix-core bodies need hidden, q width and ffn multiples of 64, at least 256");
+  // vector bodies: 128-column blocks, rounded up to an even count; matrix-core
+  // bodies: 32-column blocks (K is a multiple of 64)
+  const int kb_h = mf ? d.hidden / 32 : static_cast<int>(cdiv(d.hidden, 2 * kUnitCols) * 2);
+  const int kb_qd = mf ? d.n_q_heads * d.head_dim / 32
+                       : static_cast<int>(cdiv(int64_t(d.n_q_heads) * d.head_dim, 2 * kUnitCols) * 2);
+  const int kb_f = mf ? d.ffn / 32 : static_cast<int>(cdiv(d.ffn, 2 * kUnitCols) * 2);
+  int wave_tiles = 1;
   std::vector<DevTask> dt(g.tasks.size());
   std::vector<PackJob> jobs;
   uint64_t off = 0;
@@ -175,7 +188,8 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     }
     if (KB == 0) continue;
     const int nrb = static_cast<int>(cdiv(t.row1 - t.row0, kUnitRows));
-    const int n_vrb = t.type == T_GU ? 2 * nrb : nrb;
+    const int n_vrb = mf ? static_cast<int>(cdiv(t.row1 - t.row0, t.type == T_GU ? kMfmaRows / 2 : kMfmaRows))
+                         : t.type == T_GU ? 2 * nrb : nrb;
     x.n_units = n_vrb * KB;
     x.kb = KB;
     x.kdim = K;
@@ -186,7 +200,10 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
       const int items = x.n_units / 2;
       for (int w = 0; w < kStreams; ++w) {
         const int i0 = int(int64_t(items) * w / kStreams), i1 = int(int64_t(items) * (w + 1) / kStreams);
-        if (i1 > i0) wave_vrows = std::max(wave_vrows, ((2 * i1 - 1) / KB - (2 * i0) / KB + 1) * kUnitRows);
+        if (i1 <= i0) continue;
+        const int touched = (2 * i1 - 1) / KB - (2 * i0) / KB + 1;
+        wave_vrows = std::max(wave_vrows, touched * kUnitRows);
+        wave_tiles = std::max(wave_tiles, touched);
       }
     }
     jobs.push_back(PackJob{x.w_off, t.type, t.layer, t.g, t.row0, t.row1, K, KB, n_vrb});
@@ -233,7 +250,10 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   if (G > kMaxG) return fail(MK_EUNSUPPORTED, "mk_load_weights: more than 4 query heads per kv head");
   if (D != 64 && D != 128) return fail(MK_EUNSUPPORTED, "mk_load_weights: head_dim must be 64 or 128");
   if (d.hidden > 4096) return fail(MK_EUNSUPPORTED, "mk_load_weights: hidden above 4096");
-  if (std::max({kb_h, kb_qd, kb_f}) > 254) return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32512");
+  if (!mf && std::max({kb_h, kb_qd, kb_f}) > 254)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 32512");
+  if (mf && std::max({kb_h, kb_qd, kb_f}) > 65535)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: a K dimension above 2^21");
   if (int64_t(g.opts.attn_chunks) * (int64_t(d.max_seq) + 1) >= (int64_t(1) << 32))
     return fail(MK_EUNSUPPORTED, "mk_load_weights: attn_chunks * (max_seq + 1) must stay below 2^32");
   if (d.hidden % 4 || (d.n_q_heads * d.head_dim) % 4 || d.ffn % 4)
@@ -248,7 +268,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   // The sequences one launch stages (ncap): as many as fit the LDS; a call
   // with more sequences runs them in groups of ncap (sequences are
   // independent).
-  int ncap = std::min<int>(d.max_batch, kMaxCols);
+  int ncap = std::min<int>(d.max_batch, mf ? kMfmaCols : kMaxCols);
   const int kp = static_cast<int>(r256(std::max(d.hidden, d.n_q_heads * D)));
   const int kp_big = static_cast<int>(r256(d.ffn));
   int nlm_tasks = 0;
@@ -259,7 +279,11 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   int64_t small_floats = 0, big_floats = 0, part_floats = 0;
   size_t fixed = 0;
   for (; ncap >= 1; --ncap) {
-    const int64_t need_mv = int64_t(ncap) * kp + int64_t(ncap) * res_stride;
+    // matrix-core bodies: the gains of a normalised input (bf16) or the
+    // residual rows of all kMfmaCols sequences; vector bodies: the staged
+    // inputs and residual rows of ncap sequences
+    const int64_t need_mv = mf ? std::max(r256(d.hidden / 2), int64_t(kMfmaCols) * res_stride)
+                               : int64_t(ncap) * kp + int64_t(ncap) * res_stride;
     // attention: raw q|k|v, rotated q, new k and v, their bf16 bits, k and v of
     // position p - 1, the scaled rotated q, then the stream waves' partials (acc[wave][head][D],
     // then (m, l) per wave and head)
@@ -267,17 +291,20 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
                              int64_t(kStreams) * G * (D + 2);
     const int64_t need_arg = r256(nlm_tasks) * 2;
     const int64_t need_emb = r256(d.hidden / 2 + 1);
-    const int64_t need_mv_big = int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
+    const int64_t need_mv_big = mf ? int64_t(kMfmaCols) * res_stride : int64_t(ncap) * kp_big + int64_t(ncap) * res_stride;
     const int64_t need_comb = r256(int64_t(G) * Ncx * 2) + r256(int64_t(G) * Ncx * D);
     small_floats = (32 + std::max({need_mv, need_att, need_arg, need_emb}) + 3) & ~int64_t(3);
     // the merge slot follows the two small ones; the down-projection input
     // overlays all three, so the merge slot holds what it needs beyond them
     big_floats = (std::max(32 + need_comb, 32 + need_mv_big - 2 * small_floats) + 3) & ~int64_t(3);
-    part_floats = (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
+    part_floats = mf ? int64_t(kStreams) * wave_tiles * 256 : (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
     fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
             size_t(srec_max) * sizeof(StreamRec);
-    if (fixed <= lds_max) break;
+    if (fixed <= lds_max || mf) break;  // (the matrix-core bodies stage no per-sequence inputs)
   }
+  if (mf && fixed > lds_max)
+    return fail(MK_EUNSUPPORTED, "mk_load_weights: the matrix-core bodies need " + std::to_string(fixed) +
+                                     " bytes of LDS, more than the 160 KiB a workgroup has");
   if (ncap < 1)
     return fail(MK_EUNSUPPORTED, "mk_load_weights: staging one sequence needs " + std::to_string(fixed) +
                                      " bytes of LDS, more than the 160 KiB a workgroup has");
@@ -333,7 +360,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   uint16_t *d_embed, *d_gains;
   float2* d_rope;
   if ((rc = m->alloc(&d_wpack, m->packed_bytes, "packed weights")) || (rc = m->alloc(&d_embed, V * H + 512, "embedding")) ||
-      (rc = m->alloc(&d_gains, (2 * L + 1) * H + 2 * L * D, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")) ||
+      (rc = m->alloc(&d_gains, (2 * L + 1) * H + 2 * L * D + 512, "norm gains")) || (rc = m->alloc(&d_rope, S * (D / 2), "rope table")) ||
       (rc = m->alloc(&d_zeros, size_t(kZeroBlocks) * 2 * kUnitBytes, "zero blocks")))
     return rc;
   HIP_TRY(hipMemset(d_zeros, 0, size_t(kZeroBlocks) * 2 * kUnitBytes), "clear zero blocks");
@@ -378,30 +405,37 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     d_srcs = static_cast<PackSrc*>(ps);
     e = hipMemcpy(d_jobs, jobs.data(), jobs.size() * sizeof(PackJob), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(d_srcs, srcs.data(), srcs.size() * sizeof(PackSrc), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = launch_pack(d_jobs, static_cast<int>(jobs.size()), d_srcs, d_wpack, G, d.head_dim, d.n_layers, s);
+    if (e == hipSuccess)
+      e = launch_pack(d_jobs, static_cast<int>(jobs.size()), d_srcs, d_wpack, G, d.head_dim, d.n_layers, mf, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     (void)hipFree(pj);
     (void)hipFree(ps);
     if (e != hipSuccess) return hip_fail(e, "weight packing");
   }
 
-  float *d_x, *d_qkv, *d_pml, *d_pacc, *d_attn, *d_mlp, *d_lmv;
+  float *d_x, *d_qkv, *d_pml, *d_pacc, *d_attn, *d_mlp, *d_lmv, *d_ssq;
   int32_t *d_lmi, *d_tok, *d_status, *d_abort;
   const int64_t Nc = g.opts.attn_chunks;
+  int n_ss_o = 0, n_ss_d = 0;  // tasks of the O and D projections (each writes one sum-of-squares part)
+  for (const Task& t : g.tasks) {
+    if (t.type == T_O && t.layer == 0) ++n_ss_o;
+    if (t.type == T_D && t.layer == 0) ++n_ss_d;
+  }
+  const int64_t ssq_floats = mf ? int64_t(std::max({n_ss_o, n_ss_d, 1})) * kMfmaCols + 256 : 1;
   const int64_t slack = 4096;  // floats read past the end by 1 KiB-granular copies
   if ((rc = m->alloc(&d_x, B * H + slack, "x")) || (rc = m->alloc(&d_qkv, B * Hkv * (G + 2) * D + slack, "qkv")) ||
       (rc = m->alloc(&d_pml, B * Hq * Nc * 2 + slack, "attention partials")) ||
       (rc = m->alloc(&d_pacc, B * Hq * Nc * D + slack, "attention partials")) ||
       (rc = m->alloc(&d_attn, B * Hq * D + slack, "attn")) || (rc = m->alloc(&d_mlp, B * F + slack, "mlp")) ||
       (rc = m->alloc(&d_lmv, B * nlm + slack, "lm partials")) || (rc = m->alloc(&d_lmi, B * nlm + slack, "lm partials")) ||
-      (rc = m->alloc(&d_tok, B + 64, "tokens")) ||
+      (rc = m->alloc(&d_tok, B + 64, "tokens")) || (rc = m->alloc(&d_ssq, ssq_floats, "sums of squares")) ||
       (rc = m->alloc(&d_status, 1, "status")) || (rc = m->alloc(&d_abort, 1, "abort flag")))
     return rc;
   {
     const size_t w[kWsN] = {g.events.size() * kEventWords, 1, size_t(B * H + slack),
                             size_t(B * Hkv * (G + 2) * D + slack), size_t(B * Hq * Nc * 2 + slack),
                             size_t(B * Hq * Nc * D + slack), size_t(B * Hq * D + slack), size_t(B * F + slack),
-                            size_t(B * nlm + slack), size_t(B * nlm + slack), size_t(B + 64)};
+                            size_t(B * nlm + slack), size_t(B * nlm + slack), size_t(B + 64), size_t(ssq_floats)};
     std::copy(w, w + kWsN, m->ws_words);
   }
   HIP_TRY(hipMemset(d_status, 0, 4), "clear status");
@@ -429,6 +463,9 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   P.attn_scale = static_cast<float>(1.0 / std::sqrt(double(d.head_dim)));
   P.kp = kp;
   P.wave_vrows = wave_vrows;
+  P.wave_tiles = wave_tiles;
+  P.n_ss_o = n_ss_o;
+  P.n_ss_d = n_ss_d;
   P.res_stride = res_stride;
   P.ncap = ncap;
   P.wpack = d_wpack;
@@ -440,6 +477,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   P.rope_cs = d_rope;
   P.x = d_x; P.qkv = d_qkv; P.part_ml = d_pml; P.part_acc = d_pacc; P.attn = d_attn; P.mlp = d_mlp;
   P.lm_val = d_lmv; P.lm_idx = d_lmi; P.tok_cur = d_tok; P.status = d_status; P.abort_flag = d_abort;
+  P.ssq = d_ssq;
   *out = m;
   m = nullptr;  // ownership passes to the caller
   return MK_OK;
@@ -453,7 +491,7 @@ int mk_load_weights(const mk_graph* gr, const mk_weights* w, void* stream, mk_mo
   // LDS stages fewer). A model whose batch exceeds its group runs, on every
   // group, the graph of a desc with the group's size and the same options, so
   // that a launch holds no tasks of sequences outside its group.
-  int32_t group = std::min<int32_t>(d.max_batch, mk::kGroupCols);
+  int32_t group = std::min<int32_t>(d.max_batch, gr->g.opts.use_mfma == 2 ? mk::kMfmaCols : mk::kGroupCols);
   mk_graph_opts opts = gr->g.opts;
   for (;;) {
     mk::Graph g1;
@@ -529,7 +567,8 @@ static int run_megakernel(mk_model* m, const int32_t* tok, const int32_t* pos, i
     P.drop_task = m->drop_task;
     P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * mk::kProfWords * 8) ? m->profile : nullptr;
     P.waits = m->waits;
-    HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
+    HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, m->mfma, s),
+            "hipLaunchCooperativeKernel(mk_persistent)");
     m->epoch += static_cast<uint32_t>(n_steps);
   }
   return MK_OK;
@@ -548,7 +587,7 @@ int mk_decode_step(mk_model* m, const int32_t* d_tokens, const int32_t* d_pos, i
     P.use_events = 0;
     P.drop_task = -1;
     for (const auto& op : m->g.ops)
-      HIP_TRY(mk::launch_op(P, op.first, op.second - op.first, m->lds_bytes, s), "hipLaunchKernel(mk_oplaunch)");
+      HIP_TRY(mk::launch_op(P, op.first, op.second - op.first, m->lds_bytes, m->mfma, s), "hipLaunchKernel(mk_oplaunch)");
   }
   return MK_OK;
 }
@@ -597,12 +636,14 @@ int mk_generate_noalloc(mk_model* m, const int32_t* d_tokens0, const int32_t* d_
     P.lm_val = reinterpret_cast<float*>(base + off[kWsLmVal]);
     P.lm_idx = reinterpret_cast<int32_t*>(base + off[kWsLmIdx]);
     P.tok_cur = reinterpret_cast<int32_t*>(base + off[kWsTok]);
+    P.ssq = reinterpret_cast<float*>(base + off[kWsSsq]);
     P.epoch0 = 0;
     P.use_events = 1;
     P.drop_task = m->drop_task;
     P.profile = (m->profile && m->profile_bytes >= size_t(n_steps) * m->g.tasks.size() * mk::kProfWords * 8) ? m->profile : nullptr;
     P.waits = m->waits;
-    HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, s), "hipLaunchCooperativeKernel(mk_persistent)");
+    HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, m->mfma, s),
+            "hipLaunchCooperativeKernel(mk_persistent)");
   }
   return MK_OK;
 }

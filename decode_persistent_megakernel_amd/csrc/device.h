@@ -18,6 +18,17 @@ constexpr int kUnitBytes = 1024;
 constexpr int kUnitCols = 128;
 constexpr int kUnitRows = 4;
 
+// The matrix-core bodies (launches of up to kMfmaCols sequences) stream the
+// same 1 KiB units in another arrangement: a unit covers 16 rows and 32
+// consecutive columns, lane 16*j + i holding columns [8j, 8j+8) of row i, which
+// is the B operand of one v_mfma_f32_16x16x32_bf16 (the 16 rows are its N
+// dimension, the sequences its M dimension). A row block is 16 rows (gate/up:
+// 8 gate rows then the 8 up rows of the same outputs); an item is the units of
+// column blocks 2j and 2j+1 of one row block; a task's items are stored in
+// (row block, column pair) order.
+constexpr int kMfmaRows = 16;
+constexpr int kMfmaItemCols = 64;
+
 // Workgroup layout: wave 0 stages task inputs (and polls events), wave 1
 // retires tasks (epilogue, stores, signals); then kStreams stream waves, each
 // loading its piece of every streamed task into a ring of registers and
@@ -30,7 +41,8 @@ constexpr int kThreads = 64 * (kCtlWaves + kStreams);
 #endif
 constexpr int kRing = MK_RING;  // 2 KiB items each stream wave keeps in flight (in registers)
 constexpr int kZeroBlocks = 256;  // 2 KiB zero blocks, one per compute unit (index taken modulo)
-constexpr int kMaxCols = 4;    // sequences a matvec task handles
+constexpr int kMaxCols = 4;    // sequences a matvec task handles (vector bodies; the
+                               // matrix-core bodies handle kMfmaCols, graph.h)
 constexpr int kMaxBatch = 256; // sequences a model holds (larger calls run in groups of at most kMaxCols)
 constexpr int kMaxG = 4;       // query heads per kv head
 constexpr int kStripes = 64;   // event counter stripes: one per lane of the polling wave
@@ -94,6 +106,8 @@ struct Params {
   int32_t small_floats; // LDS staging slot size (two small slots)
   int32_t big_floats;   // LDS staging slot size for down-projection and merge tasks
   int32_t part_floats;  // LDS partial-sum area per slot
+  int32_t wave_tiles;   // matrix-core bodies: 16x16 partial tiles per stream wave (row blocks its piece touches)
+  int32_t n_ss_o, n_ss_d;  // matrix-core bodies: sum-of-squares partials the O and D projections write
   // model data
   const uint8_t* wpack;
   const uint8_t* zeros;       // [kZeroBlocks][2 KiB] of zeros: the loads that fill a stream block up
@@ -109,6 +123,8 @@ struct Params {
   float* part_acc;            // [B][Hq][Nc][D]
   float* attn;                // [B][Hq*D]
   float* mlp;                 // [B][F]
+  float* ssq;                 // matrix-core bodies: [task][16] sums of squares of the rows of x a
+                              // projection task (or the embedding, at index 0) wrote
   float* lm_val;              // [B][n_lm]
   int32_t* lm_idx;            // [B][n_lm]
   int32_t* tok_cur;           // [B]
@@ -137,6 +153,7 @@ struct PackJob {
   int64_t dst_off;
   int32_t type, layer, g, row0, row1, K, KB, n_vrb;
 };
+// (the matrix-core arrangement: KB units of 32 columns per row block, n_vrb row blocks)
 
 // Source matrices per layer: wq wk wv wo wg wu wd; entry [L].p[0] is the LM head.
 struct PackSrc {

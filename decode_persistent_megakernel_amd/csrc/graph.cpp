@@ -64,6 +64,7 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   if (o.num_cus < 0 || o.qkv_tasks_per_group < 0 || o.o_tasks < 0 || o.gu_tasks < 0 || o.d_tasks < 0 ||
       o.lm_tasks < 0 || o.attn_chunks < 0 || o.row_block < 0)
     return fail("mk_graph_opts: negative option");
+  if (o.use_mfma > 2) return fail("mk_graph_opts: use_mfma must be 0, 1 or 2");
 
   const int32_t N = o.num_cus ? o.num_cus : 256;
   const int32_t rb = o.row_block ? o.row_block : 4;
@@ -84,6 +85,11 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
                       ? o.attn_chunks
                       : std::max(1, std::min(N / (std::min(B, kGroupCols) * Hkv), std::max(1, d.max_seq / 1024)));
   const int32_t Nc = r.attn_chunks;
+  {  // the matrix-core bodies take K dimensions that are multiples of 64, at least 256
+    auto mf_ok = [](int64_t k) { return k % 64 == 0 && k >= 256; };
+    const bool shape_ok = mf_ok(d.hidden) && mf_ok(int64_t(d.n_q_heads) * d.head_dim) && mf_ok(d.ffn);
+    r.use_mfma = o.use_mfma ? o.use_mfma : (std::min(B, kMfmaCols) > kGroupCols && shape_ok ? 2 : 1);
+  }
 
   Graph& g = *out;
   g = Graph{};
@@ -209,7 +215,7 @@ std::vector<uint8_t> serialize(const Graph& g) {
   Writer w;
   const char magic[8] = {'M', 'K', 'G', 'R', 'A', 'P', 'H', '1'};
   w.b.insert(w.b.end(), magic, magic + 8);
-  w.u32(2);  // version 2: the desc carries qk_norm
+  w.u32(3);  // version 3: the desc carries qk_norm, the options use_mfma
   const mk_model_desc& d = g.desc;
   for (int32_t v : {d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab,
                     d.tied_embeddings, d.max_batch, d.max_seq})
@@ -219,7 +225,7 @@ std::vector<uint8_t> serialize(const Graph& g) {
   w.i32(d.qk_norm);
   const mk_graph_opts& o = g.opts;
   for (int32_t v : {o.num_cus, o.qkv_tasks_per_group, o.o_tasks, o.gu_tasks, o.d_tasks, o.lm_tasks,
-                    o.attn_chunks, o.row_block})
+                    o.attn_chunks, o.row_block, o.use_mfma})
     w.i32(v);
   w.i32(static_cast<int32_t>(g.tasks.size()));
   w.i32(static_cast<int32_t>(g.events.size()));

@@ -58,6 +58,10 @@ constexpr int kProfCtl = kCtlWords + kWaves * kWaitWords;
 // then, per slot and stream wave, the row blocks its piece of the task touched
 constexpr int kPieceCtl = kProfCtl + 3 * kStreams * 4;
 static_assert((kPieceCtl + 3 * kStreams * 2) * 4 <= kCtlBytes, "control area");
+// then eight bf16 ones (16 bytes): the gains of inputs that are not normalised
+// (matrix-core bodies)
+constexpr int kOnesCtl = 240;
+static_assert(kOnesCtl >= kPieceCtl + 3 * kStreams * 2 && (kOnesCtl + 4) * 4 <= kCtlBytes, "control area");
 // slot header fields (as int)
 enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11 };
 
@@ -526,6 +530,72 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
   }
 }
 
+// Matrix-core bodies (up to 16 sequences): the stream waves read the
+// activations straight from global memory, so staging a matvec task leaves
+// in the slot only what every wave shares: for an RMS-normalised input, the
+// per-sequence factor 1/rms (header words 0..15, from the sums of squares the
+// producing tasks wrote) and the gains [K] as bf16 after the header; for the
+// O and down projections, the residual rows [16][res_stride].
+__device__ __forceinline__ void stage_matvec_m16(const Params& P, const Ctx& cx, const DevTask& T, int slot) {
+  float* hdr = slot_ptr(cx, slot);
+  float* data = hdr + kHdr;
+  const int lane = cx.lane;
+  if (is_normed(T.type)) {
+    // sums of squares: part t, sequences 4q..4q+3 in lane 4t' + q (fixed order:
+    // each lane adds its parts in turn, then the lanes of one q are added in a
+    // fixed butterfly)
+    const int nparts = T.type == T_GU ? P.n_ss_o : (T.type == T_QKV && T.layer == 0 ? 1 : P.n_ss_d);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const rsrc_t r = make_rsrc(P.ssq, (uint32_t)nparts * kMfmaCols * 4);
+    for (int t0 = 0; t0 < nparts; t0 += 256) {
+      u32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((t0 + 16 * i + (lane >> 2)) * kMfmaCols + (lane & 3) * 4) * 4u,
+                                                    0, kAuxCoherent);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc.x += __uint_as_float(v[i].x); acc.y += __uint_as_float(v[i].y);
+        acc.z += __uint_as_float(v[i].z); acc.w += __uint_as_float(v[i].w);
+      }
+    }
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) {
+      acc.x += __shfl_xor(acc.x, o); acc.y += __shfl_xor(acc.y, o);
+      acc.z += __shfl_xor(acc.z, o); acc.w += __shfl_xor(acc.w, o);
+    }
+    if (lane < 4) {
+      const float inv_k = 1.0f / (float)T.kdim;
+      hdr[lane * 4 + 0] = 1.0f / sqrtf(acc.x * inv_k + P.eps);
+      hdr[lane * 4 + 1] = 1.0f / sqrtf(acc.y * inv_k + P.eps);
+      hdr[lane * 4 + 2] = 1.0f / sqrtf(acc.z * inv_k + P.eps);
+      hdr[lane * 4 + 3] = 1.0f / sqrtf(acc.w * inv_k + P.eps);
+    }
+    const uint16_t* gain = P.gains + (T.type == T_LM ? (size_t)P.L * 2 * P.H
+                                                     : ((size_t)T.layer * 2 + (T.type == T_GU)) * P.H);
+    const int nl = (T.kdim * 2 + 1023) / 1024;  // 1 KiB pieces (the gains buffer has slack)
+    for (int t = 0; t < nl; ++t) dma16<0>(gain + t * 512 + lane * 8, data + t * 256);
+    wait_all();
+  } else {  // O, D: the residual rows of the call's sequences (eight loads in flight per lane)
+    const int R = T.row1 - T.row0, total = P.batch * R;
+    const rsrc_t rx = make_rsrc(P.x, (uint32_t)P.batch * (uint32_t)P.H * 4u);
+    for (int q0 = 0; q0 < total; q0 += 512) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = q0 + 64 * i + lane, m = q / R, r = q - m * R;
+        const uint32_t off = q < total ? (uint32_t)(m * P.H + T.row0 + r) * 4u : 0xfffffff0u;  // out of range: 0
+        v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, kAuxCoherent));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = q0 + 64 * i + lane, m = q / R, r = q - m * R;
+        if (q < total) data[(size_t)m * P.res_stride + r] = v[i];
+      }
+    }
+  }
+}
+
 // Attention slot layout after the header: raw q|k|v of the kv group (rounded
 // up to 256 floats), rotated queries [G][D], new key [D] and value [D] as
 // bf16-rounded floats, their bf16 bits [2D], the key [D] and value [D] of
@@ -677,7 +747,10 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
                  P.n_lm);
       break;
     }
-    default: stage_matvec<NC>(P, cx, T, slot, pre); break;
+    default:
+      if constexpr (NC == kMfmaCols) stage_matvec_m16(P, cx, T, slot);
+      else stage_matvec<NC>(P, cx, T, slot, pre);
+      break;
   }
 }
 
@@ -702,7 +775,7 @@ __device__ __forceinline__ void run_stager(const Params& P0, const Ctx& cx) {
       waits_add(wt, 0, s0);
       if (slot == 0) last0 = i; else if (slot == 1) last1 = i; else if (slot == 2) last2 = i; else last3 = i;
       StagePre pre;
-      if (T.type == T_QKV || T.type == T_O || T.type == T_GU || T.type == T_D || T.type == T_LM)
+      if (NC <= kMaxCols && (T.type == T_QKV || T.type == T_O || T.type == T_GU || T.type == T_D || T.type == T_LM))
         stage_matvec_pre(P, cx, T, slot, pre);
       else if (T.type == T_ATT)
         stage_att_pre(P, cx, T, step, pre);
@@ -800,6 +873,104 @@ __device__ __forceinline__ void retire_matvec(const Params& P, const Ctx& cx, co
       const float* rs = res + (size_t)c * P.res_stride;
       for (int r = lane; r < R; r += 64) st_coh(dst + r, rs[r] + part_sum(P, pr, part, c, r));
     }
+  }
+}
+
+// Matrix-core bodies: per row block, the stream waves' 16 x 16 partial tiles
+// ([row][sequence]) added in wave order, then the RMS factor of each sequence
+// (normalised inputs) and the epilogue. Lane l handles tile row l >> 2 and
+// sequences 4 (l & 3) .. +3 (gate/up: output l >> 3, sequences 2 (l & 7), +1).
+__device__ __forceinline__ void retire_matvec_m16(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step) {
+  const float* hdr = slot_ptr(cx, slot);
+  const float* res = hdr + kHdr;
+  const float* part = part_ptr(cx, slot);
+  const int lane = cx.lane, R = T.row1 - T.row0;
+  const PieceRows pr = piece_rows(cx, slot);
+  const int ts = P.wave_tiles * 256;
+  const bool normed = is_normed(T.type);
+  if (T.type == T_GU) {
+    const int j = lane >> 3, p2 = (lane & 7) * 2, nrb = (R + 7) / 8;
+    const float f0 = hdr[p2], f1 = hdr[p2 + 1];
+    for (int rb = 0; rb < nrb; ++rb) {
+      float2 g = make_float2(0.f, 0.f), u = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < kStreams; ++w)
+        if (rb >= pr.a[w] && rb <= pr.b[w]) {
+          const float* t = part + w * ts + (rb - pr.a[w]) * 256;
+          const float2 a = *reinterpret_cast<const float2*>(t + j * 16 + p2);
+          const float2 b = *reinterpret_cast<const float2*>(t + (j + 8) * 16 + p2);
+          g.x += a.x; g.y += a.y; u.x += b.x; u.y += b.y;
+        }
+      const int o = rb * 8 + j;
+      if (o < R) {
+        const float gx = g.x * f0, gy = g.y * f1;
+        if (p2 < P.batch) st_coh(P.mlp + (size_t)p2 * P.F + T.row0 + o, gx / (1.0f + expf(-gx)) * (u.x * f0));
+        if (p2 + 1 < P.batch) st_coh(P.mlp + (size_t)(p2 + 1) * P.F + T.row0 + o, gy / (1.0f + expf(-gy)) * (u.y * f1));
+      }
+    }
+    return;
+  }
+  const int n = lane >> 2, q4 = (lane & 3) * 4, nrb = (R + kMfmaRows - 1) / kMfmaRows;
+  float fac[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) fac[e] = normed ? hdr[q4 + e] : 1.0f;
+  const bool last = step == P.n_steps - 1;
+  float best[4], ssum[4];
+  int bi[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { best[e] = -INFINITY; bi[e] = 0x7fffffff; ssum[e] = 0.f; }
+  for (int rb = 0; rb < nrb; ++rb) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kStreams; ++w)
+      if (rb >= pr.a[w] && rb <= pr.b[w]) {
+        const float4 t = *reinterpret_cast<const float4*>(part + w * ts + (rb - pr.a[w]) * 256 + n * 16 + q4);
+        v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
+      }
+    const int r = rb * kMfmaRows + n;
+    if (r >= R) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = q4 + e;
+      if (m >= P.batch) continue;
+      const float y = v[e] * fac[e];
+      if (T.type == T_LM) {
+        if (last && P.logits_out) P.logits_out[(size_t)m * P.V + T.row0 + r] = y;
+        if (y > best[e] || (y == best[e] && T.row0 + r < bi[e])) { best[e] = y; bi[e] = T.row0 + r; }
+      } else if (T.type == T_QKV) {
+        st_coh(P.qkv + ((size_t)m * P.Hkv + T.g) * (P.G + 2) * P.D + T.row0 + r, y);
+      } else {  // O, D: residual add; the sum of squares of the new rows for the next RMSNorm
+        const float xn = res[(size_t)m * P.res_stride + r] + y;
+        st_coh(P.x + (size_t)m * P.H + T.row0 + r, xn);
+        ssum[e] = fmaf(xn, xn, ssum[e]);
+      }
+    }
+  }
+  if (T.type == T_LM) {
+    // the 16 lanes of one sequence quad (equal lane & 3): best value, then the smallest row
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ov = __shfl_xor(best[e], o);
+        const int oi = __shfl_xor(bi[e], o);
+        if (ov > best[e] || (ov == best[e] && oi < bi[e])) { best[e] = ov; bi[e] = oi; }
+      }
+    if (lane < 4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (q4 + e < P.batch) {
+          st_coh(P.lm_val + (size_t)(q4 + e) * P.n_lm + T.ordinal, best[e]);
+          st_coh(P.lm_idx + (size_t)(q4 + e) * P.n_lm + T.ordinal, bi[e]);
+        }
+  } else if (T.type == T_O || T.type == T_D) {
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssum[e] += __shfl_xor(ssum[e], o);
+    if (lane < 4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st_coh(P.ssq + (size_t)T.ordinal * kMfmaCols + q4 + e, ssum[e]);
   }
 }
 
@@ -915,11 +1086,22 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
       if (T.b >= P.batch) break;
       const uint32_t* row = reinterpret_cast<const uint32_t*>(data);  // bf16 pairs
       const rsrc_t r = make_rsrc(P.x + (size_t)T.b * P.H, (uint32_t)P.H * 4);
+      float ss = 0.f;
       for (int k4 = lane * 4; k4 < P.H; k4 += 256) {
         const uint32_t a = row[k4 / 2], b = row[k4 / 2 + 1];
         u32x4 v;
         v.x = a << 16; v.y = a & 0xffff0000u; v.z = b << 16; v.w = b & 0xffff0000u;
         __builtin_amdgcn_raw_buffer_store_b128(v, r, k4 * 4, 0, kAuxCoherent);
+        if constexpr (NC == kMfmaCols) {
+          ss = fmaf(__uint_as_float(v.x), __uint_as_float(v.x), ss);
+          ss = fmaf(__uint_as_float(v.y), __uint_as_float(v.y), ss);
+          ss = fmaf(__uint_as_float(v.z), __uint_as_float(v.z), ss);
+          ss = fmaf(__uint_as_float(v.w), __uint_as_float(v.w), ss);
+        }
+      }
+      if constexpr (NC == kMfmaCols) {  // the sum of squares the first layer's RMSNorm reads
+        ss = wave_sum(ss);
+        if (lane == 0) st_coh(P.ssq + T.b, ss);
       }
       break;
     }
@@ -1006,7 +1188,10 @@ __device__ __forceinline__ void retire_task(const Params& P, const Ctx& cx, cons
       }
       break;
     }
-    default: retire_matvec<NC>(P, cx, T, slot, step); break;
+    default:
+      if constexpr (NC == kMfmaCols) retire_matvec_m16(P, cx, T, slot, step);
+      else retire_matvec<NC>(P, cx, T, slot, step);
+      break;
   }
 }
 
@@ -1058,6 +1243,7 @@ __device__ __forceinline__ void run_retirer(const Params& P0, const Ctx& cx) {
 }
 
 #include "pipeline.h"
+#include "mfma.h"
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -1084,7 +1270,8 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   }
   cx.lane = threadIdx.x & 63;
   cx.recs = reinterpret_cast<StreamRec*>(cx.parts + 3 * P.part_floats);
-  for (int j = threadIdx.x; j < kCtlBytes / 4; j += blockDim.x) cx.ctl[j] = 0;
+  for (int j = threadIdx.x; j < kCtlBytes / 4; j += blockDim.x)
+    cx.ctl[j] = j >= kOnesCtl && j < kOnesCtl + 4 ? 0x3F803F80 : 0;  // bf16 ones for the unnormalised inputs
   if (single < 0) {
     const int r0 = ld_uniform(P.srec_ptr, cu), r1 = ld_uniform(P.srec_ptr, cu + 1);
     cx.nrec = r1 - r0;
@@ -1113,6 +1300,7 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) run_stager<NC, PROF>(P, cx);
   else if (wave == 1) run_retirer<NC, PROF>(P, cx);
+  else if constexpr (NC == kMfmaCols) run_stream_m16<MK_RING_M, MK_XRING_M, PROF>(P, cx, wave - kCtlWaves);
   else run_stream<kRing, NC, PROF>(P, cx, wave - kCtlWaves);
 }
 
@@ -1136,6 +1324,7 @@ MK_KERNELS(1)
 MK_KERNELS(2)
 MK_KERNELS(3)
 MK_KERNELS(4)
+MK_KERNELS(16)
 #undef MK_KERNELS
 
 typedef void (*PersistentFn)(Params);
@@ -1146,6 +1335,10 @@ static const PersistentFn kPersistent[kMaxCols] = {mk_persistent_b1, mk_persiste
 static const PersistentFn kPersistentProf[kMaxCols] = {mk_persistent_prof_b1, mk_persistent_prof_b2,
                                                        mk_persistent_prof_b3, mk_persistent_prof_b4};
 static const OpFn kOplaunch[kMaxCols] = {mk_oplaunch_b1, mk_oplaunch_b2, mk_oplaunch_b3, mk_oplaunch_b4};
+// the matrix-core bodies: one variant for every launch of up to kMfmaCols sequences
+static_assert(kMfmaCols == 16, "kernel names");
+static const PersistentFn kPersistentM = mk_persistent_b16, kPersistentProfM = mk_persistent_prof_b16;
+static const OpFn kOplaunchM = mk_oplaunch_b16;
 
 // ---------------------------------------------------------------------------
 // weight packing
@@ -1198,29 +1391,75 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack(const PackJob* jobs, c
   }
 }
 
+// The matrix-core arrangement (device.h): unit u = (row block rb, column block
+// kb) of 16 rows x 32 columns, lane 16 * j + i holding columns [8j, 8j + 8) of
+// row i; gate/up row blocks hold 8 gate rows and then the up rows of the same
+// 8 outputs. Rows past the task's end and columns past K are zeros.
+__device__ __forceinline__ const uint16_t* pack_row(const PackJob& J, const PackSrc* src, int G, int D, int L, int r,
+                                                    int64_t& row) {
+  const int ar = J.row0 + r;
+  switch (J.type) {
+    case T_QKV:
+      if (ar < G * D) { row = (int64_t)J.g * G * D + ar; return src[J.layer].p[0]; }
+      if (ar < (G + 1) * D) { row = (int64_t)J.g * D + ar - G * D; return src[J.layer].p[1]; }
+      row = (int64_t)J.g * D + ar - (G + 1) * D;
+      return src[J.layer].p[2];
+    case T_O: row = ar; return src[J.layer].p[3];
+    case T_D: row = ar; return src[J.layer].p[6];
+    default: row = ar; return src[L].p[0];  // T_LM
+  }
+}
+
+extern "C" __global__ void __launch_bounds__(256) mk_pack_m16(const PackJob* jobs, const PackSrc* src, uint8_t* dst,
+                                                             int G, int D, int L) {
+  const PackJob J = jobs[blockIdx.x];
+  const int64_t lanes = (int64_t)J.n_vrb * J.KB * 64;
+  const int R = J.row1 - J.row0;
+  for (int64_t idx = threadIdx.x; idx < lanes; idx += blockDim.x) {
+    const int64_t u = idx >> 6;
+    const int lane = (int)(idx & 63);
+    const int rb = (int)(u / J.KB), kb = (int)(u - (int64_t)rb * J.KB);
+    const int i = lane & 15, col = kb * 32 + (lane >> 4) * 8;
+    int r;
+    int64_t row = 0;
+    const uint16_t* m;
+    if (J.type == T_GU) {
+      r = rb * 8 + (i & 7);
+      m = src[J.layer].p[i < 8 ? 4 : 5];
+      row = J.row0 + r;
+    } else {
+      r = rb * kMfmaRows + i;
+      m = pack_row(J, src, G, D, L, r, row);
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && col < J.K) v = *reinterpret_cast<const u32x4*>(m + row * J.K + col);
+    *reinterpret_cast<u32x4*>(dst + J.dst_off + u * kUnitBytes + lane * 16) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers (called from api.cpp)
 // ---------------------------------------------------------------------------
 
 hipError_t set_lds_limit(int bytes) {
-  for (int c = 0; c < kMaxCols; ++c) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistent[c]),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kPersistentProf[c]),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kOplaunch[c]), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              bytes);
-    if (e != hipSuccess) return e;
+  for (int c = 0; c <= kMaxCols; ++c) {
+    const void* fns[3] = {
+        reinterpret_cast<const void*>(c < kMaxCols ? kPersistent[c] : kPersistentM),
+        reinterpret_cast<const void*>(c < kMaxCols ? kPersistentProf[c] : kPersistentProfM),
+        reinterpret_cast<const void*>(c < kMaxCols ? kOplaunch[c] : kOplaunchM)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
 
 hipError_t persistent_occupancy(int lds, int* blocks_per_cu) {
   int worst = 1 << 30;
-  for (int c = 0; c < kMaxCols; ++c)
-    for (const PersistentFn f : {kPersistent[c], kPersistentProf[c]}) {
+  for (int c = 0; c <= kMaxCols; ++c)
+    for (const PersistentFn f : {c < kMaxCols ? kPersistent[c] : kPersistentM,
+                                 c < kMaxCols ? kPersistentProf[c] : kPersistentProfM}) {
       int n = 0;
       hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(f), kThreads, lds);
       if (e != hipSuccess) return e;
@@ -1231,23 +1470,26 @@ hipError_t persistent_occupancy(int lds, int* blocks_per_cu) {
 }
 
 // The variant for the call: staged columns = the call's batch.
-hipError_t launch_persistent(const Params& P, int grid, int lds, hipStream_t s) {
-  if (P.batch < 1 || P.batch > kMaxCols) return hipErrorInvalidValue;
+hipError_t launch_persistent(const Params& P, int grid, int lds, bool mfma, hipStream_t s) {
+  if (P.batch < 1 || P.batch > (mfma ? kMfmaCols : kMaxCols)) return hipErrorInvalidValue;
   Params p = P;
   void* args[] = {&p};
-  const PersistentFn f = (P.profile || P.waits) ? kPersistentProf[P.batch - 1] : kPersistent[P.batch - 1];
+  const bool prof = P.profile || P.waits;
+  const PersistentFn f = mfma ? (prof ? kPersistentProfM : kPersistentM)
+                              : (prof ? kPersistentProf[P.batch - 1] : kPersistent[P.batch - 1]);
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(f), dim3(grid), dim3(kThreads), args, lds, s);
 }
 
-hipError_t launch_op(const Params& P, int first, int count, int lds, hipStream_t s) {
-  if (P.batch < 1 || P.batch > kMaxCols) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kOplaunch[P.batch - 1], dim3(count), dim3(kThreads), lds, s, P, first);
+hipError_t launch_op(const Params& P, int first, int count, int lds, bool mfma, hipStream_t s) {
+  if (P.batch < 1 || P.batch > (mfma ? kMfmaCols : kMaxCols)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma ? kOplaunchM : kOplaunch[P.batch - 1], dim3(count), dim3(kThreads), lds, s, P, first);
   return hipGetLastError();
 }
 
 hipError_t launch_pack(const PackJob* jobs, int n_jobs, const PackSrc* src, uint8_t* dst, int G, int D, int L,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(mk_pack, dim3(n_jobs), dim3(256), 0, s, jobs, src, dst, G, D, L);
+                       bool mfma, hipStream_t s) {
+  if (mfma) hipLaunchKernelGGL(mk_pack_m16, dim3(n_jobs), dim3(256), 0, s, jobs, src, dst, G, D, L);
+  else hipLaunchKernelGGL(mk_pack, dim3(n_jobs), dim3(256), 0, s, jobs, src, dst, G, D, L);
   return hipGetLastError();
 }
 

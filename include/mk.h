@@ -65,6 +65,11 @@ typedef struct mk_graph_opts {
     int32_t o_tasks, gu_tasks, d_tasks, lm_tasks;
     int32_t attn_chunks;         /* attention position chunks per (kv group, sequence) */
     int32_t row_block;           /* rows per matvec block (task row ranges are whole blocks) */
+    int32_t use_mfma;            /* matvec bodies: 1 vector ALU (at most 4 sequences per launch),
+                                    2 matrix cores (v_mfma, at most 16 sequences per launch; hidden,
+                                    Hq*head_dim and ffn multiples of 64, at least 256);
+                                    0 = 2 when a launch would hold more than 4 sequences and the
+                                    shape allows it, else 1 */
 } mk_graph_opts;
 
 typedef struct mk_graph mk_graph;   /* host-only task graph */

@@ -46,9 +46,10 @@ EMB, QKV, ATT, COMB, OPROJ, GU, DOWN, LM, ARGMAX = range(9)
 TYPE_NAMES = ["EMB", "QKV", "ATT", "COMB", "O", "GU", "D", "LM", "ARGMAX"]
 # most sequences one launch decodes (the graph spec's group size)
 GROUP_COLS = 4
+MFMA_COLS = 16
 
 MAGIC = b"MKGRAPH1"
-VERSION = 2
+VERSION = 3
 
 
 @dataclasses.dataclass(frozen=True)
@@ -78,6 +79,7 @@ class Opts:
     lm_tasks: int = 0
     attn_chunks: int = 0
     row_block: int = 0
+    use_mfma: int = 0
 
 
 @dataclasses.dataclass
@@ -121,6 +123,10 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
+def _mfma_shape(d: Desc) -> bool:
+    return all(k % 64 == 0 and k >= 256 for k in (d.hidden, d.n_q_heads * d.head_dim, d.ffn))
+
+
 def resolve(d: Desc, o: Opts) -> Opts:
     """Fill every zero option with its default (a pure function of the shape)."""
     n = o.num_cus or 256
@@ -144,6 +150,10 @@ def resolve(d: Desc, o: Opts) -> Opts:
         lm_tasks=cap(o.lm_tasks or n, d.vocab),
         attn_chunks=chunks,
         row_block=rb,
+        # matvec bodies (1 vector ALU, 2 matrix cores): the matrix cores when a
+        # launch would hold more sequences than the vector bodies stage and
+        # every K dimension is a multiple of 64, at least 256
+        use_mfma=o.use_mfma or (2 if min(d.max_batch, MFMA_COLS) > GROUP_COLS and _mfma_shape(d) else 1),
     )
 
 
@@ -232,8 +242,8 @@ def serialize(gr: Graph) -> bytes:
                        d.ffn, d.vocab, d.tied, d.max_batch, d.max_seq)
     out += struct.pack("<2f", d.rms_eps, d.rope_theta)
     out += struct.pack("<i", d.qk_norm)
-    out += struct.pack("<8i", o.num_cus, o.qkv_tasks_per_group, o.o_tasks, o.gu_tasks,
-                       o.d_tasks, o.lm_tasks, o.attn_chunks, o.row_block)
+    out += struct.pack("<9i", o.num_cus, o.qkv_tasks_per_group, o.o_tasks, o.gu_tasks,
+                       o.d_tasks, o.lm_tasks, o.attn_chunks, o.row_block, o.use_mfma)
     out += struct.pack("<2i", len(gr.tasks), len(gr.events))
     for t in gr.tasks:
         out += struct.pack("<10i", t.type, t.layer, t.b, t.g, t.chunk, t.row0, t.row1,

@@ -51,8 +51,9 @@ def test_graph_bytes_equal_oracle_knob_sweep():
         s = shapes[it % 3]
         B = int(rng.choice([1, 2, 3, 16]))
         S = int(rng.integers(1, 5000))
-        knobs = [int(rng.choice([0, int(rng.integers(1, 400))])) for _ in range(8)]
+        knobs = [int(rng.choice([0, int(rng.integers(1, 400))])) for _ in range(9)]
         knobs[7] = int(rng.choice([0, 1, 4, 16, 7]))
+        knobs[8] = int(rng.choice([0, 1, 2]))
         o = mk.GraphOpts(*knobs)
         b = c_bytes(mk.desc_from_shape(s, B, S), o)
         ref = G.serialize(G.build(G.desc_from_shape(s, B, S), G.Opts(*knobs)))
@@ -65,10 +66,19 @@ def test_resolved_opts_match_oracle():
     nt, ne, o = mk.mk_graph_info(g)
     mk.mk_free_graph(g)
     r = G.resolve(G.desc_from_shape(wl.shape, 1, wl.max_seq), G.Opts())
-    assert (o.num_cus, o.qkv_tasks_per_group, o.o_tasks, o.gu_tasks, o.d_tasks, o.lm_tasks,
-            o.attn_chunks, o.row_block) == tuple(getattr(r, f) for f in
-                                                 ("num_cus", "qkv_tasks_per_group", "o_tasks", "gu_tasks",
-                                                  "d_tasks", "lm_tasks", "attn_chunks", "row_block"))
+    fields = ("num_cus", "qkv_tasks_per_group", "o_tasks", "gu_tasks", "d_tasks", "lm_tasks",
+              "attn_chunks", "row_block", "use_mfma")
+    assert tuple(getattr(o, f) for f in fields) == tuple(getattr(r, f) for f in fields)
+    assert r.use_mfma == 1                       # one sequence: the vector bodies
+
+
+def test_use_mfma_default_and_range():
+    wl = workload.config(4)                      # 16 sequences: the matrix-core bodies
+    g = mk.mk_build_task_graph(mk.desc_from_shape(wl.shape, wl.batch, 256))
+    assert mk.mk_graph_info(g)[2].use_mfma == 2
+    mk.mk_free_graph(g)
+    with pytest.raises(mk.MKError):
+        mk.mk_build_task_graph(mk.desc_from_shape(wl.shape, 1, 64), mk.GraphOpts(*([0] * 8 + [3])))
 
 
 @pytest.mark.parametrize("field,val", [("n_q_heads", 5), ("head_dim", 60), ("hidden", 0), ("ffn", 690),

@@ -88,6 +88,10 @@ CONFIGS: List[Workload] = [
     # test-only: the tiny config with per-head q/k RMSNorm (the attention of
     # the MPK walk-through's demo model)
     Workload(6, "tiny-2L-h256-qknorm", dataclasses.replace(_TINY, qk_norm=True), 1, 64, 8, 16, "none"),
+    # test-only: the tiny config with an FFN width the matrix-core bodies take
+    # (a multiple of 64), sixteen sequences: the batched (C4-like) path at a
+    # size the oracle runs in seconds
+    Workload(7, "tiny-2L-h256-f768-batch16", dataclasses.replace(_TINY, ffn=768), 16, 64, 8, 16, "none"),
 ]
 
 
