@@ -22,12 +22,16 @@ struct Builder {
     g->events.push_back(Event{threshold, -1, 0});
     return static_cast<int32_t>(g->events.size()) - 1;
   }
-  // Appends one operator's tasks, placing its i-th task on unit i mod N.
-  void add_op(std::vector<Task>&& op) {
-    const int32_t n = g->opts.num_cus;
+  // Appends one operator's tasks, placing its i-th task on unit
+  // (i + floor(i / N) * skew) mod N: round-robin, each further round over the
+  // N units starting `skew` units on. The attention operator passes its chunk
+  // count, so that a unit's chunks come from different sequences (whose
+  // lengths, and so chunk costs, differ) instead of all from one.
+  void add_op(std::vector<Task>&& op, int32_t skew = 0) {
+    const int64_t n = g->opts.num_cus;
     const int32_t begin = static_cast<int32_t>(g->tasks.size());
     for (size_t i = 0; i < op.size(); ++i) {
-      op[i].cu = static_cast<int32_t>(i % n);
+      op[i].cu = static_cast<int32_t>((int64_t(i) + int64_t(i) / n * skew) % n);
       g->tasks.push_back(op[i]);
     }
     g->ops.emplace_back(begin, static_cast<int32_t>(g->tasks.size()));
@@ -146,7 +150,7 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
             t.dep = e_qkv[size_t(l) * Hkv + gi]; t.trig = e_att[(size_t(l) * Hkv + gi) * B + b];
             op.push_back(t);
           }
-      bld.add_op(std::move(op));
+      bld.add_op(std::move(op), Nc);
     }
     {
       std::vector<Task> op;
@@ -215,7 +219,7 @@ std::vector<uint8_t> serialize(const Graph& g) {
   Writer w;
   const char magic[8] = {'M', 'K', 'G', 'R', 'A', 'P', 'H', '1'};
   w.b.insert(w.b.end(), magic, magic + 8);
-  w.u32(3);  // version 3: the desc carries qk_norm, the options use_mfma
+  w.u32(4);  // version 4: qk_norm in the desc, use_mfma in the options, skewed attention placement
   const mk_model_desc& d = g.desc;
   for (int32_t v : {d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab,
                     d.tied_embeddings, d.max_batch, d.max_seq})

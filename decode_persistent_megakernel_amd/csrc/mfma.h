@@ -224,10 +224,10 @@ __device__ __forceinline__ void att_run_m(const Params& P, const Ctx& cx, CompM&
 }
 
 #ifndef MK_RING_M
-#define MK_RING_M 8
+#define MK_RING_M 6
 #endif
 #ifndef MK_XRING_M
-#define MK_XRING_M 4
+#define MK_XRING_M 6
 #endif
 template <int RING, int XR, bool PROF>
 __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, int s) {
@@ -313,12 +313,13 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
     if (cur.flags & kEnd) break;
     {
       // the task's activations exist now: its first XR items' (column pairs
-      // col0, col0 + 1, ... modulo KB2; XR <= KB2 since K >= 256)
+      // col0, col0 + 1, ... modulo KB2)
       const Params& P = fresh_params();
+      int xc = C.xp.col0;
 #pragma unroll
       for (int j = 0; j < XR; ++j) {
-        const int c = C.xp.col0 + j;
-        load_x(P, cx, C.xp, c >= C.xp.KB2 ? c - C.xp.KB2 : c, j < C.xp.n, xa[j]);
+        load_x(P, cx, C.xp, xc, j < C.xp.n, xa[j]);
+        xc = xc + 1 == C.xp.KB2 ? 0 : xc + 1;
       }
       wait_all();
     }

@@ -11,7 +11,10 @@ and Figure 2; "MPK runtime" section and Figure 3):
   reaches the event's threshold (the number of tasks that trigger it) the event
   is active and every task depending on it may start;
 * tasks are spread over the compute units round-robin (MPK summary: simple
-  round-robin placement).
+  round-robin placement); the attention operator's further rounds over the
+  units are skewed by its chunk count, so that one unit's chunks come from
+  different sequences (a step beyond plain round-robin, which the MPK blog
+  translation's closing paragraph and the MPK summary list as future work).
 
 The operator order of one step is the pages' wiring (MPK walk-through section
 3.3.1): embed, then per layer [RMSNorm+QKV, attention, O-proj+residual,
@@ -49,7 +52,7 @@ GROUP_COLS = 4
 MFMA_COLS = 16
 
 MAGIC = b"MKGRAPH1"
-VERSION = 3
+VERSION = 4
 
 
 @dataclasses.dataclass(frozen=True)
@@ -193,9 +196,12 @@ def build(d: Desc, opts: Opts = Opts()) -> Graph:
         e_d.append(new_event(o.d_tasks))
     e_lm = new_event(o.lm_tasks)
 
-    def op(new: List[Task]):
-        for i, t in enumerate(new):          # round-robin within the operator
-            t.cu = i % o.num_cus
+    def op(new: List[Task], skew: int = 0):
+        # round-robin within the operator; each further round over the units
+        # starts `skew` units on (attention: the chunk count, so that a unit's
+        # chunks come from different sequences)
+        for i, t in enumerate(new):
+            t.cu = (i + (i // o.num_cus) * skew) % o.num_cus
         tasks.extend(new)
 
     op([Task(EMB, b=b, dep=e_tok, trig=e_emb) for b in range(B)])
@@ -206,7 +212,7 @@ def build(d: Desc, opts: Opts = Opts()) -> Graph:
             for g in range(Hkv)
             for r0, r1 in split_rows(grp_rows, o.qkv_tasks_per_group, o.row_block)])
         op([Task(ATT, layer=l, g=g, b=b, chunk=c, dep=e_qkv[l][g], trig=e_att[l][g][b])
-            for g in range(Hkv) for b in range(B) for c in range(Nc)])
+            for g in range(Hkv) for b in range(B) for c in range(Nc)], skew=Nc)
         op([Task(COMB, layer=l, g=g, b=b, dep=e_att[l][g][b], trig=e_comb[l])
             for g in range(Hkv) for b in range(B)])
         op([Task(OPROJ, layer=l, row0=r0, row1=r1, dep=e_comb[l], trig=e_o[l])

@@ -124,5 +124,5 @@ def test_serialize_layout():
     raw = G.serialize(gr)
     nt, ne = len(gr.tasks), len(gr.events)
     assert raw[:8] == b"MKGRAPH1"
-    assert raw[8:12] == (3).to_bytes(4, "little")     # version 3: qk_norm in the desc, use_mfma in the options
+    assert raw[8:12] == (4).to_bytes(4, "little")     # version 4: skewed attention placement
     assert len(raw) == 8 + 4 + 40 + 8 + 4 + 36 + 8 + nt * 40 + ne * 12 + 4 * 4 + nt * 4
