@@ -213,8 +213,9 @@ __device__ __forceinline__ void comp_finish_m(const Params& P, const Ctx& cx, in
 }
 
 // The attention-task path of the vector bodies, on this compute state.
+template <int AR>
 __device__ __forceinline__ void att_run_m(const Params& P, const Ctx& cx, CompM& C, AttState& S, const Piece& pc,
-                                          u32x4 (&ka)[kAttRing], u32x4 (&kv)[kAttRing]) {
+                                          u32x4 (&ka)[AR], u32x4 (&kv)[AR]) {
   Comp A;
   A.lo = C.lo;
   A.end = C.end;
@@ -223,11 +224,17 @@ __device__ __forceinline__ void att_run_m(const Params& P, const Ctx& cx, CompM&
   C.any = A.any;
 }
 
+// KV items an attention task keeps in flight on the matrix-core stream waves
+// (fewer than the vector bodies' kAttRing: the activation ring's registers)
+#ifndef MK_ATT_RING_M
+#define MK_ATT_RING_M 4
+#endif
+constexpr int kAttRingM = MK_ATT_RING_M;
 #ifndef MK_RING_M
-#define MK_RING_M 6
+#define MK_RING_M 8
 #endif
 #ifndef MK_XRING_M
-#define MK_XRING_M 6
+#define MK_XRING_M 4
 #endif
 template <int RING, int XR, bool PROF>
 __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, int s) {
@@ -294,7 +301,7 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
         if (!at && (rfl(cx.recs[r].tsbg) & 15) == T_ATT) {
           // an attention task: its first KV blocks load while it is staged
           AttState S;
-          u32x4 ka[kAttRing], kv[kAttRing];
+          u32x4 ka[kAttRingM], kv[kAttRingM];
           const Piece kpc = kv_piece_of(P, cx, s, r, st);
           att_prefetch(P, cx, kpc, ka, kv);
           if (!comp_start_m<PROF>(P, cx, s, C, acc, S, wt, prof)) return;

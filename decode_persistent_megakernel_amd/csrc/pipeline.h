@@ -280,40 +280,57 @@ __device__ __forceinline__ float across_groups(float v, bool l16) {
   return MAX ? fmaxf(lo, hi) : lo + hi;
 }
 
-// Sum over the lpp lanes of a position group.
-__device__ __forceinline__ float in_group(float v, bool l16) {
-  v += dpp<kDppSwap1>(v);
-  v += dpp<kDppSwap2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  const float w = v + dpp<kDppMirror>(v);
-  return l16 ? w : v;
-}
-
-// One item (position block) of attention: for each of the G heads, the score
-// of this lane's position, and the online-softmax update of its group's
-// running maximum, denominator and weighted values. Scores are in base-2 units
-// (the queries carry scale * log2(e)), so the exponentials are the hardware's
-// exp2.
-__device__ __forceinline__ void att_item(const Params& P, AttState& S, const u32x4 wk, const u32x4 wv, bool valid,
+// Two items (position blocks) of attention: for each of the G heads, the
+// scores of this lane's two positions, then one online-softmax update of its
+// group's running maximum, denominator and weighted values for both (one
+// rescale per pair of items). Scores are in base-2 units (the queries carry
+// scale * log2(e)), so the exponentials are the hardware's exp2. The heads'
+// dot products and lane-group sums are computed side by side, so the
+// cross-lane steps of different heads overlap. q: this lane's 8 dims of each
+// head's scaled query (registers for the whole task).
+__device__ __forceinline__ void att_pair(const Params& P, AttState& S, const float (&q)[kMaxG][8], const u32x4 k0,
+                                         const u32x4 v0, const u32x4 k1, const u32x4 v1, bool valid0, bool valid1,
                                          bool l16) {
-  float kf[8], vf[8];
-  unpack8(wk, kf);
-  unpack8(wv, vf);
+  float kf0[8], kf1[8];
+  unpack8(k0, kf0);
+  unpack8(k1, kf1);
+  float s0[kMaxG], s1[kMaxG];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      d0 = fmaf(q[h][e], kf0[e], d0);
+      d1 = fmaf(q[h][e], kf1[e], d1);
+    }
+    s0[h] = d0;
+    s1[h] = d1;
+  }
+  // sums over the lanes of a position group, all heads at each step
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) { s0[h] += dpp<kDppSwap1>(s0[h]); s1[h] += dpp<kDppSwap1>(s1[h]); }
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) { s0[h] += dpp<kDppSwap2>(s0[h]); s1[h] += dpp<kDppSwap2>(s1[h]); }
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) { s0[h] += dpp<kDppHalfMirror>(s0[h]); s1[h] += dpp<kDppHalfMirror>(s1[h]); }
+  if (l16) {
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) { s0[h] += dpp<kDppMirror>(s0[h]); s1[h] += dpp<kDppMirror>(s1[h]); }
+  }
+  float vf0[8], vf1[8];
+  unpack8(v0, vf0);
+  unpack8(v1, vf1);
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
     if (h < P.G) {
-      const float4 q0 = ld_f4(S.qs + h * P.D), q1 = ld_f4(S.qs + h * P.D + 4);
-      const float q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(q[e], kf[e], d);
-      const float sc = valid ? in_group(d, l16) : -INFINITY;
-      const float mn = fmaxf(S.m[h], sc);
+      const float a = valid0 ? s0[h] : -INFINITY, b = valid1 ? s1[h] : -INFINITY;
+      const float mn = fmaxf(S.m[h], fmaxf(a, b));
       const float al = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(S.m[h] - mn);
-      const float pe = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
-      S.l[h] = fmaf(S.l[h], al, pe);
+      const float p0 = valid0 ? __builtin_amdgcn_exp2f(a - mn) : 0.f;
+      const float p1 = valid1 ? __builtin_amdgcn_exp2f(b - mn) : 0.f;
+      S.l[h] = fmaf(S.l[h], al, p0 + p1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) S.acc[h][e] = fmaf(pe, vf[e], S.acc[h][e] * al);
+      for (int e = 0; e < 8; ++e) S.acc[h][e] = fmaf(p1, vf1[e], fmaf(p0, vf0[e], S.acc[h][e] * al));
       S.m[h] = mn;
     }
   }
@@ -464,37 +481,50 @@ __device__ __forceinline__ void mv_item(const Params& P, Comp& C, Acc<NC>& A, co
 // kAttRing blocks are loaded before the task is staged (att_prefetch): the
 // step is open by then, since this compute unit's previous task was staged.
 constexpr int kAttRing = 8;
-__device__ __forceinline__ void att_prefetch(const Params& P, const Ctx& cx, const Piece& pc, u32x4 (&ka)[kAttRing],
-                                             u32x4 (&kv)[kAttRing]) {
+template <int AR>
+__device__ __forceinline__ void att_prefetch(const Params& P, const Ctx& cx, const Piece& pc, u32x4 (&ka)[AR],
+                                             u32x4 (&kv)[AR]) {
 #pragma unroll
-  for (int j = 0; j < kAttRing; ++j) {
+  for (int j = 0; j < AR; ++j) {
     load_item(P, cx, pc, j, j < pc.n, ka[j], kv[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
+template <int AR>
 __device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C, AttState& S, const Piece& pc,
-                                        u32x4 (&ka)[kAttRing], u32x4 (&kv)[kAttRing]) {
+                                        u32x4 (&ka)[AR], u32x4 (&kv)[AR]) {
+  static_assert(AR % 2 == 0, "attention items are computed in pairs");
   const int lane = cx.lane, lpp = P.D / 8, ppi = 64 / lpp;
   const bool l16 = lpp == 16;
-  int cn = min(kAttRing, pc.n), cbase = 0, base = kAttRing;  // blocks computed in this pass, their first; next to load
+  // this lane's 8 dims of each head's scaled query, for the whole task
+  float q[kMaxG][8];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    const float4 a = h < P.G ? ld_f4(S.qs + h * P.D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b = h < P.G ? ld_f4(S.qs + h * P.D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    q[h][0] = a.x; q[h][1] = a.y; q[h][2] = a.z; q[h][3] = a.w;
+    q[h][4] = b.x; q[h][5] = b.y; q[h][6] = b.z; q[h][7] = b.w;
+  }
+  int cn = min(AR, pc.n), cbase = 0, base = AR;  // blocks computed in this pass, their first; next to load
   for (;;) {
     cn = (int)rfl((uint32_t)cn);
     asm volatile("" : "+s"(cn));  // opaque: no peeled first pass
-    const int ln = min(kAttRing, max(0, pc.n - base));
+    const int ln = min(AR, max(0, pc.n - base));
 #pragma unroll
-    for (int j = 0; j < kAttRing; ++j) {
-      asm volatile("" : : "v"(ka[j]), "v"(kv[j]));
+    for (int j = 0; j < AR; j += 2) {
+      asm volatile("" : : "v"(ka[j]), "v"(kv[j]), "v"(ka[j + 1]), "v"(kv[j + 1]));
       if (j < cn) {
-        const bool valid = C.lo + (C.u0 + cbase + j) * ppi + lane / lpp < C.end;
-        att_item(P, S, ka[j], kv[j], valid, l16);
+        const int pos0 = C.lo + (C.u0 + cbase + j) * ppi + lane / lpp;
+        att_pair(P, S, q, ka[j], kv[j], ka[j + 1], kv[j + 1], pos0 < C.end, j + 1 < cn && pos0 + ppi < C.end, l16);
       }
       load_item(P, cx, pc, base + j, j < ln, ka[j], kv[j]);
+      load_item(P, cx, pc, base + j + 1, j + 1 < ln, ka[j + 1], kv[j + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (ln == 0) break;
     cbase = base;
     cn = ln;
-    base += kAttRing;
+    base += AR;
   }
   // the last pass's zero loads: let them land here, so that the weight ring's
   // waits after this path keep their exact counts
