@@ -169,6 +169,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
   const int kb_f = mf ? d.ffn / 32 : static_cast<int>(cdiv(d.ffn, 2 * kUnitCols) * 2);
   int wave_tiles = 1;
   std::vector<DevTask> dt(g.tasks.size());
+  std::vector<int32_t> walk(g.tasks.size(), 0);  // units the stream waves walk (column-major: 8 row blocks)
   std::vector<PackJob> jobs;
   uint64_t off = 0;
   int max_vrows = 4, wave_vrows = 4, max_res = 4;
@@ -194,9 +195,12 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     x.kb = KB;
     x.kdim = K;
     x.w_off = static_cast<int64_t>(off);
+    x.cm = mf && n_vrb >= 3 && n_vrb <= 8 ? n_vrb : 0;
+    walk[i] = x.cm ? 8 * KB : x.n_units;
     max_vrows = std::max(max_vrows, n_vrb * kUnitRows);
     if (t.type == T_O || t.type == T_D) max_res = std::max(max_res, t.row1 - t.row0);
-    {  // rows of the row blocks each stream wave's piece touches (its partial sums)
+    if (x.cm) wave_tiles = std::max(wave_tiles, x.cm);  // column-major: every wave touches every row block
+    else {  // rows of the row blocks each stream wave's piece touches (its partial sums)
       const int items = x.n_units / 2;
       for (int w = 0; w < kStreams; ++w) {
         const int i0 = int(int64_t(items) * w / kStreams), i1 = int(int64_t(items) * (w + 1) / kStreams);
@@ -206,7 +210,7 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
         wave_tiles = std::max(wave_tiles, touched);
       }
     }
-    jobs.push_back(PackJob{x.w_off, t.type, t.layer, t.g, t.row0, t.row1, K, KB, n_vrb});
+    jobs.push_back(PackJob{x.w_off, t.type, t.layer, t.g, t.row0, t.row1, K, KB, n_vrb, x.cm});
     off += uint64_t(x.n_units) * kUnitBytes;
   }
   m->packed_bytes = off;
@@ -231,8 +235,9 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
         return fail(MK_EUNSUPPORTED, "mk_load_weights: task field out of the stream record's range");
       StreamRec r{};
       r.tsbg = uint32_t(x.type) | uint32_t(slot) << 4 | uint32_t(x.b) << 6 | uint32_t(x.g) << 16;
-      r.lc = uint32_t(x.layer) | uint32_t(x.chunk) << 16;
-      r.n_units = x.n_units;
+      r.lc = x.type == T_ATT ? uint32_t(x.layer) | uint32_t(x.chunk) << 16
+                             : (uint32_t(x.layer) & 0xffffu) | uint32_t(x.cm) << 16;
+      r.n_units = walk[q[qp]];
       r.kq = uint32_t(x.kb) | uint32_t(qp) << 16;
       r.w_off = x.w_off;
       r.id = q[qp];

@@ -25,7 +25,9 @@ constexpr int kUnitRows = 4;
 // dimension, the sequences its M dimension). A row block is 16 rows (gate/up:
 // 8 gate rows then the 8 up rows of the same outputs); an item is the units of
 // column blocks 2j and 2j+1 of one row block; a task's items are stored in
-// (row block, column pair) order.
+// (row block, column pair) order, or, for a task of 3 to 8 row blocks, in
+// (column pair, row block) order (column-major: a stream wave then reads each
+// column pair's activations once for all the task's row blocks).
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaItemCols = 64;
 
@@ -64,7 +66,7 @@ struct DevTask {
   int32_t n_units;   // weight units of a matvec task (0 otherwise)
   int32_t kb;        // column blocks of a matvec task
   int32_t kdim;      // K of a matvec task
-  int32_t pad;
+  int32_t cm;        // matrix-core bodies: row blocks of a task stored column-major (3..8), 0: row-block-major
   int64_t w_off;     // byte offset of the task's units in the packed weights
 };
 
@@ -73,8 +75,9 @@ struct DevTask {
 struct StreamRec {
   uint32_t tsbg;     // type | slot << 4 | b << 6 | g << 16  (staging slot in the first step:
                      // 0, 1 small, 2 big)
-  uint32_t lc;       // layer | chunk << 16
-  int32_t n_units;   // weight units (matvec)
+  uint32_t lc;       // layer | chunk << 16 (attention); layer | column-major row blocks << 16 (matvec)
+  int32_t n_units;   // weight units (matvec; column-major: 8 items per column pair, the missing row
+                     // blocks read as zeros)
   uint32_t kq;       // column blocks | queue position << 16
   int64_t w_off;     // packed weight offset (matvec)
   int32_t flip;      // 1: the small slots swap from one step to the next (odd count per step)
@@ -152,6 +155,7 @@ struct Params {
 struct PackJob {
   int64_t dst_off;
   int32_t type, layer, g, row0, row1, K, KB, n_vrb;
+  int32_t cm;  // matrix-core arrangement stored column-major (items (column pair, row block)), 0: row-block-major
 };
 // (the matrix-core arrangement: KB units of 32 columns per row block, n_vrb row blocks)
 

@@ -84,7 +84,6 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   r.o_tasks = cap(o.o_tasks ? o.o_tasks : N, d.hidden);
   r.gu_tasks = cap(o.gu_tasks ? o.gu_tasks : N, d.ffn);
   r.d_tasks = cap(o.d_tasks ? o.d_tasks : N, d.hidden);
-  r.lm_tasks = cap(o.lm_tasks ? o.lm_tasks : N, d.vocab);
   r.attn_chunks = o.attn_chunks
                       ? o.attn_chunks
                       : std::max(1, std::min(N / (std::min(B, kGroupCols) * Hkv), std::max(1, d.max_seq / 1024)));
@@ -94,6 +93,10 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
     const bool shape_ok = mf_ok(d.hidden) && mf_ok(int64_t(d.n_q_heads) * d.head_dim) && mf_ok(d.ffn);
     r.use_mfma = o.use_mfma ? o.use_mfma : (std::min(B, kMfmaCols) > kGroupCols && shape_ok ? 2 : 1);
   }
+  // LM head: the matrix-core bodies' tasks default to 8 row blocks (128 rows),
+  // so that a stream wave keeps all of a task's row blocks in registers
+  r.lm_tasks = cap(o.lm_tasks ? o.lm_tasks : (r.use_mfma == 2 ? std::max<int32_t>(N, int32_t(cdiv(d.vocab, 128))) : N),
+                   d.vocab);
 
   Graph& g = *out;
   g = Graph{};

@@ -1286,8 +1286,10 @@ __device__ __forceinline__ void run(const Params& P, int cu, int single) {
       StreamRec r;
       int nsmall = 0;
       r.tsbg = (uint32_t)T.type | (uint32_t)next_slot(nsmall, T.type) << 4 | (uint32_t)T.b << 6 | (uint32_t)T.g << 16;
-      r.lc = (uint32_t)T.layer | (uint32_t)T.chunk << 16;
-      r.n_units = T.n_units;
+      // as the host builds the records: column-major matvec tasks walk 8 row blocks per column pair
+      r.lc = T.type == T_ATT ? (uint32_t)T.layer | (uint32_t)T.chunk << 16
+                             : ((uint32_t)T.layer & 0xffffu) | (uint32_t)T.cm << 16;
+      r.n_units = T.cm ? 8 * T.kb : T.n_units;
       r.kq = (uint32_t)T.kb;
       r.w_off = T.w_off;
       r.flip = 0;
@@ -1418,7 +1420,16 @@ extern "C" __global__ void __launch_bounds__(256) mk_pack_m16(const PackJob* job
   for (int64_t idx = threadIdx.x; idx < lanes; idx += blockDim.x) {
     const int64_t u = idx >> 6;
     const int lane = (int)(idx & 63);
-    const int rb = (int)(u / J.KB), kb = (int)(u - (int64_t)rb * J.KB);
+    int rb, kb;
+    if (J.cm) {  // item (column pair c, row block r) at c * cm + r; unit h of it: column block 2c + h
+      const int64_t it = u >> 1;
+      const int c = (int)(it / J.cm);
+      rb = (int)(it - (int64_t)c * J.cm);
+      kb = 2 * c + (int)(u & 1);
+    } else {
+      rb = (int)(u / J.KB);
+      kb = (int)(u - (int64_t)rb * J.KB);
+    }
     const int i = lane & 15, col = kb * 32 + (lane >> 4) * 8;
     int r;
     int64_t row = 0;

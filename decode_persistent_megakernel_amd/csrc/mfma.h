@@ -96,6 +96,82 @@ __device__ __forceinline__ u32x4 lds_ld16(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((uintptr_t)addr);
 }
 
+// The matrix-core walk: wave s's piece of record r. Row-block-major records
+// are cut into items as on the vector bodies (make_piece); a column-major
+// record (lc >> 16 = its row blocks, 3..8) is cut by column pairs, 8 items
+// per column pair (item j of a column is row block j; those past the task's
+// row blocks read zeros).
+struct PieceM {
+  Piece pc;
+  int cm;  // row blocks of a column-major record, 0: row-block-major
+};
+__device__ __forceinline__ PieceM make_piece_m(const Params& P, const Ctx& cx, int s, int r) {
+  PieceM m;
+  m.pc = make_piece(P, cx, s, r);
+  m.cm = 0;
+  const StreamRec R = cx.recs[r];
+  if ((rfl(R.tsbg) & 15) == T_ATT) return m;
+  const int cm = (int)(rfl(R.lc) >> 16);
+  if (cm == 0) return m;
+  const int ncol = (int)rfl((uint32_t)R.n_units) / 16;  // column pairs (8 items, 16 units each)
+  int c0, c1;
+  piece(ncol, s, c0, c1);
+  const int64_t woff =
+      (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
+  m.pc.n = 8 * (c1 - c0);
+  m.pc.ra = m.pc.rb = make_rsrc(P.wpack + woff + (int64_t)c0 * cm * kItemBytes,
+                                (uint32_t)(c1 - c0) * (uint32_t)cm * (uint32_t)kItemBytes);
+  m.cm = cm;
+  return m;
+}
+
+// Loads of piece item i into one ring slot: row-block-major as load_item;
+// column-major item i is row block i & 7 of column pair i >> 3, stored at
+// (i >> 3) * cm + (i & 7) (zeros past the task's row blocks).
+__device__ __forceinline__ void load_item_m(const Params& P, const Ctx& cx, const PieceM& m, int i, bool real, u32x4& a,
+                                            u32x4& b) {
+  const bool cmr = m.cm != 0;
+  const int it = cmr ? (i >> 3) * m.cm + (i & 7) : i;
+  load_item(P, cx, m.pc, it, real && (!cmr || (i & 7) < m.cm), a, b);
+}
+
+struct WalkM {
+  int r, step, t;
+  PieceM pm;
+};
+template <int RING>
+__device__ __forceinline__ Blk next_block_m(const Params& P, const Ctx& cx, int s, WalkM& W) {
+  Blk B;
+  B.i0 = 0;
+  B.n = 0;
+  if (W.t >= W.pm.pc.n) {
+    for (;;) {
+      if (++W.r >= cx.nrec) {
+        W.r = 0;
+        ++W.step;
+      }
+      if (W.step >= P.n_steps || cx.nrec == 0) {
+        B.r = W.r;
+        B.step = W.step;
+        B.flags = kEnd;
+        W.pm.pc.n = 0;
+        W.t = 0;
+        return B;
+      }
+      W.pm = make_piece_m(P, cx, s, W.r);
+      W.t = 0;
+      if (W.pm.pc.n > 0) break;
+    }
+  }
+  B.r = W.r;
+  B.step = W.step;
+  B.i0 = W.t;
+  B.n = min(RING, W.pm.pc.n - W.t);
+  B.flags = (W.t == 0 ? kFirst : 0) | (W.t + B.n == W.pm.pc.n ? kLast : 0);
+  W.t += B.n;
+  return B;
+}
+
 // Compute state of the matvec task being computed.
 struct CompM {
   int r, step;      // stream record and step
@@ -105,6 +181,7 @@ struct CompM {
   bool any;
   float* tiles;     // this wave's partial tiles (LDS)
   XPiece xp;
+  int cm, col, c1;  // column-major: row blocks, next column pair, end of this wave's column pairs
   int natt;
   int layer, b, g;  // attention
   int lo, end, u0;
@@ -180,14 +257,25 @@ __device__ __forceinline__ bool comp_start_m(const Params& P, const Ctx& cx, int
   } else {
     C.tiles = part_ptr(cx, C.slot) + (size_t)s * P.wave_tiles * 256;
     C.xp = make_xpiece(P, cx, s, R, C.slot, C.type);
-    const int items = (int)rfl((uint32_t)R.n_units) / 2;
-    int i0, i1;
-    piece(items, s, i0, i1);
-    C.rb = i0 / C.xp.KB2;
-    C.rb0 = C.rb;
-    C.kc = C.xp.col0;
-    C.pend = false;
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    C.cm = (int)(rfl(R.lc) >> 16);
+    if (C.cm) {  // column-major: this wave's column pairs, all the task's row blocks
+      int c0, c1;
+      piece(C.xp.KB2, s, c0, c1);
+      C.col = c0;
+      C.c1 = c1;
+      C.rb0 = 0;
+      C.rb = C.cm;
+      C.pend = false;
+    } else {
+      const int items = (int)rfl((uint32_t)R.n_units) / 2;
+      int i0, i1;
+      piece(items, s, i0, i1);
+      C.rb = i0 / C.xp.KB2;
+      C.rb0 = C.rb;
+      C.kc = C.xp.col0;
+      C.pend = false;
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
   C.any = false;
   return true;
@@ -197,6 +285,10 @@ __device__ __forceinline__ void comp_finish_m(const Params& P, const Ctx& cx, in
                                               bool prof, uint32_t t_first) {
   if (C.type == T_ATT) {
     att_finish(P, S, C.tiles, s, cx.lane, !C.any);
+  } else if (C.cm) {  // column-major: every row block of the task (the tiles are written at its last pass)
+    int* pr = piece_words(cx, C.slot, s);
+    pr[0] = 0;
+    pr[1] = C.any ? C.cm - 1 : -1;
   } else {
     if (C.pend) tile_flush(acc, C.tiles, C.rb - C.rb0, cx.lane);
     int* pr = piece_words(cx, C.slot, s);
@@ -220,7 +312,8 @@ __device__ __forceinline__ void att_run_m(const Params& P, const Ctx& cx, CompM&
   A.lo = C.lo;
   A.end = C.end;
   A.u0 = C.u0;
-  att_run(P, cx, A, S, pc, ka, kv);
+  att_run<AR, false>(P, cx, A, S, pc, ka, kv);  // queries from LDS: the registers are the rings'
+
   C.any = A.any;
 }
 
@@ -245,12 +338,12 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
   Waits wt;
   waits_init<PROF>(P, cx, wt);
 
-  Walk W;
+  WalkM W;
   W.r = -1;
   W.step = 0;
   W.t = 0;
-  W.pc = make_piece(P, cx, s, 0);
-  W.pc.n = 0;
+  W.pm = make_piece_m(P, cx, s, 0);
+  W.pm.pc.n = 0;
 
   CompM C;
   C.r = -1;
@@ -261,6 +354,7 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
   C.xp.n = 0;
   C.xp.KB2 = 4;
   C.xp.col0 = 0;
+  C.cm = 0;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   uint32_t t_first = 0;
 
@@ -268,10 +362,11 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
   u32x4 xa[XR][4];
 
   // the first block's weights
-  Blk cur = next_block<RING>(P, cx, s, W);
+  static_assert(RING == 8, "a column-major block is one column pair of 8 row blocks");
+  Blk cur = next_block_m<RING>(P, cx, s, W);
 #pragma unroll
   for (int j = 0; j < RING; ++j) {
-    load_item(P, cx, W.pc, cur.i0 + j, j < cur.n, ra[j], rb[j]);
+    load_item_m(P, cx, W.pm, cur.i0 + j, j < cur.n, ra[j], rb[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
   bool fin = false;
@@ -318,6 +413,63 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
       }
     }
     if (cur.flags & kEnd) break;
+    if (C.cm) {
+      // column-major task: per pass one column pair of 8 row blocks; the
+      // activations of a column pair are read once, split into hi/lo once,
+      // and the next column pair's are read at the start of the pass (as far
+      // ahead as the weights)
+      const Params& P = fresh_params();
+      load_x(P, cx, C.xp, C.col, C.col < C.c1, xa[0]);
+      f32x4 acc8[8];  // the sums of each row block of the task
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc8[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      wait_all();
+      for (;;) {
+        cur.n = (int)rfl((uint32_t)cur.n);
+        cur.flags = (int)rfl((uint32_t)cur.flags);
+        cur.i0 = (int)rfl((uint32_t)cur.i0);
+        asm volatile("" : "+s"(cur.n), "+s"(cur.flags), "+s"(cur.i0));
+        const Params& P = fresh_params();
+        if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
+        waits_count(wt, 3, cur.n);
+        const Blk nxt = next_block_m<RING>(P, cx, s, W);
+        asm volatile("" : : "v"(xa[0][0]), "v"(xa[0][1]), "v"(xa[0][2]), "v"(xa[0][3]));
+        bf16x8 h0, l0, h1, l1;
+        {
+          const uint32_t ga = C.xp.gl + (uint32_t)C.col * C.xp.gstep;
+          const u32x4 g0 = lds_ld16(ga), g1 = lds_ld16(ga + C.xp.gstep / 2u);
+          split8(xa[0][0], xa[0][1], g0, h0, l0);
+          split8(xa[0][2], xa[0][3], g1, h1, l1);
+        }
+        load_x(P, cx, C.xp, C.col + 1, C.col + 1 < C.c1, xa[1]);
+        C.any = true;
+#pragma unroll
+        for (int j = 0; j < RING; ++j) {
+          asm volatile("" : : "v"(ra[j]), "v"(rb[j]));
+          if (j < C.cm) {
+            const bf16x8 b0 = __builtin_bit_cast(bf16x8, ra[j]), b1 = __builtin_bit_cast(bf16x8, rb[j]);
+            acc8[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, b0, acc8[j], 0, 0, 0);
+            acc8[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l0, b0, acc8[j], 0, 0, 0);
+            acc8[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, b1, acc8[j], 0, 0, 0);
+            acc8[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l1, b1, acc8[j], 0, 0, 0);
+          }
+          load_item_m(P, cx, W.pm, nxt.i0 + j, j < nxt.n, ra[j], rb[j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ++C.col;
+        const bool last = (cur.flags & kLast) != 0;
+        cur = nxt;
+        if (last) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xa[0][e] = xa[1][e];
+      }
+      // the sums of every row block of the task
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r < C.cm) tile_flush(acc8[r], C.tiles, r, lane);
+      fin = true;
+      continue;
+    }
     {
       // the task's activations exist now: its first XR items' (column pairs
       // col0, col0 + 1, ... modulo KB2)
@@ -338,7 +490,7 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
       const Params& P = fresh_params();
       if (prof && t_first == 0) t_first = rfl((uint32_t)wall_clock64());
       waits_count(wt, 3, cur.n);
-      const Blk nxt = next_block<RING>(P, cx, s, W);
+      const Blk nxt = next_block_m<RING>(P, cx, s, W);
       // column pair of piece item cur.i0 + XR, advanced one item per slot
       int xc = (int)rfl((uint32_t)((C.xp.col0 + cur.i0 + XR) % C.xp.KB2));
 #pragma unroll
@@ -353,7 +505,7 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
         const int t = cur.i0 + j + XR;
         load_x(P, cx, C.xp, xc, t < C.xp.n, xa[j % XR]);
         xc = xc + 1 == C.xp.KB2 ? 0 : xc + 1;
-        load_item(P, cx, W.pc, nxt.i0 + j, j < nxt.n, ra[j], rb[j]);
+        load_item_m(P, cx, W.pm, nxt.i0 + j, j < nxt.n, ra[j], rb[j]);
         __builtin_amdgcn_sched_barrier(0);
       }
       const bool last = (cur.flags & kLast) != 0;

@@ -287,10 +287,24 @@ __device__ __forceinline__ float across_groups(float v, bool l16) {
 // scale * log2(e)), so the exponentials are the hardware's exp2. The heads'
 // dot products and lane-group sums are computed side by side, so the
 // cross-lane steps of different heads overlap. q: this lane's 8 dims of each
-// head's scaled query (registers for the whole task).
-__device__ __forceinline__ void att_pair(const Params& P, AttState& S, const float (&q)[kMaxG][8], const u32x4 k0,
+// head's scaled query (QREG: registers for the whole task; else read from the
+// staging slot here, once per pair).
+__device__ __forceinline__ void load_q(const Params& P, const AttState& S, float (&q)[kMaxG][8]) {
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    const float4 a = h < P.G ? ld_f4(S.qs + h * P.D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b = h < P.G ? ld_f4(S.qs + h * P.D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    q[h][0] = a.x; q[h][1] = a.y; q[h][2] = a.z; q[h][3] = a.w;
+    q[h][4] = b.x; q[h][5] = b.y; q[h][6] = b.z; q[h][7] = b.w;
+  }
+}
+template <bool QREG>
+__device__ __forceinline__ void att_pair(const Params& P, AttState& S, const float (&qr)[kMaxG][8], const u32x4 k0,
                                          const u32x4 v0, const u32x4 k1, const u32x4 v1, bool valid0, bool valid1,
                                          bool l16) {
+  float ql[kMaxG][8];
+  if constexpr (!QREG) load_q(P, S, ql);
+  const float(&q)[kMaxG][8] = QREG ? qr : ql;
   float kf0[8], kf1[8];
   unpack8(k0, kf0);
   unpack8(k1, kf1);
@@ -490,21 +504,15 @@ __device__ __forceinline__ void att_prefetch(const Params& P, const Ctx& cx, con
     __builtin_amdgcn_sched_barrier(0);
   }
 }
-template <int AR>
+template <int AR, bool QREG = true>
 __device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C, AttState& S, const Piece& pc,
                                         u32x4 (&ka)[AR], u32x4 (&kv)[AR]) {
   static_assert(AR % 2 == 0, "attention items are computed in pairs");
   const int lane = cx.lane, lpp = P.D / 8, ppi = 64 / lpp;
   const bool l16 = lpp == 16;
-  // this lane's 8 dims of each head's scaled query, for the whole task
+  // this lane's 8 dims of each head's scaled query, for the whole task (QREG)
   float q[kMaxG][8];
-#pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
-    const float4 a = h < P.G ? ld_f4(S.qs + h * P.D) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 b = h < P.G ? ld_f4(S.qs + h * P.D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    q[h][0] = a.x; q[h][1] = a.y; q[h][2] = a.z; q[h][3] = a.w;
-    q[h][4] = b.x; q[h][5] = b.y; q[h][6] = b.z; q[h][7] = b.w;
-  }
+  if constexpr (QREG) load_q(P, S, q);
   int cn = min(AR, pc.n), cbase = 0, base = AR;  // blocks computed in this pass, their first; next to load
   for (;;) {
     cn = (int)rfl((uint32_t)cn);
@@ -515,7 +523,8 @@ __device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C,
       asm volatile("" : : "v"(ka[j]), "v"(kv[j]), "v"(ka[j + 1]), "v"(kv[j + 1]));
       if (j < cn) {
         const int pos0 = C.lo + (C.u0 + cbase + j) * ppi + lane / lpp;
-        att_pair(P, S, q, ka[j], kv[j], ka[j + 1], kv[j + 1], pos0 < C.end, j + 1 < cn && pos0 + ppi < C.end, l16);
+        att_pair<QREG>(P, S, q, ka[j], kv[j], ka[j + 1], kv[j + 1], pos0 < C.end, j + 1 < cn && pos0 + ppi < C.end,
+                       l16);
       }
       load_item(P, cx, pc, base + j, j < ln, ka[j], kv[j]);
       load_item(P, cx, pc, base + j + 1, j + 1 < ln, ka[j + 1], kv[j + 1]);

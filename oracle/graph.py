@@ -144,19 +144,21 @@ def resolve(d: Desc, o: Opts) -> Opts:
     # sized so that one group's attention tasks cover the compute units
     chunks = o.attn_chunks or max(1, min(n // (min(d.max_batch, GROUP_COLS) * d.n_kv_heads),
                                          max(1, d.max_seq // 1024)))
+    # matvec bodies (1 vector ALU, 2 matrix cores): the matrix cores when a
+    # launch would hold more sequences than the vector bodies stage and every
+    # K dimension is a multiple of 64, at least 256
+    use_mfma = o.use_mfma or (2 if min(d.max_batch, MFMA_COLS) > GROUP_COLS and _mfma_shape(d) else 1)
     return Opts(
         num_cus=n,
         qkv_tasks_per_group=cap(o.qkv_tasks_per_group or _ceil_div(n, d.n_kv_heads), grp_rows),
         o_tasks=cap(o.o_tasks or n, d.hidden),
         gu_tasks=cap(o.gu_tasks or n, d.ffn),
         d_tasks=cap(o.d_tasks or n, d.hidden),
-        lm_tasks=cap(o.lm_tasks or n, d.vocab),
         attn_chunks=chunks,
         row_block=rb,
-        # matvec bodies (1 vector ALU, 2 matrix cores): the matrix cores when a
-        # launch would hold more sequences than the vector bodies stage and
-        # every K dimension is a multiple of 64, at least 256
-        use_mfma=o.use_mfma or (2 if min(d.max_batch, MFMA_COLS) > GROUP_COLS and _mfma_shape(d) else 1),
+        use_mfma=use_mfma,
+        # LM head: the matrix-core bodies' tasks default to 8 row blocks of 16
+        lm_tasks=cap(o.lm_tasks or (max(n, _ceil_div(d.vocab, 128)) if use_mfma == 2 else n), d.vocab),
     )
 
 
