@@ -52,7 +52,7 @@ def algorithmic_bytes(shape, positions) -> int:
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc", f)
-                  for f in ("kernels.hip", "pipeline.h", "device.h")]
+                  for f in ("kernels.hip", "pipeline.h", "mfma.h", "device.h")]
 
 
 def recorded_traffic(kernel: str, workload_name: str, steps: int, batch: int):

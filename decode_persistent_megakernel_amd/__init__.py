@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "mk_decode_step": [vp, vp, vp, i32, vp, vp, i32, vp],
         "mk_generate": [vp, vp, vp, i32, i32, vp, vp, vp],
         "mk_generate_noalloc": [vp, vp, vp, i32, i32, vp, vp, vp],
+        "mk_prefill": [vp, vp, i32, i32, i32, vp, vp, vp],
         "mk_check": [vp, vp],
         "mk_set_watchdog_ms": [vp, i32],
         "mk_debug_drop_signal": [vp, i32],
@@ -194,6 +195,11 @@ def mk_generate_noalloc(model: int, tokens0, pos0, batch: int, n_steps: int, out
                         stream=None) -> None:
     _ok(lib().mk_generate_noalloc(model, _ptr(tokens0), _ptr(pos0), batch, n_steps, _ptr(out_tokens),
                                   _ptr(last_logits), _stream(stream)))
+
+
+def mk_prefill(model: int, tokens, n_tokens: int, seq: int, pos0: int, logits, next_tokens, stream=None) -> None:
+    _ok(lib().mk_prefill(model, _ptr(tokens), n_tokens, seq, pos0, _ptr(logits), _ptr(next_tokens),
+                         _stream(stream)))
 
 
 def mk_check(model: int, stream=None) -> None:

@@ -303,6 +303,9 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     // overlays all three, so the merge slot holds what it needs beyond them
     big_floats = (std::max(32 + need_comb, 32 + need_mv_big - 2 * small_floats) + 3) & ~int64_t(3);
     part_floats = mf ? int64_t(kStreams) * wave_tiles * 256 : (int64_t(kStreams) * ncap * wave_vrows + 3) & ~int64_t(3);
+    // a prefill step's attention stages its earlier columns' keys and values
+    // (and their scores) in the partial-sum area of its slot
+    part_floats = std::max<int64_t>(part_floats, (int64_t(ncap - 1) * 2 * D + kMaxG * kPrefillMax + 3) & ~int64_t(3));
     fixed = kCtlBytes + size_t(4) * size_t(2 * small_floats + big_floats + 3 * part_floats) +
             size_t(srec_max) * sizeof(StreamRec);
     if (fixed <= lds_max || mf) break;  // (the matrix-core bodies stage no per-sequence inputs)
@@ -649,6 +652,46 @@ int mk_generate_noalloc(mk_model* m, const int32_t* d_tokens0, const int32_t* d_
     P.waits = m->waits;
     HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, m->mfma, s),
             "hipLaunchCooperativeKernel(mk_persistent)");
+  }
+  return MK_OK;
+}
+
+int mk_prefill(mk_model* m, const int32_t* d_tokens, int32_t n_tokens, int32_t seq, int32_t pos0, float* d_logits,
+               int32_t* d_next, void* stream) {
+  if (!m) return fail(MK_EINVAL, "mk_prefill: NULL model");
+  if (!d_tokens || !d_next) return fail(MK_EINVAL, "mk_prefill: NULL token or output pointer");
+  if (n_tokens < 1 || seq < 0 || seq >= m->max_batch || pos0 < 0 || int64_t(pos0) + n_tokens > m->base.S)
+    return fail(MK_EINVAL, "mk_prefill: need n_tokens >= 1, 0 <= seq < max_batch and pos0 + n_tokens <= max_seq");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != m->device)
+    return fail(MK_EINVAL, "the current HIP device is not the model's device");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t seq_kv = size_t(m->base.Hkv) * size_t(m->base.S) * size_t(m->base.D);
+  for (int32_t c0 = 0; c0 < n_tokens; c0 += m->ncap) {
+    const int32_t nb = std::min(m->ncap, n_tokens - c0);
+    int rc = prepare_epoch(m, 1, s);
+    if (rc) return rc;
+    mk::Params P = m->base;
+    P.tokens_in = d_tokens + c0;
+    P.pos_in = d_tokens + c0;  // (positions come from pre_p0)
+    P.out_tokens = d_next + c0;
+    P.out_stride = nb;
+    P.logits_out = d_logits ? d_logits + size_t(c0) * size_t(P.V) : nullptr;
+    P.kcache = m->base.kcache + size_t(seq) * seq_kv;
+    P.vcache = m->base.vcache + size_t(seq) * seq_kv;
+    P.batch = nb;
+    P.n_steps = 1;
+    P.prefill = 1;
+    P.pre_p0 = pos0 + c0;
+    P.timeout_ticks = m->timeout_ticks;
+    P.epoch0 = m->epoch;
+    P.use_events = 1;
+    P.drop_task = m->drop_task;
+    P.profile = nullptr;
+    P.waits = m->waits;
+    HIP_TRY(mk::launch_persistent(P, m->g.opts.num_cus, m->lds_bytes, m->mfma, s),
+            "hipLaunchCooperativeKernel(mk_persistent)");
+    m->epoch += 1;
   }
   return MK_OK;
 }

@@ -47,6 +47,7 @@ constexpr int kMaxCols = 4;    // sequences a matvec task handles (vector bodies
                                // matrix-core bodies handle kMfmaCols, graph.h)
 constexpr int kMaxBatch = 256; // sequences a model holds (larger calls run in groups of at most kMaxCols)
 constexpr int kMaxG = 4;       // query heads per kv head
+constexpr int kPrefillMax = 16;  // columns of a prefill step (the matrix-core bodies' width)
 constexpr int kStripes = 64;   // event counter stripes: one per lane of the polling wave
 constexpr int kEventWords = kStripes * 32;  // each stripe in its own 128-byte line
 constexpr int kCtlBytes = 1024;             // control words (see kernels)
@@ -141,6 +142,9 @@ struct Params {
   float* logits_out;          // [batch][V] or null (written at the last step)
   int32_t batch;
   int32_t n_steps;
+  int32_t prefill;            // 1: the columns are the consecutive positions pre_p0 + b of one sequence (its
+                              //    cache rows are the call's, kcache / vcache point at them), one step
+  int32_t pre_p0;             // prefill: position of column 0
   uint32_t epoch0;
   int32_t use_events;         // 0: single-task workgroups ordered by the stream
   uint64_t timeout_ticks;     // 100 MHz constant clock

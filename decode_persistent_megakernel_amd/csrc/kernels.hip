@@ -63,7 +63,7 @@ static_assert((kPieceCtl + 3 * kStreams * 2) * 4 <= kCtlBytes, "control area");
 constexpr int kOnesCtl = 240;
 static_assert(kOnesCtl >= kPieceCtl + 3 * kStreams * 2 && (kOnesCtl + 4) * 4 <= kCtlBytes, "control area");
 // slot header fields (as int)
-enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11 };
+enum { H_P = 8, H_LO = 9, H_END = 10, H_FLAGS = 11, H_NIN = 12 };
 
 // ---------------------------------------------------------------------------
 // helpers
@@ -302,6 +302,29 @@ __device__ __forceinline__ int task_at(const Params& P, const Ctx& cx, int qi) {
 // of len positions (c <= Nc <= 256 and len <= 2^22 keep the product in 32 bits).
 __device__ __forceinline__ int chunk_bound(int c, int64_t len, int Nc) {
   return (int)((uint32_t)c * (uint32_t)len / (uint32_t)Nc);
+}
+
+// Position of column b at `step` (prefill: consecutive positions of one
+// sequence from pre_p0), and the column's row index in the KV caches (prefill:
+// every column is the one sequence whose rows kcache / vcache point at).
+__device__ __forceinline__ int call_pos(const Params& P, int b, int step) {
+  return P.prefill ? P.pre_p0 + b : ld_uniform(P.pos_in, b) + step;
+}
+__device__ __forceinline__ int kv_row_b(const Params& P, int b) { return P.prefill ? 0 : b; }
+
+// Positions attention chunk c of a column at position p streams from the KV
+// cache: decode, the chunk's share of [0, p + 1) below p - 1 (p - 1 and p are
+// staged); prefill, the chunk's share of [0, pre_p0) (the positions of this
+// call's columns up to p are staged from this step's projections).
+__device__ __forceinline__ void att_stream_range(const Params& P, int chunk, int p, int& lo, int& end) {
+  if (P.prefill) {
+    lo = chunk_bound(chunk, P.pre_p0, P.Nc);
+    end = chunk_bound(chunk + 1, P.pre_p0, P.Nc);
+  } else {
+    const int64_t len = (int64_t)p + 1;
+    lo = chunk_bound(chunk, len, P.Nc);
+    end = max(lo, min(chunk_bound(chunk + 1, len, P.Nc), p - 1));
+  }
 }
 
 // Staging slots: two small ones (0, 1), the merge slot (2) and the
@@ -615,10 +638,67 @@ __device__ __forceinline__ float* att_part_ptr(const Params& P, const Ctx& cx, i
 // the task appends, which does not depend on the event (held in pre.g[0]).
 __device__ __forceinline__ void stage_att_pre(const Params& P, const Ctx& cx, const DevTask& T, int step,
                                               StagePre& pre) {
-  const int p = T.b < P.batch ? ld_uniform(P.pos_in, T.b) + step : -1;
+  const int p = T.b < P.batch ? call_pos(P, T.b, step) : -1;
   float2 cs = make_float2(0.f, 0.f);
   if (p >= 0 && p < P.S && cx.lane < P.D / 2) cs = P.rope_cs[(size_t)p * (P.D / 2) + cx.lane];
   pre.g[0] = make_uint2(__float_as_uint(cs.x), __float_as_uint(cs.y));
+}
+
+// Prefill, the owner chunk of a column at position p: the keys and values of
+// positions pre_p0 .. p - 1 (columns 0 .. n_in - 1 of this call, their
+// projections from this step), each key RMS-normalised per head (qk_norm) and
+// rotated at its own position, both rounded to bf16 as the cache stores them,
+// into the slot's partial-sum area (idle during an attention task):
+// [n_in][key D | value D] floats (n_in < ncap), then, from (ncap - 1) * 2D,
+// the scores [kMaxG][kPrefillMax].
+__device__ __forceinline__ float* prefill_kv_ptr(const Ctx& cx, int slot) { return part_ptr(cx, slot); }
+__device__ __forceinline__ void stage_att_prefill(const Params& P, const Ctx& cx, const DevTask& T, int slot, int n_in) {
+  const int G = P.G, D = P.D, Dh = D / 2, GR = (G + 2) * D;
+  const int lane = cx.lane;
+  float* dst = prefill_kv_ptr(cx, slot);
+  const uint16_t* gk = P.gains + (size_t)(2 * P.L + 1) * P.H + (size_t)T.layer * 2 * D + D;
+  // lane jj < Dh handles the rotation pair (jj, jj + Dh) of the key and the
+  // value dims jj and jj + Dh; four columns' loads in flight at a time
+  constexpr int kGrp = 4;
+  for (int j0 = 0; j0 < n_in; j0 += kGrp) {
+    float ka[kGrp], kb[kGrp], va[kGrp], vb[kGrp];
+    float2 cs[kGrp];
+#pragma unroll
+    for (int i = 0; i < kGrp; ++i) {
+      const int j = j0 + i;
+      ka[i] = kb[i] = va[i] = vb[i] = 0.f;
+      cs[i] = make_float2(1.f, 0.f);
+      if (j < n_in && lane < Dh) {
+        const float* src = P.qkv + ((size_t)j * P.Hkv + T.g) * GR;
+        ka[i] = ld_coh(src + G * D + lane);
+        kb[i] = ld_coh(src + G * D + lane + Dh);
+        va[i] = ld_coh(src + (G + 1) * D + lane);
+        vb[i] = ld_coh(src + (G + 1) * D + lane + Dh);
+        cs[i] = P.rope_cs[(size_t)(P.pre_p0 + j) * Dh + lane];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kGrp; ++i) {
+      const int j = j0 + i;
+      if (j < n_in) {
+        float a = ka[i], b = kb[i];
+        if (P.qk_norm) {
+          const float f = 1.0f / sqrtf(wave_sum(a * a + b * b) / (float)D + P.eps);
+          if (lane < Dh) {
+            a *= f * bf2f(gk[lane]);
+            b *= f * bf2f(gk[lane + Dh]);
+          }
+        }
+        if (lane < Dh) {
+          float* kd = dst + (size_t)j * 2 * D;
+          kd[lane] = bf2f(f2bf(a * cs[i].x - b * cs[i].y));
+          kd[lane + Dh] = bf2f(f2bf(b * cs[i].x + a * cs[i].y));
+          kd[D + lane] = bf2f(f2bf(va[i]));
+          kd[D + lane + Dh] = bf2f(f2bf(vb[i]));
+        }
+      }
+    }
+  }
 }
 
 __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const DevTask& T, int slot, int step,
@@ -635,28 +715,33 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
   const float qscale = P.attn_scale * 1.4426950408889634f;  // scores in base-2 units
   const int lane = cx.lane;
   const bool active = T.b < P.batch;
-  int p = active ? ld_uniform(P.pos_in, T.b) + step : 0;
+  int p = active ? call_pos(P, T.b, step) : 0;
   const bool valid = active && p >= 0 && p < P.S;
   if (active && !valid && lane == 0) __hip_atomic_fetch_or(P.status, kStatusBadPos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!valid) p = 0;
-  const int64_t len = (int64_t)p + 1;
-  const int lo = chunk_bound(T.chunk, len, P.Nc), hi = chunk_bound(T.chunk + 1, len, P.Nc);
+  int lo, end;
+  att_stream_range(P, T.chunk, p, lo, end);
+  const int hi = chunk_bound(T.chunk + 1, (int64_t)p + 1, P.Nc);
   const bool owner = valid && T.chunk == P.Nc - 1;
-  // position p - 1 (appended by the previous step) is not streamed: this
-  // task's dependency implies its append is complete, and the chunk that holds
-  // it reads it here
-  const bool prev = valid && p >= 1 && lo <= p - 1 && p - 1 < hi;
+  // decode: position p - 1 (appended by the previous step) is not streamed:
+  // this task's dependency implies its append is complete, and the chunk that
+  // holds it reads it here
+  const bool prev = valid && !P.prefill && p >= 1 && lo <= p - 1 && p - 1 < hi;
+  // prefill: the owner chunk also takes the positions pre_p0 .. p - 1 (this
+  // call's earlier columns), staged below from this step's projections
+  const int n_in = valid && owner && P.prefill ? p - P.pre_p0 : 0;
   if (lane == 0) {
     ih[H_P] = p;
     ih[H_LO] = lo;
-    ih[H_END] = valid ? max(lo, min(hi, p - 1)) : lo;
+    ih[H_END] = valid ? end : lo;
     ih[H_FLAGS] = (valid ? 1 : 0) | (owner ? 2 : 0) | (active ? 4 : 0) | (prev ? 8 : 0);
+    ih[H_NIN] = n_in;
   }
   if (!valid) return;
   if (prev) {
     float* kf1 = vf + D + D;  // after the bf16 bits of the new key and value
     float* vf1 = kf1 + D;
-    const size_t row = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.S + (p - 1)) * D;
+    const size_t row = ((((size_t)T.layer * P.B + kv_row_b(P, T.b)) * P.Hkv + T.g) * P.S + (p - 1)) * D;
     const uint32_t* kc = reinterpret_cast<const uint32_t*>(P.kcache + row);
     const uint32_t* vc = reinterpret_cast<const uint32_t*>(P.vcache + row);
     for (int w = lane; w < D / 2; w += 64) {
@@ -707,6 +792,7 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
     vf[d] = bf2f(vb);
     kvb[D + d] = (uint16_t)vb;
   }
+  if (n_in > 0) stage_att_prefill(P, cx, T, slot, n_in);
 }
 
 // offset of the second staged array of merge / argmax tasks
@@ -993,6 +1079,20 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
   const float* part = att_part_ptr(P, cx, slot);
   const float* pml = part + kStreams * G * D;  // (m, l) of [wave][head]
   const int lane = cx.lane, p = ih[H_P];
+  // prefill: the scores of this call's earlier positions (staged keys), one
+  // lane per (head, position), kept beside them in LDS
+  const int n_in = ih[H_NIN];
+  float* kin = prefill_kv_ptr(cx, slot);
+  float* s_in = kin + (size_t)(P.ncap - 1) * 2 * D;  // [kMaxG][kPrefillMax] (n_in < ncap)
+  if (n_in > 0) {
+    const int h = lane / kPrefillMax, j = lane % kPrefillMax;
+    if (h < G && j < n_in) {
+      float a = 0.f;
+      for (int d = 0; d < D; ++d) a = fmaf(q[h * D + d], kin[(size_t)j * 2 * D + d], a);
+      s_in[h * kPrefillMax + j] = a * P.attn_scale;
+    }
+    wait_lgkm();
+  }
   // scores of the new position and of p - 1 (their keys and values are the
   // staged ones)
   float sp[kMaxG], sq[kMaxG];
@@ -1035,6 +1135,7 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
     float M = fmaxf(s_new, s_prev);
 #pragma unroll
     for (int w = 0; w < kStreams; ++w) M = fmaxf(M, mw[w]);
+    for (int j = 0; j < n_in; ++j) M = fmaxf(M, s_in[h * kPrefillMax + j]);
     float l = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1049,6 +1150,13 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
       l += e;
       a.x = fmaf(e, vf1[d], a.x); a.y = fmaf(e, vf1[d + 1], a.y);
       a.z = fmaf(e, vf1[d + 2], a.z); a.w = fmaf(e, vf1[d + 3], a.w);
+    }
+    for (int j = 0; j < n_in; ++j) {  // prefill: this call's earlier positions
+      const float e = expf(s_in[h * kPrefillMax + j] - M);
+      const float* vj = kin + (size_t)j * 2 * D + D + d;
+      l += e;
+      a.x = fmaf(e, vj[0], a.x); a.y = fmaf(e, vj[1], a.y);
+      a.z = fmaf(e, vj[2], a.z); a.w = fmaf(e, vj[3], a.w);
     }
     if (owner) {
       const float e = expf(s_new - M);
@@ -1066,7 +1174,7 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
     }
   }
   if (owner) {
-    const size_t row = ((((size_t)T.layer * P.B + T.b) * P.Hkv + T.g) * P.S + p) * D;
+    const size_t row = ((((size_t)T.layer * P.B + kv_row_b(P, T.b)) * P.Hkv + T.g) * P.S + p) * D;
     uint32_t* kc = reinterpret_cast<uint32_t*>(P.kcache + row);
     uint32_t* vc = reinterpret_cast<uint32_t*>(P.vcache + row);
     for (int w = lane; w < D / 2; w += 64) {

@@ -59,14 +59,6 @@ struct Piece {
   uint32_t lane_off;     // this lane's byte offset within a unit (weights) or a position's row (attention)
 };
 
-// The streamed positions of attention chunk `chunk` for a sequence at position
-// p: [lo, end), the chunk's share of [0, p + 1) minus p - 1 and p.
-__device__ __forceinline__ void att_stream_range(int chunk, int p, int Nc, int& lo, int& end) {
-  const int64_t len = (int64_t)p + 1;
-  lo = chunk_bound(chunk, len, Nc);
-  end = max(lo, min(chunk_bound(chunk + 1, len, Nc), p - 1));
-}
-
 __device__ __forceinline__ rsrc_t zero_rsrc(const Params& P, const Ctx& cx) {
   return make_rsrc(P.zeros + (size_t)rfl((uint32_t)cx.cu & (kZeroBlocks - 1)) * 2 * kUnitBytes, 2 * kUnitBytes);
 }
@@ -119,14 +111,14 @@ __device__ __forceinline__ Piece kv_piece_of(const Params& P, const Ctx& cx, int
   const StreamRec R = cx.recs[r];
   const uint32_t tsbg = rfl(R.tsbg), lc = rfl(R.lc);
   const int b = (tsbg >> 6) & 1023, g = tsbg >> 16, layer = lc & 0xffff, chunk = lc >> 16;
-  const int pos = b < P.batch ? ld_uniform(P.pos_in, b) + step : -1;
+  const int pos = b < P.batch ? call_pos(P, b, step) : -1;
   int lo = 0, end = 0, j0 = 0, j1 = 0;
   if (pos >= 0 && pos < P.S) {
-    att_stream_range(chunk, pos, P.Nc, lo, end);
+    att_stream_range(P, chunk, pos, lo, end);
     const int ppi = 64 / (P.D / 8);
     piece(end > lo ? (end - lo + ppi - 1) / ppi : 0, s, j0, j1);
   }
-  return make_kv_piece(P, cx, layer, b < P.batch ? b : 0, g, lo, end, j0, j1 - j0);
+  return make_kv_piece(P, cx, layer, b < P.batch ? kv_row_b(P, b) : 0, g, lo, end, j0, j1 - j0);
 }
 
 // A block: up to RING consecutive items of one piece.

@@ -7,6 +7,7 @@ from typing import Dict, Optional
 
 from . import (GraphOpts, MK_MODE_MEGAKERNEL, desc_from_shape, mk_build_task_graph, mk_check,
                mk_decode_step, mk_free_graph, mk_free_model, mk_generate, mk_generate_noalloc, mk_graph_info,
+               mk_prefill,
                mk_graph_serialize, mk_load_weights, mk_model_info)
 
 
@@ -73,6 +74,16 @@ class Session:
         fn = mk_generate_noalloc if noalloc else mk_generate
         fn(self.model, self.tok, self.pos, b, n_steps, out, self.logits if last_logits else None)
         return out
+
+    def prefill(self, tokens, seq: int = 0, pos0: int = 0, logits: bool = True):
+        """Prompt tokens of sequence ``seq`` at positions pos0.. as columns of
+        one graph step per launch group; returns (next tokens, logits [n, V])."""
+        n = len(tokens)
+        t = self.torch.as_tensor(list(tokens), dtype=self.torch.int32, device=self.tok.device)
+        nxt = self.torch.zeros(n, dtype=self.torch.int32, device=self.tok.device)
+        lg = self.torch.zeros((n, self.shape.vocab), dtype=self.torch.float32, device=self.tok.device) if logits else None
+        mk_prefill(self.model, t, n, seq, pos0, lg, nxt)
+        return nxt, lg
 
     def check(self):
         mk_check(self.model)

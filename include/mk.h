@@ -186,6 +186,26 @@ int mk_generate(mk_model *m, const int32_t *d_tokens0, const int32_t *d_pos0, in
 int mk_generate_noalloc(mk_model *m, const int32_t *d_tokens0, const int32_t *d_pos0, int32_t batch,
                         int32_t n_steps, int32_t *d_out_tokens, float *d_last_logits, void *stream);
 
+/* Prefill: the n_tokens prompt tokens d_tokens (device int32) of sequence
+ * `seq` at positions pos0 .. pos0 + n_tokens - 1, as columns of one graph
+ * step per group of batch_per_launch consecutive tokens (16 on the
+ * matrix-core bodies) instead of one step per token (MPK blog translation,
+ * Figure 1 workload: a prompt then generation; MPK walk-through 3.2: the
+ * prompt is placed in the token buffer before the kernel runs). Every column
+ * runs the whole decoder for its position: the projections and the MLP as
+ * one batched matvec over the columns, attention over the sequence's cached
+ * positions before the group plus the group's own positions up to the
+ * column's (causal), its key and value appended to the sequence's caches.
+ * Writes the greedy next token of every position to d_next[n_tokens] and, if
+ * d_logits != NULL, the fp32 logits of every position to d_logits
+ * [n_tokens, V] (device). Positions below pos0 must hold the sequence's
+ * cache entries already (a previous prefill or decode). Asynchronous on
+ * `stream`; MK_EINVAL for a NULL pointer, seq outside 0..max_batch-1,
+ * n_tokens < 1 or pos0 + n_tokens > max_seq; device errors as for
+ * mk_decode_step. */
+int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t seq, int32_t pos0, float *d_logits,
+               int32_t *d_next, void *stream);
+
 /* Synchronise `stream`, then read and clear the model's device status word.
  * Returns MK_OK, MK_EDEVICE (token or position out of range was seen; the
  * offending task was skipped), or MK_ETIMEOUT (a wait exceeded the watchdog;
