@@ -78,6 +78,51 @@ def recorded_traffic(kernel: str, workload_name: str, steps: int, batch: int):
     return int(v) if v is not None else None
 
 
+def prefill_timing(wl, weights, prompt, ss):
+    """The prompt through mk_prefill on a matrix-core model of the same weights
+    (16 columns per graph step), against the same prompt as one-token
+    megakernel launches on the benchmark's model; each timed after one
+    untimed run, with HIP events on the launch stream. The prefill's tokens
+    are checked against the one-token launches' (same greedy choice at every
+    position)."""
+    import torch
+    import decode_persistent_megakernel_amd as mk
+    from decode_persistent_megakernel_amd import MK_MODE_MEGAKERNEL, mk_decode_step
+    from decode_persistent_megakernel_amd.session import Session
+    P = len(prompt)
+    o = mk.GraphOpts()
+    o.use_mfma = 2
+    pf = Session(wl.shape, weights, 16, P + 8, o)
+    stream = torch.cuda.current_stream()
+    toks = [int(t) for t in prompt]
+    pf.prefill(toks)  # untimed
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    nxt, _ = pf.prefill(toks, logits=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pf.check()
+    us_pre = e0.elapsed_time(e1) * 1e3
+    steps = (P + pf.batch_per_launch - 1) // pf.batch_per_launch
+    pf.close()
+    tok = torch.as_tensor(toks, dtype=torch.int32, device="cuda")
+    pos = torch.arange(P, dtype=torch.int32, device="cuda")
+    out = torch.zeros(P, dtype=torch.int32, device="cuda")
+    for rep in range(2):  # the first run untimed
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for p in range(P):
+            mk_decode_step(ss.model, tok[p:p + 1], pos[p:p + 1], 1, None, out[p:p + 1], MK_MODE_MEGAKERNEL)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ss.check()
+    us_step = e0.elapsed_time(e1) * 1e3
+    agree = int((nxt == out).sum())
+    return {"tokens": P, "us": round(us_pre, 1), "us_per_token": round(us_pre / P, 2), "graph_steps": steps,
+            "stepwise_us": round(us_step, 1), "greedy_tokens_equal_stepwise": agree}
+
+
 def cpu_baseline(wl, weights, seconds: float = 15.0):
     """The float64 oracle as it stands, timed on the host cores: single decode
     steps of the same shape at the prompt's last position (empty cache prefix),
@@ -115,6 +160,9 @@ def main():
     ap.add_argument("--oplaunch-steps", type=int, default=32, help="steps timed for the per-operator baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-prefill timing")
+    ap.add_argument("--use-mfma", type=int, default=0, choices=(0, 1, 2),
+                    help="matvec bodies of the timed model (graph option use_mfma; 0: the default choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (a plain copy of known size, to scale "
                          "hardware byte counters) and exit")
@@ -146,7 +194,10 @@ def main():
     w = workload.make_weights(wl)
     kv = workload.make_prefill(wl)
     log(f"weights generated in {time.time() - t:.1f}s")
-    ss = Session(wl.shape, w, wl.batch, wl.max_seq, kv=kv)
+    import decode_persistent_megakernel_amd as mkp
+    gopts = mkp.GraphOpts()
+    gopts.use_mfma = args.use_mfma
+    ss = Session(wl.shape, w, wl.batch, wl.max_seq, gopts, kv=kv)
     kv = None
     log(f"model loaded: {ss.n_tasks} tasks, {ss.num_cus} CUs, packed weights {ss.packed_bytes / 1e9:.3f} GB, "
         f"register ring {ss.ring_slots} items per stream wave, LDS {ss.lds_bytes} B, {ss.batch_per_launch} sequence(s) per launch")
@@ -225,12 +276,18 @@ def main():
         sys.exit(3)
     log(f"timed launch checked: {Kb} steps x {B} sequence(s) equal the per-operator replay")
 
+    pre = None
+    if wl.kv_prefill == "none" and not args.no_prefill:
+        pre = prefill_timing(wl, w, prompt, ss)
+        log(f"prefill of the {pre['tokens']}-token prompt: {pre['us']:.1f} us as {pre['graph_steps']} graph steps "
+            f"(matrix-core bodies), {pre['stepwise_us']:.1f} us as {pre['tokens']} one-token launches")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, w, args.cpu_seconds)
         log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads")
 
-    kernel = f"mk_persistent_b{min(B, ss.batch_per_launch)}"
+    kernel = "mk_persistent_b16" if ss.opts.use_mfma == 2 else f"mk_persistent_b{min(B, ss.batch_per_launch)}"
     per = "token at batch 1" if B == 1 else f"step at batch {B}"
     rec = {
         "metric": f"decode \u00b5s/{per} + achieved HBM GB/s as % of roofline",
@@ -251,6 +308,7 @@ def main():
         "oplaunch_baseline_us_per_step": round(us_b, 3),
         "timed_launch_checked_steps": Kb,
         "cpu_baseline": cpu,
+        "prefill": pre,
     }
     if B > 1:
         rec["us_per_sequence_token"] = round(us_tok / B, 3)
