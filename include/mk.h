@@ -106,9 +106,17 @@ typedef struct mk_weights {
  * head_dim, K dims not multiples of 8, qk_norm not 0 or 1, ...), MK_ENOMEM. */
 int mk_build_task_graph(const mk_model_desc *desc, const mk_graph_opts *opts, mk_graph **out);
 
-/* Canonical little-endian bytes of the graph (header, tasks, events, queues).
- * Writes at most cap bytes into buf (buf may be NULL with cap 0 to query) and
- * always stores the full length in *len. MK_EINVAL if buf is too small. */
+/* Canonical little-endian bytes of the graph (header, tasks, events, queues):
+ * the compiled form of the task graph that the runtime executes (MPK blog
+ * translation, "MPK compiler" section: the compiler's output is the task graph
+ * the runtime consumes; MPK walk-through 3.2: TaskDesc / EventDesc arrays).
+ * The layout is this library's own, version 4 (magic, version, desc, resolved
+ * options, then each task's type, layer, sequence, kv group, chunk, row range,
+ * dependent and triggering event and compute unit, each event's threshold and
+ * dependents, each unit's queue), so that two builders of the same
+ * specification can be compared byte for byte. Writes at most cap bytes into
+ * buf (buf may be NULL with cap 0 to query) and always stores the full length
+ * in *len. MK_EINVAL if buf is too small or g is NULL. */
 int mk_graph_serialize(const mk_graph *g, uint8_t *buf, size_t cap, size_t *len);
 
 /* Counts and the resolved (default-filled) options of a graph. Any output
@@ -137,7 +145,12 @@ void mk_free_graph(mk_graph *g);
  * units than num_cus, shape outside this build), MK_ENOMEM, MK_EHIP. */
 int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_model **out);
 
-/* One decode step for `batch` (1..max_batch) sequences: feed d_tokens[b] at
+/* One decode step for `batch` (1..max_batch) sequences (MPK walk-through
+ * 3.3.1, the per-step model: embedding, per layer RMSNorm + QKV, attention with
+ * the KV cache, O projection + residual, RMSNorm + gate/up, SiLU, down
+ * projection + residual, final RMSNorm, LM head, argmax; MPK blog translation,
+ * "MPK runtime" section: the step's task graph run by per-unit workers that
+ * wait on and trigger events): feed d_tokens[b] at
  * position d_pos[b], write K/V there, attend over 0..d_pos[b], and write the
  * greedy next token to d_next[b] and (if d_logits != NULL) the fp32 logits to
  * d_logits [batch, V] row-major. All four arrays are device pointers (int32 /
@@ -206,7 +219,11 @@ int mk_generate_noalloc(mk_model *m, const int32_t *d_tokens0, const int32_t *d_
 int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t seq, int32_t pos0, float *d_logits,
                int32_t *d_next, void *stream);
 
-/* Synchronise `stream`, then read and clear the model's device status word.
+/* Synchronise `stream`, then read and clear the model's device status word
+ * (this error reporting is the library's own: argument errors the kernel
+ * sees and its watchdog, which bounds every wait so that a missing event ends
+ * the kernel instead of hanging it, set bits in a device word that this call
+ * reports).
  * Returns MK_OK, MK_EDEVICE (token or position out of range was seen; the
  * offending task was skipped), or MK_ETIMEOUT (a wait exceeded the watchdog;
  * every wave left the kernel). After MK_ETIMEOUT the event counters are reset
