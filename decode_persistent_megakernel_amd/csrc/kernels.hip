@@ -28,7 +28,7 @@
 //
 // mk_oplaunch runs the same roles on a one-task queue per workgroup with no
 // event waits: one launch per operator (the conventional many-kernel engine
-// the pages compare against). mk_pack repacks the weights into units.
+// that the MPK blog translation's introduction and Figure 1 measure against). mk_pack repacks the weights into units.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -160,8 +160,11 @@ int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_mod
  * sequences (sequences never interact), each group's outputs at its own rows.
  * Asynchronous on `stream`;
  * argument errors return synchronously. Device-side errors (token >= V,
- * position >= max_seq, watchdog) are recorded in the model's status word and
- * returned by mk_check or by the next call. */
+ * position >= max_seq, watchdog) are recorded in the model's status word,
+ * which only mk_check reads and reports: a later call still returns MK_OK.
+ * After a watchdog expiry the abort word stays raised until mk_check has
+ * reported it, so launches made in between leave at their first wait and
+ * write no outputs; the call after mk_check resets the counters. */
 int mk_decode_step(mk_model *m, const int32_t *d_tokens, const int32_t *d_pos, int32_t batch,
                    float *d_logits, int32_t *d_next, int32_t mode, void *stream);
 

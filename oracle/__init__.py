@@ -28,6 +28,6 @@ Sources (the pages on compiling LLM decoding into one persistent kernel):
 
 Parity pins for every function live in ``tests/oracle``. Nothing here is
 "parity unpinned" except the greedy token ids / logits at random
-initialisation themselves, which the pages never print (they are fixed only
+initialisation themselves, which none of these sources prints (they are fixed only
 through the invariants the tests check).
 """

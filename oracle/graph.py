@@ -273,7 +273,9 @@ def sha256(gr: Graph) -> str:
 # ----------------------------------------------------------------------------
 
 def check_structure(gr: Graph) -> None:
-    """Raise AssertionError unless the graph keeps the pages' event contract."""
+    """Raise AssertionError unless the graph keeps the event contract of the MPK blog
+    translation's "MPK compiler" section (one dependent and one triggering
+    event per task, threshold = number of triggering tasks)."""
     n = len(gr.tasks)
     producers = [0] * len(gr.events)
     for t in gr.tasks:

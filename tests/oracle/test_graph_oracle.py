@@ -1,6 +1,6 @@
 """Pins for the task-graph oracle.
 
-* The event contract of the pages (one dependent and one triggering event per
+* The event contract (MPK blog translation, "MPK compiler" section: one dependent and one triggering event per
   task, threshold = number of triggering tasks, round-robin queues).
 * Static race check: every conflicting pair of buffer accesses is ordered by
   an event path, and the closing argmax follows every task (so the next step
@@ -46,6 +46,33 @@ def test_structure_full_size(cfg):
     for op in (G.QKV, G.OPROJ, G.GU, G.DOWN, G.LM):
         cus = {t.cu for t in gr.tasks if t.type == op and t.layer in (-1, 0)}
         assert len(cus) == 256, (op, len(cus))
+
+
+def test_attention_placement_spreads_sequences():
+    """The attention operator's rounds over the units are skewed by the chunk
+    count: on the batch-16 8B shape (16 sequences x 8 kv groups x 8 chunks =
+    1024 tasks over 256 units) plain round-robin would give each unit the same
+    sequence in all four rounds (1.73x the mean load on the busiest unit for
+    the seeded ragged context lengths); the skewed rule gives each unit four
+    different sequences, and the busiest unit streams at most 1.3x the mean
+    (1.25x)."""
+    wl = workload.config(4)
+    gr = G.build(G.desc_from_shape(wl.shape, wl.batch, wl.max_seq))
+    N, Nc = gr.opts.num_cus, gr.opts.attn_chunks
+    att = [t for t in gr.tasks if t.type == G.ATT and t.layer == 0]
+    assert len(att) == 4 * N
+    for i, t in enumerate(att):
+        assert t.cu == (i + (i // N) * Nc) % N
+    seqs = [set() for _ in range(N)]
+    for t in att:
+        seqs[t.cu].add(t.b)
+    assert all(len(s) == 4 for s in seqs)
+    lens = workload.kv_lengths(wl)
+    load = np.zeros(N)
+    for t in att:
+        n = int(lens[t.b]) + 1
+        load[t.cu] += (t.chunk + 1) * n // Nc - t.chunk * n // Nc
+    assert load.max() <= 1.3 * load.mean()
 
 
 def test_race_check_catches_a_missing_edge():
