@@ -164,8 +164,8 @@ def main():
     ap.add_argument("--use-mfma", type=int, default=0, choices=(0, 1, 2),
                     help="matvec bodies of the timed model (graph option use_mfma; 0: the default choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only copy MIB MiB device-to-device 3 times (a plain copy of known size, to scale "
-                         "hardware byte counters) and exit")
+                    help="only copy MIB MiB device-to-device 3 times, then sum the same MIB MiB 3 times (a plain "
+                         "copy and a read-only pass of known size, to scale hardware byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -180,7 +180,12 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_dispatch": n}), flush=True)
+        # a read-only pass of the same size (a reduction: loads only), to check
+        # the read counter's factor on a path with no stores
+        for _ in range(3):
+            float(src.sum())
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": n, "read_bytes_per_reduction": n}), flush=True)
         return
     import workload
     from decode_persistent_megakernel_amd import MK_MODE_OPLAUNCH
