@@ -738,21 +738,23 @@ __device__ __forceinline__ void stage_att(const Params& P, const Ctx& cx, const 
     ih[H_NIN] = n_in;
   }
   if (!valid) return;
-  if (prev) {
-    float* kf1 = vf + D + D;  // after the bf16 bits of the new key and value
-    float* vf1 = kf1 + D;
+  // the key and value of position p - 1 (D / 2 <= 64 words each: one per
+  // lane), loaded beside the q|k|v copy so both take one round trip
+  uint32_t kw = 0u, vw = 0u;
+  if (prev && lane < D / 2) {
     const size_t row = ((((size_t)T.layer * P.B + kv_row_b(P, T.b)) * P.Hkv + T.g) * P.S + (p - 1)) * D;
-    const uint32_t* kc = reinterpret_cast<const uint32_t*>(P.kcache + row);
-    const uint32_t* vc = reinterpret_cast<const uint32_t*>(P.vcache + row);
-    for (int w = lane; w < D / 2; w += 64) {
-      const uint32_t kw = ld_coh(kc + w), vw = ld_coh(vc + w);
-      kf1[2 * w] = bf2f(kw & 0xffffu);
-      kf1[2 * w + 1] = bf2f(kw >> 16);
-      vf1[2 * w] = bf2f(vw & 0xffffu);
-      vf1[2 * w + 1] = bf2f(vw >> 16);
-    }
+    kw = ld_coh(reinterpret_cast<const uint32_t*>(P.kcache + row) + lane);
+    vw = ld_coh(reinterpret_cast<const uint32_t*>(P.vcache + row) + lane);
   }
   stage_copy(cx, P.qkv + ((size_t)T.b * P.Hkv + T.g) * GR, raw, GR);
+  if (prev && lane < D / 2) {
+    float* kf1 = vf + D + D;  // after the bf16 bits of the new key and value
+    float* vf1 = kf1 + D;
+    kf1[2 * lane] = bf2f(kw & 0xffffu);
+    kf1[2 * lane + 1] = bf2f(kw >> 16);
+    vf1[2 * lane] = bf2f(vw & 0xffffu);
+    vf1[2 * lane + 1] = bf2f(vw >> 16);
+  }
   if (P.qk_norm) {
     // per-head RMSNorm of the G query heads and the key head, each over D with
     // its [D] gain, before RoPE (the raw q|k rows are contiguous)

@@ -486,7 +486,10 @@ __device__ __forceinline__ void mv_item(const Params& P, Comp& C, Acc<NC>& A, co
 // weight ring: compute the slot's block, then refill the slot). The first
 // kAttRing blocks are loaded before the task is staged (att_prefetch): the
 // step is open by then, since this compute unit's previous task was staged.
-constexpr int kAttRing = 8;
+#ifndef MK_ATT_RING
+#define MK_ATT_RING 8
+#endif
+constexpr int kAttRing = MK_ATT_RING;
 template <int AR>
 __device__ __forceinline__ void att_prefetch(const Params& P, const Ctx& cx, const Piece& pc, u32x4 (&ka)[AR],
                                              u32x4 (&kv)[AR]) {
@@ -527,9 +530,10 @@ __device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C,
     cn = ln;
     base += AR;
   }
-  // the last pass's zero loads: let them land here, so that the weight ring's
-  // waits after this path keep their exact counts
-  wait_all();
+  // The last pass's zero loads are left in flight: waiting for them here would
+  // also wait for every older load, the weight ring's included, and the task
+  // is done without them (the compiler waits before their registers are
+  // reused).
   C.any = pc.n > 0;
 }
 
