@@ -464,10 +464,11 @@ __device__ __forceinline__ bool wait_event(const Params& P, const Ctx& cx, int e
 // DMA `n` floats (coherent) from global src into LDS dst (both 16-byte
 // aligned), in whole 1 KiB pieces: up to 255 floats past n are read (every
 // activation buffer has slack) and written (every LDS region is sized for it).
-__device__ __forceinline__ void stage_copy(const Ctx& cx, const float* src, float* dst, int n) {
+// (wait = false: the copy is left in flight, for a later copy's wait to cover)
+__device__ __forceinline__ void stage_copy(const Ctx& cx, const float* src, float* dst, int n, bool wait = true) {
   const int nl = (n + 255) / 256;
   for (int t = 0; t < nl; ++t) dma16<kAuxCoherent>(src + t * 256 + cx.lane * 4, dst + t * 256);
-  wait_all();
+  if (wait) wait_all();
 }
 
 // Work of a matvec task that does not depend on its event, done while the
@@ -824,13 +825,14 @@ __device__ __forceinline__ void stage_task(const Params& P, const Ctx& cx, const
     case T_COMB: {
       if (T.b >= P.batch) break;
       const size_t head0 = (size_t)T.b * P.Hq + (size_t)T.g * P.G;
-      stage_copy(cx, P.part_ml + head0 * P.Nc * 2, data, P.G * P.Nc * 2);
+      // both copies in one round trip
+      stage_copy(cx, P.part_ml + head0 * P.Nc * 2, data, P.G * P.Nc * 2, false);
       stage_copy(cx, P.part_acc + head0 * P.Nc * P.D, data + second_off(P.G * P.Nc * 2), P.G * P.Nc * P.D);
       break;
     }
     case T_ARGMAX: {
       if (T.b >= P.batch) break;
-      stage_copy(cx, P.lm_val + (size_t)T.b * P.n_lm, data, P.n_lm);
+      stage_copy(cx, P.lm_val + (size_t)T.b * P.n_lm, data, P.n_lm, false);
       stage_copy(cx, reinterpret_cast<const float*>(P.lm_idx + (size_t)T.b * P.n_lm), data + second_off(P.n_lm),
                  P.n_lm);
       break;

@@ -127,3 +127,37 @@ def test_1b_prefill_prompt():
         assert kv_close(got, np.asarray(ref_kv), what=f"1b prefill {name} cache")
     ss.check()
     ss.close()
+
+
+@pytest.mark.parametrize("use_mfma", [1, 2])
+def test_prefill_to_the_last_position(use_mfma):
+    """The cache filled to its end: a 60-token prompt prefilled into a
+    64-position cache, then greedy decode steps at positions 60..63 (the last
+    one the cache holds) in one mk_generate launch; their logits against
+    forward_full over the 64 tokens (the oracle's greedy continuation is fed
+    teacher-forced through stepwise decoding, so both sides see the same
+    tokens), on the vector bodies and the matrix cores."""
+    import decode_persistent_megakernel_amd as mk
+    cfg = 7
+    o = mk.GraphOpts()
+    o.use_mfma = use_mfma
+    ss = session(cfg, "random", opts=o, max_batch=16 if use_mfma == 2 else 4, max_seq=64)
+    om = oracle_model(cfg, "random")
+    toks = prompt_tokens(cfg, 60, 400)
+    progress(f"[prefill to the end] use_mfma {use_mfma}")
+    nxt, lg = ss.prefill(toks, seq=0, pos0=0)
+    ref, _, _ = om.forward_full(toks)
+    check_logits(lg[59].double().cpu().numpy(), ref[59], "prefill pos 59")
+    # four steps at positions 60..63, each fed the oracle's greedy token
+    seq = list(toks)
+    for p in range(60, 64):
+        t = int(np.argmax(ref[-1]))
+        seq.append(t)
+        _, g = ss.decode_step([t], [p])
+        ref, _, _ = om.forward_full(seq)
+        check_logits(g[0].double().cpu().numpy(), ref[-1], f"decode at position {p}")
+    # position 64 is past the cache: reported, not written
+    _, _ = ss.decode_step([0], [64], logits=False)
+    with pytest.raises(mk.MKError):
+        ss.check()
+    ss.close()
