@@ -540,15 +540,20 @@ __device__ __forceinline__ void stage_matvec(const Params& P, const Ctx& cx, con
   } else {  // O (attention output) or D (SiLU*up), plus the residual rows
     const float* src = T.type == T_O ? P.attn : P.mlp;
     const int R = T.row1 - T.row0;
+    // every column's input copy and residual rows in one round trip
+    float rv[NC];
+    const int nl = (K + 255) / 256;
+#pragma unroll
     for (int c = 0; c < ncols; ++c) {
-      // the residual rows travel with the input copy: one round trip
-      float rv = 0.f;
-      if (lane < R) rv = ld_coh(P.x + (size_t)c * P.H + T.row0 + lane);
-      const int nl = (K + 255) / 256;
+      rv[c] = 0.f;
+      if (lane < R) rv[c] = ld_coh(P.x + (size_t)c * P.H + T.row0 + lane);
       for (int t = 0; t < nl; ++t) dma16<kAuxCoherent>(src + (size_t)c * K + t * 256 + lane * 4, in + (size_t)c * kp + t * 256);
-      wait_all();
+    }
+    wait_all();
+#pragma unroll
+    for (int c = 0; c < ncols; ++c) {
       for (int k = K + lane; k < kp; k += 64) in[(size_t)c * kp + k] = 0.f;
-      if (lane < R) res[(size_t)c * P.res_stride + lane] = rv;
+      if (lane < R) res[(size_t)c * P.res_stride + lane] = rv[c];
       for (int r = 64 + lane; r < R; r += 64) res[(size_t)c * P.res_stride + r] = ld_coh(P.x + (size_t)c * P.H + T.row0 + r);
     }
   }
