@@ -114,6 +114,8 @@ def test_serialize_small_buffer_and_nulls():
     assert L.mk_decode_step(None, None, None, 1, None, None, 0, None) == mk.MK_EINVAL
     assert L.mk_generate(None, None, None, 1, 1, None, None, None) == mk.MK_EINVAL
     assert L.mk_generate_noalloc(None, None, None, 1, 1, None, None, None) == mk.MK_EINVAL
+    assert L.mk_prefill(None, None, 1, 0, 0, None, None, None) == mk.MK_EINVAL
+    assert b"NULL model" in L.mk_last_error()
     assert L.mk_check(None, None) == mk.MK_EINVAL
     mk.mk_free_graph(g)
 
