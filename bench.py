@@ -17,8 +17,8 @@ equal the token the timed launch chose at that step (the two paths are
 bit-identical by construction); any difference exits with status 3 before the
 JSON line is printed.
 
-Prints one JSON line (rank 0). `--gpus N` with N > 1 exits: this build runs on
-one GPU.
+Prints one JSON line (rank 0). `--gpus N` with N > 1 exits: the library runs
+on one GPU.
 """
 from __future__ import annotations
 
@@ -168,8 +168,8 @@ def main():
                          "copy and a read-only pass of known size, to scale hardware byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sharding across GPUs is described in the design record, not built", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is a design, not built", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -4,8 +4,10 @@
 // The operator order is the pages' wiring of one step (MPK walk-through
 // section 3.3.1, build_mirage_graph; Hazy megakernel summary, fused
 // instruction list). The partition, event and byte-format rules are this
-// project's specification (design record, section 1); oracle/graph.py
-// implements the same specification separately and the tests compare bytes.
+// project's own specification, written out in this file (defaults in the
+// resolve step, tasks and events in creation order, bytes in serialize);
+// oracle/graph.py implements the same specification separately and the
+// tests compare bytes.
 #include "graph.h"
 
 #include <algorithm>

@@ -31,7 +31,7 @@ extern "C" {
 #define MK_ENOMEM       (-2)   /* device or host allocation failed */
 #define MK_EHIP         (-3)   /* a HIP runtime call failed */
 #define MK_ETIMEOUT     (-4)   /* device watchdog expired inside the kernel */
-#define MK_EUNSUPPORTED (-5)   /* shape/option/device this build cannot run */
+#define MK_EUNSUPPORTED (-5)   /* shape/option/device the library does not support */
 #define MK_EDEVICE      (-6)   /* device-side argument error (token or position out of range) */
 
 /* decode modes for mk_decode_step */
@@ -56,9 +56,15 @@ typedef struct mk_model_desc {
 } mk_model_desc;
 
 /* Task-graph knobs (MPK walk-through 3.3.1: per-layer grid sizes and worker
- * counts). 0 = default; the defaults and the partition rules are a pure
- * function of (desc, num_cus) and are spelled out with the canonical byte
- * format in the design record. */
+ * counts). 0 = default; the defaults are a pure function of the desc:
+ * num_cus 256, row_block 4, use_mfma 2 when a launch holds more than 4
+ * sequences (min(max_batch, 16) > 4) and hidden, n_q_heads * head_dim and ffn
+ * are multiples of 64 of at least 256, else 1; qkv_tasks_per_group
+ * ceil(num_cus / n_kv_heads); o_tasks = gu_tasks = d_tasks = num_cus; lm_tasks
+ * num_cus (use_mfma 1) or max(num_cus, ceil(vocab / 128)) (use_mfma 2);
+ * attn_chunks max(1, min(num_cus / (min(max_batch, 4) * n_kv_heads),
+ * max_seq / 1024)). Every task count is then capped at the number of
+ * row_block-row blocks of its operator's rows. */
 typedef struct mk_graph_opts {
     int32_t num_cus;             /* compute units = workgroups of the persistent kernel */
     int32_t qkv_tasks_per_group; /* QKV tasks per kv head group */
@@ -142,7 +148,7 @@ void mk_free_graph(mk_graph *g);
  * (mk_model_info's n_tasks counts that graph's tasks).
  * Errors: MK_EINVAL (NULL pointer, a NULL q_norm/k_norm with qk_norm = 1),
  * MK_EUNSUPPORTED (fewer resident compute
- * units than num_cus, shape outside this build), MK_ENOMEM, MK_EHIP. */
+ * units than num_cus, shape the library does not support), MK_ENOMEM, MK_EHIP. */
 int mk_load_weights(const mk_graph *g, const mk_weights *w, void *stream, mk_model **out);
 
 /* One decode step for `batch` (1..max_batch) sequences (MPK walk-through
