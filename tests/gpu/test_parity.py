@@ -385,7 +385,7 @@ def test_1b_full_size_sampled():
 @pytest.mark.slow
 def test_8b_full_size_sampled():
     """Llama-3-8B shape (hidden 4096, head dim 128, untied LM head, the
-    smallest ring depth the LDS leaves room for): the first 8 prompt tokens."""
+    largest LDS staging of the vector bodies): the first 8 prompt tokens."""
     full_size_sampled(2, 8, "8B")
 
 
