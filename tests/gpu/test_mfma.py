@@ -125,3 +125,41 @@ def test_mfma_graph_options(knobs):
     progress(f"[mfma options] {knobs}: {ss.n_tasks} tasks")
     ss.check()
     ss.close()
+
+
+def test_mfma_batch_above_one_launch():
+    """max_batch 21 on the matrix cores: a launch takes 16 sequences, so a
+    call of 21 runs as groups of 16 and 5 (the second group's KV rows start at
+    sequence 16). Ragged positions; every sequence's logits against the oracle;
+    megakernel and per-operator launches bit-identical; mk_generate over the
+    groups equal to stepwise decoding."""
+    wl = workload.config(7)
+    a = session(7, "random", opts=mf_opts(), max_batch=21, max_seq=40)
+    b = session(7, "random", opts=mf_opts(), max_batch=21, max_seq=40)
+    assert a.batch_per_launch == 16
+    om = oracle_model(7, "random")
+    st = om.new_state(21, 40)
+    toks = workload.make_prompt(wl)
+    for k in range(3):
+        tk = [int(toks[s % 16, k]) for s in range(21)]
+        ps = [k + (s % 7) for s in range(21)]
+        na, la = a.decode_step(tk, ps, mode=0)
+        nb_, lb = b.decode_step(tk, ps, mode=1)
+        assert torch.equal(la, lb) and torch.equal(na, nb_), k
+        ref = om.decode_step(st, tk, ps)
+        g = la.double().cpu().numpy()
+        for s in range(21):
+            check_logits(g[s], ref[s], f"step {k} seq {s}")
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+    t0 = [int(toks[s % 16, 3]) for s in range(21)]
+    p0 = [3 + (s % 7) for s in range(21)]
+    out = a.generate(t0, p0, 3)
+    tk = list(t0)
+    for k in range(3):
+        nxt, _ = b.decode_step(tk, [p + k for p in p0], mode=1)
+        tk = [int(x) for x in nxt.cpu().tolist()]
+        assert tk == out[k].cpu().tolist(), k
+    a.check()
+    b.check()
+    a.close()
+    b.close()
