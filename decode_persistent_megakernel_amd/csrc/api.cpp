@@ -203,7 +203,11 @@ static int load_model(const mk::Graph& gsrc, int32_t cache_batch, const mk_weigh
     else {  // rows of the row blocks each stream wave's piece touches (its partial sums)
       const int items = x.n_units / 2;
       for (int w = 0; w < kStreams; ++w) {
-        const int i0 = int(int64_t(items) * w / kStreams), i1 = int(int64_t(items) * (w + 1) / kStreams);
+        // the stream waves' cut of the items (the kernels' piece()): weighted
+        // on the vector bodies, equal quarters on the matrix cores
+        static const int64_t cum[kStreams + 1] = {0, 67, 134, 195, 256};
+        const int i0 = mf ? int(int64_t(items) * w / kStreams) : int((int64_t(items) * cum[w]) >> 8);
+        const int i1 = mf ? int(int64_t(items) * (w + 1) / kStreams) : int((int64_t(items) * cum[w + 1]) >> 8);
         if (i1 <= i0) continue;
         const int touched = (2 * i1 - 1) / KB - (2 * i0) / KB + 1;
         wave_vrows = std::max(wave_vrows, touched * kUnitRows);

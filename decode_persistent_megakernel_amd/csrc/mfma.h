@@ -49,7 +49,7 @@ __device__ __forceinline__ XPiece make_xpiece(const Params& P, const Ctx& cx, in
   xp.KB2 = K / kMfmaItemCols;
   const int items = (int)rfl((uint32_t)R.n_units) / 2;
   int i0, i1;
-  piece(items, s, i0, i1);
+  piece<false>(items, s, i0, i1);
   xp.n = i1 - i0;
   xp.col0 = i0 % xp.KB2;
   const bool normed = is_normed(type);
@@ -107,7 +107,7 @@ struct PieceM {
 };
 __device__ __forceinline__ PieceM make_piece_m(const Params& P, const Ctx& cx, int s, int r) {
   PieceM m;
-  m.pc = make_piece(P, cx, s, r);
+  m.pc = make_piece<false>(P, cx, s, r);
   m.cm = 0;
   const StreamRec R = cx.recs[r];
   if ((rfl(R.tsbg) & 15) == T_ATT) return m;
@@ -115,7 +115,7 @@ __device__ __forceinline__ PieceM make_piece_m(const Params& P, const Ctx& cx, i
   if (cm == 0) return m;
   const int ncol = (int)rfl((uint32_t)R.n_units) / 16;  // column pairs (8 items, 16 units each)
   int c0, c1;
-  piece(ncol, s, c0, c1);
+  piece<false>(ncol, s, c0, c1);
   const int64_t woff =
       (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
   m.pc.n = 8 * (c1 - c0);
@@ -240,7 +240,7 @@ __device__ __forceinline__ bool comp_start_m(const Params& P, const Ctx& cx, int
     const int lpp = P.D / 8, ppi = 64 / lpp;
     const int nb = (flags & 1) && C.end > C.lo ? (C.end - C.lo + ppi - 1) / ppi : 0;
     int j1;
-    piece(nb, s, C.u0, j1);
+    piece<false>(nb, s, C.u0, j1);
     C.natt = j1 - C.u0;
     const uint32_t lc = rfl(R.lc);
     C.layer = lc & 0xffff;
@@ -260,7 +260,7 @@ __device__ __forceinline__ bool comp_start_m(const Params& P, const Ctx& cx, int
     C.cm = (int)(rfl(R.lc) >> 16);
     if (C.cm) {  // column-major: this wave's column pairs, all the task's row blocks
       int c0, c1;
-      piece(C.xp.KB2, s, c0, c1);
+      piece<false>(C.xp.KB2, s, c0, c1);
       C.col = c0;
       C.c1 = c1;
       C.rb0 = 0;
@@ -269,7 +269,7 @@ __device__ __forceinline__ bool comp_start_m(const Params& P, const Ctx& cx, int
     } else {
       const int items = (int)rfl((uint32_t)R.n_units) / 2;
       int i0, i1;
-      piece(items, s, i0, i1);
+      piece<false>(items, s, i0, i1);
       C.rb = i0 / C.xp.KB2;
       C.rb0 = C.rb;
       C.kc = C.xp.col0;
@@ -315,7 +315,7 @@ __device__ __forceinline__ void att_run_m(const Params& P, const Ctx& cx, CompM&
   A.lo = C.lo;
   A.end = C.end;
   A.u0 = C.u0;
-  att_run<AR, true>(P, cx, A, S, pc, ka, kv);
+  att_run<AR>(P, cx, A, S, pc, ka, kv);
 
   C.any = A.any;
 }
@@ -401,7 +401,7 @@ __device__ __forceinline__ void run_stream_m16(const Params& P0, const Ctx& cx, 
           // an attention task: its first KV blocks load while it is staged
           AttState S;
           u32x4 ka[kAttRingM], kv[kAttRingM];
-          const Piece kpc = kv_piece_of(P, cx, s, r, st);
+          const Piece kpc = kv_piece_of<false>(P, cx, s, r, st);
           att_prefetch(P, cx, kpc, ka, kv);
           if (!comp_start_m<PROF>(P, cx, s, C, acc, S, wt, prof)) return;
           const uint32_t t_att = prof ? rfl((uint32_t)wall_clock64()) : 0u;

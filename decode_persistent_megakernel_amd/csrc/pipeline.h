@@ -37,10 +37,25 @@ constexpr int kItemBytes = 2 * kUnitBytes;
 __device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// [a0, a1): piece s of n things cut into kStreams nearly equal contiguous pieces
+// [a0, a1): piece s of n things cut into kStreams contiguous pieces. The
+// vector bodies (W) give stream waves 0 and 1 (waves 2 and 3, a SIMD each)
+// 67/256 of the things each and stream waves 2 and 3 (waves 4 and 5, which
+// share their SIMDs with the stager and the retirer) 61/256 each: measured on
+// the 1B shape, equal quarters left waves 4 and 5 finishing 0.1-0.4 us after
+// the others on every matvec (879.5 -> 868.4 us/token with the weighted cut).
+// The matrix-core bodies keep equal quarters (the weighted cut measured
+// slower there). The host computes the same cut (api.cpp).
+template <bool W = true>
 __device__ __forceinline__ void piece(int n, int s, int& a0, int& a1) {
-  a0 = (int)((uint32_t)n * (uint32_t)s / kStreams);
-  a1 = (int)((uint32_t)n * (uint32_t)(s + 1) / kStreams);
+  if constexpr (W) {
+    const uint32_t c0 = s == 0 ? 0u : s == 1 ? 67u : s == 2 ? 134u : 195u;
+    const uint32_t c1 = s == 0 ? 67u : s == 1 ? 134u : s == 2 ? 195u : 256u;
+    a0 = (int)(((uint32_t)n * c0) >> 8);
+    a1 = (int)(((uint32_t)n * c1) >> 8);
+  } else {
+    a0 = (int)((uint32_t)n * (uint32_t)s / kStreams);
+    a1 = (int)((uint32_t)n * (uint32_t)(s + 1) / kStreams);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -64,6 +79,7 @@ __device__ __forceinline__ rsrc_t zero_rsrc(const Params& P, const Ctx& cx) {
 }
 
 // Wave s's piece of a matvec record (an attention record has no ring items).
+template <bool W = true>
 __device__ __forceinline__ Piece make_piece(const Params& P, const Ctx& cx, int s, int r) {
   Piece pc;
   pc.n = 0;
@@ -78,7 +94,7 @@ __device__ __forceinline__ Piece make_piece(const Params& P, const Ctx& cx, int 
   if ((tsbg & 15) == T_ATT) return pc;
   const int items = (int)rfl((uint32_t)R.n_units) / 2;
   int i0, i1;
-  piece(items, s, i0, i1);
+  piece<W>(items, s, i0, i1);
   pc.n = i1 - i0;
   const int64_t woff =
       (int64_t)(((uint64_t)rfl((uint32_t)((uint64_t)R.w_off >> 32)) << 32) | rfl((uint32_t)R.w_off));
@@ -107,6 +123,7 @@ __device__ __forceinline__ Piece make_kv_piece(const Params& P, const Ctx& cx, i
 
 // The same piece computed from an attention record and the call's positions,
 // before the task is staged (the staged header gives the same bounds).
+template <bool W = true>
 __device__ __forceinline__ Piece kv_piece_of(const Params& P, const Ctx& cx, int s, int r, int step) {
   const StreamRec R = cx.recs[r];
   const uint32_t tsbg = rfl(R.tsbg), lc = rfl(R.lc);
@@ -116,7 +133,7 @@ __device__ __forceinline__ Piece kv_piece_of(const Params& P, const Ctx& cx, int
   if (pos >= 0 && pos < P.S) {
     att_stream_range(P, chunk, pos, lo, end);
     const int ppi = 64 / (P.D / 8);
-    piece(end > lo ? (end - lo + ppi - 1) / ppi : 0, s, j0, j1);
+    piece<W>(end > lo ? (end - lo + ppi - 1) / ppi : 0, s, j0, j1);
   }
   return make_kv_piece(P, cx, layer, b < P.batch ? kv_row_b(P, b) : 0, g, lo, end, j0, j1 - j0);
 }
@@ -279,8 +296,8 @@ __device__ __forceinline__ float across_groups(float v, bool l16) {
 // scale * log2(e)), so the exponentials are the hardware's exp2. The heads'
 // dot products and lane-group sums are computed side by side, so the
 // cross-lane steps of different heads overlap. q: this lane's 8 dims of each
-// head's scaled query (QREG: registers for the whole task; else read from the
-// staging slot here, once per pair).
+// head's scaled query, read from the staging slot once per task (load_q) and
+// held in registers.
 __device__ __forceinline__ void load_q(const Params& P, const AttState& S, float (&q)[kMaxG][8]) {
 #pragma unroll
   for (int h = 0; h < kMaxG; ++h) {
@@ -290,13 +307,9 @@ __device__ __forceinline__ void load_q(const Params& P, const AttState& S, float
     q[h][4] = b.x; q[h][5] = b.y; q[h][6] = b.z; q[h][7] = b.w;
   }
 }
-template <bool QREG>
-__device__ __forceinline__ void att_pair(const Params& P, AttState& S, const float (&qr)[kMaxG][8], const u32x4 k0,
+__device__ __forceinline__ void att_pair(const Params& P, AttState& S, const float (&q)[kMaxG][8], const u32x4 k0,
                                          const u32x4 v0, const u32x4 k1, const u32x4 v1, bool valid0, bool valid1,
                                          bool l16) {
-  float ql[kMaxG][8];
-  if constexpr (!QREG) load_q(P, S, ql);
-  const float(&q)[kMaxG][8] = QREG ? qr : ql;
   float kf0[8], kf1[8];
   unpack8(k0, kf0);
   unpack8(k1, kf1);
@@ -499,15 +512,15 @@ __device__ __forceinline__ void att_prefetch(const Params& P, const Ctx& cx, con
     __builtin_amdgcn_sched_barrier(0);
   }
 }
-template <int AR, bool QREG = true>
+template <int AR>
 __device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C, AttState& S, const Piece& pc,
                                         u32x4 (&ka)[AR], u32x4 (&kv)[AR]) {
   static_assert(AR % 2 == 0, "attention items are computed in pairs");
   const int lane = cx.lane, lpp = P.D / 8, ppi = 64 / lpp;
   const bool l16 = lpp == 16;
-  // this lane's 8 dims of each head's scaled query, for the whole task (QREG)
+  // this lane's 8 dims of each head's scaled query, for the whole task
   float q[kMaxG][8];
-  if constexpr (QREG) load_q(P, S, q);
+  load_q(P, S, q);
   int cn = min(AR, pc.n), cbase = 0, base = AR;  // blocks computed in this pass, their first; next to load
   for (;;) {
     cn = (int)rfl((uint32_t)cn);
@@ -518,7 +531,7 @@ __device__ __forceinline__ void att_run(const Params& P, const Ctx& cx, Comp& C,
       asm volatile("" : : "v"(ka[j]), "v"(kv[j]), "v"(ka[j + 1]), "v"(kv[j + 1]));
       if (j < cn) {
         const int pos0 = C.lo + (C.u0 + cbase + j) * ppi + lane / lpp;
-        att_pair<QREG>(P, S, q, ka[j], kv[j], ka[j + 1], kv[j + 1], pos0 < C.end, j + 1 < cn && pos0 + ppi < C.end,
+        att_pair(P, S, q, ka[j], kv[j], ka[j + 1], kv[j + 1], pos0 < C.end, j + 1 < cn && pos0 + ppi < C.end,
                        l16);
       }
       load_item(P, cx, pc, base + j, j < ln, ka[j], kv[j]);
