@@ -110,11 +110,17 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   const int32_t e_tok = bld.new_event(B);
   const int32_t e_emb = bld.new_event(B);
   const int32_t L = d.n_layers;
-  std::vector<int32_t> e_qkv(size_t(L) * Hkv), e_att(size_t(L) * Hkv * B), e_comb(L), e_o(L), e_gu(L), e_d(L);
+  // With one chunk per (sequence, kv group) each attention task merges its
+  // own result: no per-chunk events, no COMB tasks, and the attention tasks
+  // count the layer's merged event directly (one hand-off fewer per layer).
+  const bool fold = Nc == 1;
+  std::vector<int32_t> e_qkv(size_t(L) * Hkv), e_att(fold ? 0 : size_t(L) * Hkv * B), e_comb(L), e_o(L), e_gu(L),
+      e_d(L);
   for (int32_t l = 0; l < L; ++l) {
     for (int32_t gi = 0; gi < Hkv; ++gi) e_qkv[size_t(l) * Hkv + gi] = bld.new_event(r.qkv_tasks_per_group);
-    for (int32_t gi = 0; gi < Hkv; ++gi)
-      for (int32_t b = 0; b < B; ++b) e_att[(size_t(l) * Hkv + gi) * B + b] = bld.new_event(Nc);
+    if (!fold)
+      for (int32_t gi = 0; gi < Hkv; ++gi)
+        for (int32_t b = 0; b < B; ++b) e_att[(size_t(l) * Hkv + gi) * B + b] = bld.new_event(Nc);
     e_comb[l] = bld.new_event(Hkv * B);
     e_o[l] = bld.new_event(r.o_tasks);
     e_gu[l] = bld.new_event(r.gu_tasks);
@@ -152,12 +158,13 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
           for (int32_t c = 0; c < Nc; ++c) {
             Task t = blank(T_ATT);
             t.layer = l; t.g = gi; t.b = b; t.chunk = c;
-            t.dep = e_qkv[size_t(l) * Hkv + gi]; t.trig = e_att[(size_t(l) * Hkv + gi) * B + b];
+            t.dep = e_qkv[size_t(l) * Hkv + gi];
+            t.trig = fold ? e_comb[l] : e_att[(size_t(l) * Hkv + gi) * B + b];
             op.push_back(t);
           }
       bld.add_op(std::move(op), Nc);
     }
-    {
+    if (!fold) {
       std::vector<Task> op;
       for (int32_t gi = 0; gi < Hkv; ++gi)
         for (int32_t b = 0; b < B; ++b) {
@@ -224,7 +231,8 @@ std::vector<uint8_t> serialize(const Graph& g) {
   Writer w;
   const char magic[8] = {'M', 'K', 'G', 'R', 'A', 'P', 'H', '1'};
   w.b.insert(w.b.end(), magic, magic + 8);
-  w.u32(4);  // version 4: qk_norm in the desc, use_mfma in the options, skewed attention placement
+  w.u32(5);  // version 5: qk_norm in the desc, use_mfma in the options, skewed attention placement,
+            // single-chunk attention merged in its own task
   const mk_model_desc& d = g.desc;
   for (int32_t v : {d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab,
                     d.tied_embeddings, d.max_batch, d.max_seq})

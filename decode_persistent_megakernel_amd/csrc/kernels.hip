@@ -1124,6 +1124,7 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
   // owns four dims of one head
   const size_t chunk0 = ((size_t)T.b * P.Hq + (size_t)T.g * G) * P.Nc + T.chunk;  // head 0 of the group
   const rsrc_t racc = make_rsrc(P.part_acc, 0xffffffffu);
+  const rsrc_t rattn = make_rsrc(P.attn + (size_t)T.b * P.Hq * D + (size_t)T.g * G * D, (uint32_t)(G * D) * 4);
   for (int qd = lane; qd < G * D4; qd += 64) {
     const int h = qd / D4, d = (qd - h * D4) * 4;
     float s_new = sp[0], s_prev = sq[0];
@@ -1173,8 +1174,17 @@ __device__ __forceinline__ void retire_att(const Params& P, const Ctx& cx, const
       a.x = fmaf(e, vf[d], a.x); a.y = fmaf(e, vf[d + 1], a.y);
       a.z = fmaf(e, vf[d + 2], a.z); a.w = fmaf(e, vf[d + 3], a.w);
     }
-    const size_t ci = chunk0 + (size_t)h * P.Nc;
     u32x4 v;
+    if (P.Nc == 1) {
+      // the only chunk: this task is the merge (the graph has no COMB task),
+      // so it stores the normalised output where the O projection reads it
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      v.x = __float_as_uint(inv * a.x); v.y = __float_as_uint(inv * a.y);
+      v.z = __float_as_uint(inv * a.z); v.w = __float_as_uint(inv * a.w);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rattn, (uint32_t)((h * D + d) * 4), 0, kAuxCoherent);
+      continue;
+    }
+    const size_t ci = chunk0 + (size_t)h * P.Nc;
     v.x = __float_as_uint(a.x); v.y = __float_as_uint(a.y); v.z = __float_as_uint(a.z); v.w = __float_as_uint(a.w);
     __builtin_amdgcn_raw_buffer_store_b128(v, racc, (uint32_t)((ci * D + d) * 4), 0, kAuxCoherent);
     if (d == 0) {

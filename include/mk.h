@@ -116,7 +116,7 @@ int mk_build_task_graph(const mk_model_desc *desc, const mk_graph_opts *opts, mk
  * the compiled form of the task graph that the runtime executes (MPK blog
  * translation, "MPK compiler" section: the compiler's output is the task graph
  * the runtime consumes; MPK walk-through 3.2: TaskDesc / EventDesc arrays).
- * The layout is this library's own, version 4 (magic, version, desc, resolved
+ * The layout is this library's own, version 5 (magic, version, desc, resolved
  * options, then each task's type, layer, sequence, kv group, chunk, row range,
  * dependent and triggering event and compute unit, each event's threshold and
  * dependents, each unit's queue), so that two builders of the same

@@ -20,7 +20,9 @@ The operator order of one step is the pages' wiring (MPK walk-through section
 3.3.1): embed, then per layer [RMSNorm+QKV, attention, O-proj+residual,
 RMSNorm+gate/up, down+residual], final RMSNorm+LM head, argmax. Attention is
 split over position chunks and merged by a reduction task (Hazy summary:
-attention as "matmul + reduction").
+attention as "matmul + reduction"); with a single chunk the attention task
+normalises its own result and counts the merged event itself, so the graph
+has no reduction tasks (see ``merge_mode``).
 
 The layout of the task list, the event list, the partition rules and the
 canonical byte format below are this project's specification; the C++ host
@@ -52,7 +54,9 @@ GROUP_COLS = 4
 MFMA_COLS = 16
 
 MAGIC = b"MKGRAPH1"
-VERSION = 4
+VERSION = 5
+# where a layer's attention chunks are merged
+MERGE_IN_ATT, MERGE_TASKS = range(2)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -173,6 +177,13 @@ def split_rows(rows: int, tasks: int, rb: int) -> List[Tuple[int, int]]:
     return out
 
 
+def merge_mode(d: Desc, o: Opts) -> int:
+    """Where the attention chunks of a layer are merged (``o`` resolved): in
+    the attention task itself when there is one chunk, else by one merge
+    (COMB) task per (kv group, sequence)."""
+    return MERGE_IN_ATT if o.attn_chunks == 1 else MERGE_TASKS
+
+
 def build(d: Desc, opts: Opts = Opts()) -> Graph:
     o = resolve(d, opts)
     B, L, Hkv = d.max_batch, d.n_layers, d.n_kv_heads
@@ -189,9 +200,14 @@ def build(d: Desc, opts: Opts = Opts()) -> Graph:
     e_tok = new_event(B)
     e_emb = new_event(B)
     e_qkv, e_att, e_comb, e_o, e_gu, e_d = [], [], [], [], [], []
+    # one chunk per (sequence, kv group): the attention task merges its own
+    # result, so there are no per-chunk events and no COMB tasks, and the
+    # attention tasks count the merged event directly
+    fold = merge_mode(d, o) == MERGE_IN_ATT
     for l in range(L):
         e_qkv.append([new_event(o.qkv_tasks_per_group) for g in range(Hkv)])
-        e_att.append([[new_event(Nc) for b in range(B)] for g in range(Hkv)])
+        if not fold:
+            e_att.append([[new_event(Nc) for b in range(B)] for g in range(Hkv)])
         e_comb.append(new_event(Hkv * B))
         e_o.append(new_event(o.o_tasks))
         e_gu.append(new_event(o.gu_tasks))
@@ -213,10 +229,12 @@ def build(d: Desc, opts: Opts = Opts()) -> Graph:
         op([Task(QKV, layer=l, g=g, row0=r0, row1=r1, dep=dep, trig=e_qkv[l][g])
             for g in range(Hkv)
             for r0, r1 in split_rows(grp_rows, o.qkv_tasks_per_group, o.row_block)])
-        op([Task(ATT, layer=l, g=g, b=b, chunk=c, dep=e_qkv[l][g], trig=e_att[l][g][b])
+        op([Task(ATT, layer=l, g=g, b=b, chunk=c, dep=e_qkv[l][g],
+                 trig=e_comb[l] if fold else e_att[l][g][b])
             for g in range(Hkv) for b in range(B) for c in range(Nc)], skew=Nc)
-        op([Task(COMB, layer=l, g=g, b=b, dep=e_att[l][g][b], trig=e_comb[l])
-            for g in range(Hkv) for b in range(B)])
+        if not fold:
+            op([Task(COMB, layer=l, g=g, b=b, dep=e_att[l][g][b], trig=e_comb[l])
+                for g in range(Hkv) for b in range(B)])
         op([Task(OPROJ, layer=l, row0=r0, row1=r1, dep=e_comb[l], trig=e_o[l])
             for r0, r1 in split_rows(d.hidden, o.o_tasks, o.row_block)])
         op([Task(GU, layer=l, row0=r0, row1=r1, dep=e_o[l], trig=e_gu[l])
@@ -350,9 +368,13 @@ def accesses(gr: Graph, i: int) -> List[Tuple[str, str, int, int]]:
         acc += [("r", "qkv", base, base + GR), ("r", "kvpast", kvb, kvb + 1)]
         if t.chunk == Nc - 1:
             acc += [("w", "kvcur", kvb, kvb + 1), ("r", "kvcur", kvb, kvb + 1)]
-        for h in range(t.g * G, (t.g + 1) * G):
-            p = ((t.b * d.n_q_heads + h) * Nc + t.chunk)
-            acc.append(("w", "part", p, p + 1))
+        if merge_mode(d, o) == MERGE_IN_ATT:     # merged in the task itself
+            a = t.b * d.n_q_heads * D + t.g * G * D
+            acc.append(("w", "attn", a, a + G * D))
+        else:
+            for h in range(t.g * G, (t.g + 1) * G):
+                p = ((t.b * d.n_q_heads + h) * Nc + t.chunk)
+                acc.append(("w", "part", p, p + 1))
     elif t.type == COMB:
         for h in range(t.g * G, (t.g + 1) * G):
             p = (t.b * d.n_q_heads + h) * Nc
@@ -442,6 +464,7 @@ def replay(gr: Graph, m: Model, st: State, tokens: Sequence[int], pos: Sequence[
     G = Hq // Hkv
     GR = (G + 2) * D
     Nc = o.attn_chunks
+    mode = merge_mode(d, o)
     x = np.zeros((B, H))
     qkv = np.zeros((B, Hkv, GR))
     pm = np.full((B, Hq, Nc), -np.inf)
@@ -459,6 +482,15 @@ def replay(gr: Graph, m: Model, st: State, tokens: Sequence[int], pos: Sequence[
         return np.concatenate([m.W(f"l{l}.wq")[g * G * D:(g + 1) * G * D],
                                m.W(f"l{l}.wk")[g * D:(g + 1) * D],
                                m.W(f"l{l}.wv")[g * D:(g + 1) * D]])
+
+    def merge(b: int, g: int):
+        # softmax over the union of the chunks: rescale each chunk's sums by
+        # exp(m_c - M), M the largest chunk maximum
+        for j in range(G):
+            h = g * G + j
+            M = np.max(pm[b, h])
+            wts = np.exp(pm[b, h] - M)
+            attn[b, h * D:(h + 1) * D] = (wts @ pa[b, h]) / (wts @ pl[b, h])
 
     def run(i: int, t: Task):
         if t.type == EMB:
@@ -492,12 +524,10 @@ def replay(gr: Graph, m: Model, st: State, tokens: Sequence[int], pos: Sequence[
                 mx = np.max(sc)
                 e = np.exp(sc - mx)
                 pm[b, h, t.chunk], pl[b, h, t.chunk], pa[b, h, t.chunk] = mx, e.sum(), e @ vv
+            if mode == MERGE_IN_ATT:             # the only chunk: merge here
+                merge(b, g)
         elif t.type == COMB:
-            for j in range(G):
-                h = t.g * G + j
-                M = np.max(pm[t.b, h])
-                wts = np.exp(pm[t.b, h] - M)
-                attn[t.b, h * D:(h + 1) * D] = (wts @ pa[t.b, h]) / (wts @ pl[t.b, h])
+            merge(t.b, t.g)
         elif t.type == OPROJ:
             w = m.W(f"l{t.layer}.wo")[t.row0:t.row1]
             x[:, t.row0:t.row1] += attn @ w.T

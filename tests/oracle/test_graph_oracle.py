@@ -41,7 +41,10 @@ def test_structure_full_size(cfg):
     gr = G.build(G.desc_from_shape(wl.shape, wl.batch, wl.max_seq))
     G.check_structure(gr)
     n = {t.type for t in gr.tasks}
-    assert n == set(range(9))
+    # merge tasks exist only where attention is split over several chunks
+    # (every full-size workload: 4 chunks of a 4096-position cache, 32 of the
+    # long context, 8 on the batch-16 shape)
+    assert gr.opts.attn_chunks > 1 and n == set(range(9))
     # every large operator spreads over all 256 compute units
     for op in (G.QKV, G.OPROJ, G.GU, G.DOWN, G.LM):
         cus = {t.cu for t in gr.tasks if t.type == op and t.layer in (-1, 0)}
@@ -73,6 +76,32 @@ def test_attention_placement_spreads_sequences():
         n = int(lens[t.b]) + 1
         load[t.cu] += (t.chunk + 1) * n // Nc - t.chunk * n // Nc
     assert load.max() <= 1.3 * load.mean()
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_single_chunk_attention_counts_the_merged_event(batch):
+    """With one chunk per (sequence, kv group) the attention tasks are the
+    merge: no COMB tasks and no per-chunk events, each attention task counts
+    the layer's merged event (threshold Hkv * B, the number of attention tasks
+    of the layer), and the O projection waits for that event."""
+    d, _ = tiny_desc(batch)
+    gr = G.build(d, G.Opts(num_cus=8, attn_chunks=1))
+    split = G.build(d, G.Opts(num_cus=8, attn_chunks=2))
+    assert not any(t.type == G.COMB for t in gr.tasks)
+    # per layer: Hkv * B per-chunk events and as many COMB tasks fewer
+    L, Hkv = d.n_layers, d.n_kv_heads
+    assert len(split.events) - len(gr.events) == L * Hkv * batch
+    for l in range(L):
+        att = [t for t in gr.tasks if t.type == G.ATT and t.layer == l]
+        o = [t for t in gr.tasks if t.type == G.OPROJ and t.layer == l]
+        assert len(att) == Hkv * batch and len({t.trig for t in att}) == 1
+        assert gr.events[att[0].trig].threshold == len(att)
+        assert all(t.dep == att[0].trig for t in o)
+    # a plant in the oracle's graph: one attention task counts the wrong event
+    # (its output is then no longer ordered before the O projection)
+    t0 = next(t for t in gr.tasks if t.type == G.ATT and t.layer == 0)
+    t0.trig = next(t.trig for t in gr.tasks if t.type == G.QKV and t.layer == 1)
+    assert any(buf == "attn" for _, _, buf in G.race_check(gr))
 
 
 def test_race_check_catches_a_missing_edge():
@@ -151,5 +180,5 @@ def test_serialize_layout():
     raw = G.serialize(gr)
     nt, ne = len(gr.tasks), len(gr.events)
     assert raw[:8] == b"MKGRAPH1"
-    assert raw[8:12] == (4).to_bytes(4, "little")     # version 4: skewed attention placement
+    assert raw[8:12] == (5).to_bytes(4, "little")     # version 5: single-chunk attention merges itself
     assert len(raw) == 8 + 4 + 40 + 8 + 4 + 36 + 8 + nt * 40 + ne * 12 + 4 * 4 + nt * 4

@@ -93,8 +93,10 @@ def test_noalloc_second_model_shares_the_workspace():
 def test_noalloc_refuses_a_model_beyond_the_workspace():
     import decode_persistent_megakernel_amd as mk
     wl0 = workload.config(0)
-    # 256 tiny layers: 2051 events of 8 KiB counters each, just over 16 MiB
-    wl = dataclasses.replace(wl0, shape=dataclasses.replace(wl0.shape, n_layers=256))
+    # 352 tiny layers with one attention chunk (6 events per layer: 2 kv
+    # groups' QKV, merged attention, O, gate/up, down), plus 3: 2115 events of
+    # 8 KiB counters each, just over 16 MiB
+    wl = dataclasses.replace(wl0, shape=dataclasses.replace(wl0.shape, n_layers=352))
     w = workload.make_weights(wl, gains="ones")
     ss = _session(wl.shape, w, 1, wl.max_seq)
     out = torch.full((2, 1), -7, dtype=torch.int32, device="cuda")
