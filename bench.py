@@ -51,8 +51,10 @@ def algorithmic_bytes(shape, positions) -> int:
     return w + sum((p + 1) * kv_per_pos for p in positions)
 
 
+# the sources whose hash keys a traffic record: the kernels and the host code
+# that builds the graph they run and lays out its data
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_persistent_megakernel_amd", "csrc", f)
-                  for f in ("kernels.hip", "pipeline.h", "mfma.h", "device.h")]
+                  for f in ("kernels.hip", "pipeline.h", "mfma.h", "device.h", "graph.cpp", "graph.h", "api.cpp")]
 
 
 def recorded_traffic(kernel: str, workload_name: str, steps: int, batch: int):

@@ -83,7 +83,6 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   r.num_cus = N;
   r.row_block = rb;
   r.qkv_tasks_per_group = cap(o.qkv_tasks_per_group ? o.qkv_tasks_per_group : cdiv(N, Hkv), grp_rows);
-  r.o_tasks = cap(o.o_tasks ? o.o_tasks : N, d.hidden);
   r.gu_tasks = cap(o.gu_tasks ? o.gu_tasks : N, d.ffn);
   r.d_tasks = cap(o.d_tasks ? o.d_tasks : N, d.hidden);
   r.attn_chunks = o.attn_chunks
@@ -94,6 +93,14 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
     auto mf_ok = [](int64_t k) { return k % 64 == 0 && k >= 256; };
     const bool shape_ok = mf_ok(d.hidden) && mf_ok(int64_t(d.n_q_heads) * d.head_dim) && mf_ok(d.ffn);
     r.use_mfma = o.use_mfma ? o.use_mfma : (std::min(B, kMfmaCols) > kGroupCols && shape_ok ? 2 : 1);
+  }
+  // O projection on the vector bodies: half the units when its weights would
+  // give each of N tasks less than 64 KiB. The units without an O task start
+  // streaming the gate/up weights that much sooner (measured: 1B shape 878 ->
+  // 866 us/token, 8B shape, 128 KiB per task at N, slower with half).
+  {
+    const bool small_o = int64_t(d.hidden) * d.n_q_heads * d.head_dim * 2 < int64_t(N) * 65536;
+    r.o_tasks = cap(o.o_tasks ? o.o_tasks : (r.use_mfma == 1 && small_o ? int32_t(cdiv(N, 2)) : N), d.hidden);
   }
   // LM head: the matrix-core bodies' tasks default to 8 row blocks (128 rows),
   // so that a stream wave keeps all of a task's row blocks in registers

@@ -152,10 +152,15 @@ def resolve(d: Desc, o: Opts) -> Opts:
     # launch would hold more sequences than the vector bodies stage and every
     # K dimension is a multiple of 64, at least 256
     use_mfma = o.use_mfma or (2 if min(d.max_batch, MFMA_COLS) > GROUP_COLS and _mfma_shape(d) else 1)
+    # O projection on the vector bodies: half the units when its weights would
+    # give each of n tasks less than 64 KiB
+    o_def = n
+    if use_mfma == 1 and d.hidden * d.n_q_heads * d.head_dim * 2 < n * 65536:
+        o_def = _ceil_div(n, 2)
     return Opts(
         num_cus=n,
         qkv_tasks_per_group=cap(o.qkv_tasks_per_group or _ceil_div(n, d.n_kv_heads), grp_rows),
-        o_tasks=cap(o.o_tasks or n, d.hidden),
+        o_tasks=cap(o.o_tasks or o_def, d.hidden),
         gu_tasks=cap(o.gu_tasks or n, d.ffn),
         d_tasks=cap(o.d_tasks or n, d.hidden),
         attn_chunks=chunks,

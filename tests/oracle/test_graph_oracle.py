@@ -45,10 +45,15 @@ def test_structure_full_size(cfg):
     # (every full-size workload: 4 chunks of a 4096-position cache, 32 of the
     # long context, 8 on the batch-16 shape)
     assert gr.opts.attn_chunks > 1 and n == set(range(9))
-    # every large operator spreads over all 256 compute units
+    # every large operator spreads over all 256 compute units; the O
+    # projection over half of them where its weights come to under 64 KiB
+    # per unit (the 1B shape's 8 MiB on the vector bodies)
+    small_o = (gr.opts.use_mfma == 1 and
+               wl.shape.hidden * wl.shape.n_q_heads * wl.shape.head_dim * 2 < 256 * 65536)
+    assert small_o == (cfg in (1, 3))
     for op in (G.QKV, G.OPROJ, G.GU, G.DOWN, G.LM):
         cus = {t.cu for t in gr.tasks if t.type == op and t.layer in (-1, 0)}
-        assert len(cus) == 256, (op, len(cus))
+        assert len(cus) == (128 if op == G.OPROJ and small_o else 256), (op, len(cus))
 
 
 def test_attention_placement_spreads_sequences():
