@@ -82,7 +82,6 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
   mk_graph_opts r{};
   r.num_cus = N;
   r.row_block = rb;
-  r.qkv_tasks_per_group = cap(o.qkv_tasks_per_group ? o.qkv_tasks_per_group : cdiv(N, Hkv), grp_rows);
   r.gu_tasks = cap(o.gu_tasks ? o.gu_tasks : N, d.ffn);
   r.d_tasks = cap(o.d_tasks ? o.d_tasks : N, d.hidden);
   r.attn_chunks = o.attn_chunks
@@ -93,6 +92,15 @@ int build_graph(const mk_model_desc& d, const mk_graph_opts* in, Graph* out, std
     auto mf_ok = [](int64_t k) { return k % 64 == 0 && k >= 256; };
     const bool shape_ok = mf_ok(d.hidden) && mf_ok(int64_t(d.n_q_heads) * d.head_dim) && mf_ok(d.ffn);
     r.use_mfma = o.use_mfma ? o.use_mfma : (std::min(B, kMfmaCols) > kGroupCols && shape_ok ? 2 : 1);
+  }
+  // QKV on the matrix cores: at least one task per 16-row block of a group. A
+  // task's rows are padded to whole blocks, and a padded row streams at the
+  // same per-unit cost (batch-16 8B shape: 24-row tasks padded to 32, 8.29
+  // ms per step; one 16-row block per task, 8.06).
+  {
+    int64_t q = cdiv(N, Hkv);
+    if (r.use_mfma == 2) q = std::max<int64_t>(q, cdiv(grp_rows, kMfmaRowBlock));
+    r.qkv_tasks_per_group = cap(o.qkv_tasks_per_group ? o.qkv_tasks_per_group : int32_t(q), grp_rows);
   }
   // O projection on the vector bodies: half the units when its weights would
   // give each of N tasks less than 64 KiB. The units without an O task start

@@ -17,6 +17,7 @@ namespace mk {
 // for a group of this many
 constexpr int32_t kGroupCols = 4;
 constexpr int32_t kMfmaCols = 16;  // sequences one launch of the matrix-core bodies handles
+constexpr int32_t kMfmaRowBlock = 16;  // rows of one matrix-core row block
 
 enum TaskType : int32_t {
   T_EMB = 0, T_QKV = 1, T_ATT = 2, T_COMB = 3, T_O = 4, T_GU = 5, T_D = 6, T_LM = 7, T_ARGMAX = 8,

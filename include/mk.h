@@ -60,7 +60,8 @@ typedef struct mk_model_desc {
  * num_cus 256, row_block 4, use_mfma 2 when a launch holds more than 4
  * sequences (min(max_batch, 16) > 4) and hidden, n_q_heads * head_dim and ffn
  * are multiples of 64 of at least 256, else 1; qkv_tasks_per_group
- * ceil(num_cus / n_kv_heads); gu_tasks = d_tasks = num_cus; o_tasks num_cus,
+ * ceil(num_cus / n_kv_heads), with use_mfma 2 at least one per 16 rows of a
+ * group ((n_q_heads / n_kv_heads + 2) * head_dim rows); gu_tasks = d_tasks = num_cus; o_tasks num_cus,
  * or ceil(num_cus / 2) with use_mfma 1 when the O projection's weights
  * (hidden * n_q_heads * head_dim bf16) are under 64 KiB per num_cus task; lm_tasks
  * num_cus (use_mfma 1) or max(num_cus, ceil(vocab / 128)) (use_mfma 2);

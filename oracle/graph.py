@@ -52,6 +52,7 @@ TYPE_NAMES = ["EMB", "QKV", "ATT", "COMB", "O", "GU", "D", "LM", "ARGMAX"]
 # most sequences one launch decodes (the graph spec's group size)
 GROUP_COLS = 4
 MFMA_COLS = 16
+MFMA_ROWS = 16   # rows of one matrix-core row block
 
 MAGIC = b"MKGRAPH1"
 VERSION = 5
@@ -157,9 +158,14 @@ def resolve(d: Desc, o: Opts) -> Opts:
     o_def = n
     if use_mfma == 1 and d.hidden * d.n_q_heads * d.head_dim * 2 < n * 65536:
         o_def = _ceil_div(n, 2)
+    # QKV on the matrix cores: at least one task per 16-row block of a group
+    # (a task's rows are padded to whole blocks)
+    qkv_def = _ceil_div(n, d.n_kv_heads)
+    if use_mfma == 2:
+        qkv_def = max(qkv_def, _ceil_div(grp_rows, MFMA_ROWS))
     return Opts(
         num_cus=n,
-        qkv_tasks_per_group=cap(o.qkv_tasks_per_group or _ceil_div(n, d.n_kv_heads), grp_rows),
+        qkv_tasks_per_group=cap(o.qkv_tasks_per_group or qkv_def, grp_rows),
         o_tasks=cap(o.o_tasks or o_def, d.hidden),
         gu_tasks=cap(o.gu_tasks or n, d.ffn),
         d_tasks=cap(o.d_tasks or n, d.hidden),
