@@ -54,6 +54,9 @@ def test_structure_full_size(cfg):
     for op in (G.QKV, G.OPROJ, G.GU, G.DOWN, G.LM):
         cus = {t.cu for t in gr.tasks if t.type == op and t.layer in (-1, 0)}
         assert len(cus) == (128 if op == G.OPROJ and small_o else 256), (op, len(cus))
+    # on the matrix cores every QKV task is one whole 16-row block (no padded rows)
+    if gr.opts.use_mfma == 2:
+        assert all(t.row1 - t.row0 == G.MFMA_ROWS for t in gr.tasks if t.type == G.QKV)
 
 
 def test_attention_placement_spreads_sequences():
